@@ -1,0 +1,9 @@
+"""CPU oracle for exact Lloyd k-means (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package.  The k-means library never imports it, and it imports nothing from
+the library.
+"""
+from .oracle import (  # noqa: F401
+    DTYPES, assign, decode, fit, lib, near_tie, num_threads, round_to, update,
+)

@@ -1,0 +1,26 @@
+"""Compile the C oracle (plain Lloyd, fp64) into oracle/liblloyd_oracle.so.
+
+Test infrastructure: the library never loads it.  gcc, -O2, OpenMP, no
+floating-point contraction and no fast-math, so the fp64 loops run as written.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "lloyd_oracle.c")
+LIB = os.path.join(HERE, "liblloyd_oracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+           "-shared", "-fPIC", SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,287 @@
+/*
+ * Plain CPU oracle for exact Lloyd k-means.  TEST INFRASTRUCTURE ONLY: it is
+ * called by the tests, by the smoke check and by the CPU-baseline leg of the
+ * benchmark, never by the library.  It shares no code with the GPU path.
+ *
+ * What it computes (one Lloyd iteration = assignment stage, then update
+ * stage), as described on the pages:
+ *   - technologypulse.uk "Flash-KMeans" article, section "math unchanged,
+ *     dataflow changed": the assignment stage computes the distance of every
+ *     point to every centroid and picks the nearest; the update stage averages
+ *     the points of each cluster into its new centroid.  The accelerated
+ *     kernels claim a result identical to standard Lloyd, so this file is
+ *     standard Lloyd written out with explicit loops.
+ *   - daily.steinslab.io "e-means" article, section "Breaking 70 Years of
+ *     Full-Batch Inertia": each cluster keeps a sum vector S_j and a count
+ *     N_j, the centroid is S_j / N_j, and the accumulators are reset and the
+ *     whole dataset is streamed every round.
+ *   - github LeanModels/LeanQuant issue #1 "1D k-means", the kmeans_fit diff:
+ *     per-point sample weights; the weighted centroid is sum(w x) / sum(w).
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   - distance is the squared Euclidean distance, summed in fp64 as
+ *     sum_k (x_k - c_k)^2 with k ascending;
+ *   - ties go to the smallest centroid index (j ascending, strict '<');
+ *   - a cluster with no points keeps its previous centroid;
+ *   - the distances of iteration t use C_t rounded (IEEE round-to-nearest-
+ *     even) to the storage type of the points, because that is the operand
+ *     the accelerated assignment multiplies; the fp32 centroids are the state;
+ *   - the assignment ignores weights; the update and the objective use them;
+ *     counts are unweighted integers; "empty" means count 0;
+ *   - the objective of iteration t is J_t = sum_i w_i * min_j D_ij.
+ *
+ * Everything is fp64 except the fp32 centroid state and the conversions,
+ * which follow the IEEE 754 binary16 / bfloat16 formats bit by bit.
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math).
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+/* ----------------------------------------------------------------------- *
+ * IEEE conversions.  A small binary format is (man_bits stored mantissa bits,
+ * exponent bias, emin = 1 - bias).  binary16: 10 / 15; bfloat16: 7 / 127.
+ * ----------------------------------------------------------------------- */
+
+static void format_of(int dtype, int *man_bits, int *bias, int *exp_bits)
+{
+    if (dtype == ORC_F16) { *man_bits = 10; *bias = 15; *exp_bits = 5; }
+    else                  { *man_bits = 7;  *bias = 127; *exp_bits = 8; }
+}
+
+/* Exact value of a stored element, as a double. */
+double oracle_decode_one(uint32_t bits, int dtype)
+{
+    if (dtype == ORC_F32) {
+        float f;
+        memcpy(&f, &bits, 4);
+        return (double)f;
+    }
+    int man_bits, bias, exp_bits;
+    format_of(dtype, &man_bits, &bias, &exp_bits);
+    uint32_t total = 1u + (uint32_t)exp_bits + (uint32_t)man_bits;
+    uint32_t sign = (bits >> (total - 1)) & 1u;
+    uint32_t e = (bits >> man_bits) & ((1u << exp_bits) - 1u);
+    uint32_t m = bits & ((1u << man_bits) - 1u);
+    double v;
+    if (e == (1u << exp_bits) - 1u)
+        v = m ? NAN : INFINITY;
+    else if (e == 0) /* zero or subnormal: m * 2^(emin - man_bits) */
+        v = ldexp((double)m, (1 - bias) - man_bits);
+    else             /* normal: (2^man_bits + m) * 2^(e - bias - man_bits) */
+        v = ldexp((double)((1u << man_bits) + m), (int)e - bias - man_bits);
+    return sign ? -v : v;
+}
+
+/* Round a float32 to the small format with round-to-nearest, ties to even. */
+uint32_t oracle_round_one(float f, int dtype)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (dtype == ORC_F32) return u;
+    int man_bits, bias, exp_bits;
+    format_of(dtype, &man_bits, &bias, &exp_bits);
+    uint32_t total = 1u + (uint32_t)exp_bits + (uint32_t)man_bits;
+    uint32_t sign = (u >> 31) << (total - 1);
+    uint32_t emax_field = (1u << exp_bits) - 1u;
+    uint32_t fe = (u >> 23) & 0xffu;
+    uint32_t fm = u & 0x7fffffu;
+    if (fe == 0xffu) /* inf or nan */
+        return sign | (emax_field << man_bits) | (fm ? (1u << (man_bits - 1)) : 0u);
+    if (fe == 0 && fm == 0) return sign;
+    /* |f| = sig * 2^p2 exactly */
+    uint64_t sig = fe ? (fm | 0x800000u) : fm;
+    int p2 = fe ? (int)fe - 150 : -149;
+    int msb = 63 - __builtin_clzll(sig);
+    int E = p2 + msb;                       /* floor(log2 |f|) */
+    int emin = 1 - bias;
+    int qexp = (E < emin ? emin : E) - man_bits; /* log2 of the quantum at |f| */
+    int sh = qexp - p2;                     /* |f| / quantum = sig / 2^sh */
+    uint64_t n;
+    if (sh <= 0) {
+        n = sig << (-sh);
+    } else if (sh > 62) {
+        n = 0;                              /* far below half a quantum */
+    } else {
+        uint64_t q = sig >> sh, r = sig & ((1ull << sh) - 1ull), half = 1ull << (sh - 1);
+        if (r > half || (r == half && (q & 1ull))) q += 1ull;
+        n = q;
+    }
+    /* value = n * 2^qexp */
+    if (E < emin) {
+        /* subnormal range: n <= 2^man_bits; n == 2^man_bits is the smallest normal,
+         * whose encoding (exponent field 1, mantissa 0) equals n. */
+        return sign | (uint32_t)n;
+    }
+    int Eo = E;
+    if (n == (2ull << man_bits)) { n >>= 1; Eo += 1; } /* rounding carried into the next binade */
+    if (Eo + bias >= (int)emax_field)
+        return sign | (emax_field << man_bits);        /* overflow to infinity */
+    return sign | ((uint32_t)(Eo + bias) << man_bits) | (uint32_t)(n - (1ull << man_bits));
+}
+
+/* Element-wise helpers over arrays. `bits` is uint16 for fp16/bf16, uint32 for fp32. */
+void oracle_decode(const void *bits, int dtype, int64_t n, double *out)
+{
+    if (dtype == ORC_F32) {
+        const float *p = (const float *)bits;
+        for (int64_t i = 0; i < n; ++i) out[i] = (double)p[i];
+    } else {
+        const uint16_t *p = (const uint16_t *)bits;
+        for (int64_t i = 0; i < n; ++i) out[i] = oracle_decode_one(p[i], dtype);
+    }
+}
+
+void oracle_round(const float *in, int64_t n, int dtype, void *bits_out)
+{
+    if (dtype == ORC_F32) {
+        memcpy(bits_out, in, (size_t)n * 4);
+    } else {
+        uint16_t *p = (uint16_t *)bits_out;
+        for (int64_t i = 0; i < n; ++i) p[i] = (uint16_t)oracle_round_one(in[i], dtype);
+    }
+}
+
+/* ----------------------------------------------------------------------- *
+ * Assignment stage: for each point, the squared distance to every centroid,
+ * and the nearest one.  X [B,N,d], C [B,K,d] (fp64, C already rounded to the
+ * point dtype).  Outputs: labels [B,N]; d1 = nearest distance; d2 = second
+ * nearest (INFINITY when K == 1), both [B,N].
+ * ----------------------------------------------------------------------- */
+void oracle_assign(const double *X, int64_t B, int64_t N, int64_t d,
+                   const double *C, int64_t K,
+                   int32_t *labels, double *d1, double *d2)
+{
+    int64_t total = B * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < total; ++bi) {
+        int64_t b = bi / N;
+        const double *x = X + bi * d;
+        const double *Cb = C + b * K * d;
+        double best = INFINITY, second = INFINITY;
+        int32_t arg = -1;
+        for (int64_t j = 0; j < K; ++j) {
+            const double *c = Cb + j * d;
+            double D = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                double t = x[k] - c[k];
+                D += t * t;
+            }
+            if (D < best) {            /* strict: the smallest index wins a tie */
+                second = best;
+                best = D;
+                arg = (int32_t)j;
+            } else if (D < second) {
+                second = D;
+            }
+        }
+        labels[bi] = arg;
+        d1[bi] = best;
+        d2[bi] = second;
+    }
+}
+
+/* ----------------------------------------------------------------------- *
+ * Update stage: per cluster j the sum S_j = sum w_i x_i, the weight
+ * W_j = sum w_i and the count N_j = #{i : l_i = j}, all accumulated in
+ * point order; the new centroid is S_j / W_j, or the old one when N_j == 0.
+ * w may be NULL (all weights 1).  S_out [B,K,d] and W_out [B,K] may be NULL.
+ * c_new may alias c_old.
+ * ----------------------------------------------------------------------- */
+void oracle_update(const double *X, const double *w, const int32_t *labels,
+                   int64_t B, int64_t N, int64_t d, int64_t K,
+                   const float *c_old, float *c_new, int32_t *counts,
+                   double *S_out, double *W_out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        double *S = (double *)calloc((size_t)(K * d), sizeof(double));
+        double *W = (double *)calloc((size_t)K, sizeof(double));
+        int64_t *Nj = (int64_t *)calloc((size_t)K, sizeof(int64_t));
+        for (int64_t i = 0; i < N; ++i) {
+            int64_t j = labels[b * N + i];
+            double wi = w ? w[b * N + i] : 1.0;
+            const double *x = X + (b * N + i) * d;
+            Nj[j] += 1;
+            W[j] += wi;
+            for (int64_t k = 0; k < d; ++k) S[j * d + k] += wi * x[k];
+        }
+        for (int64_t j = 0; j < K; ++j) {
+            const float *co = c_old + (b * K + j) * d;
+            float *cn = c_new + (b * K + j) * d;
+            for (int64_t k = 0; k < d; ++k)
+                cn[k] = Nj[j] > 0 ? (float)(S[j * d + k] / W[j]) : co[k];
+            counts[b * K + j] = (int32_t)Nj[j];
+            if (W_out) W_out[b * K + j] = W[j];
+            if (S_out)
+                for (int64_t k = 0; k < d; ++k) S_out[(b * K + j) * d + k] = S[j * d + k];
+        }
+        free(S);
+        free(W);
+        free(Nj);
+    }
+}
+
+/* ----------------------------------------------------------------------- *
+ * n_iter Lloyd iterations from init [B,K,d] fp32.  x holds the stored bits
+ * (float32, or uint16 for fp16/bf16).  w [B,N] fp32 or NULL.
+ * Outputs: C_out [B,K,d] (centroids after the last update), labels_out and
+ * d1_out / d2_out [B,N] (last assignment), counts_out [B,K] (last update),
+ * J_out [B, n_iter] (objective of each assignment).  Returns 0, or -1 when
+ * memory runs out.
+ * ----------------------------------------------------------------------- */
+int oracle_fit(const void *x, int dtype, const float *w,
+               int64_t B, int64_t N, int64_t d, int64_t K,
+               const float *init, int32_t n_iter,
+               float *C_out, int32_t *labels_out, int32_t *counts_out,
+               double *J_out, double *d1_out, double *d2_out)
+{
+    int64_t nx = B * N * d, nc = B * K * d;
+    double *X = (double *)malloc((size_t)nx * sizeof(double));
+    double *Wd = w ? (double *)malloc((size_t)(B * N) * sizeof(double)) : NULL;
+    double *Ch = (double *)malloc((size_t)nc * sizeof(double));
+    uint32_t *cbits = (uint32_t *)malloc((size_t)nc * sizeof(uint32_t));
+    int ok = X && Ch && cbits && (!w || Wd);
+    if (ok) {
+        oracle_decode(x, dtype, nx, X);
+        if (w)
+            for (int64_t i = 0; i < B * N; ++i) Wd[i] = (double)w[i];
+        memcpy(C_out, init, (size_t)nc * sizeof(float));
+        for (int32_t t = 0; t < n_iter; ++t) {
+            /* centroids as the assignment sees them: rounded to the point dtype */
+            for (int64_t i = 0; i < nc; ++i) {
+                cbits[i] = oracle_round_one(C_out[i], dtype);
+                Ch[i] = oracle_decode_one(cbits[i], dtype);
+            }
+            oracle_assign(X, B, N, d, Ch, K, labels_out, d1_out, d2_out);
+            for (int64_t b = 0; b < B; ++b) {
+                double J = 0.0;
+                for (int64_t i = 0; i < N; ++i)
+                    J += (Wd ? Wd[b * N + i] : 1.0) * d1_out[b * N + i];
+                J_out[b * n_iter + t] = J;
+            }
+            oracle_update(X, Wd, labels_out, B, N, d, K, C_out, C_out, counts_out, NULL, NULL);
+        }
+    }
+    free(X);
+    free(Wd);
+    free(Ch);
+    free(cbits);
+    return ok ? 0 : -1;
+}
+
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}

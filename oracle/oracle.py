@@ -1,0 +1,144 @@
+"""ctypes wrapper of the C oracle (plain Lloyd k-means in fp64).
+
+TEST INFRASTRUCTURE ONLY.  Imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the library.  It shares no code with
+the GPU path: the only common module is the seeded input generator.
+
+Arrays are numpy.  Points are passed as their stored bits: float32 arrays for
+fp32, uint16 arrays for fp16 / bf16 (with the dtype name), and are decoded to
+fp64 exactly inside the C code.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+
+_lib = None
+
+
+def lib():
+    """The loaded oracle library; compiled first if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = C.CDLL(_build.LIB)
+        p = C.c_void_p
+        i64 = C.c_int64
+        L.oracle_decode_one.argtypes = [C.c_uint32, C.c_int]
+        L.oracle_decode_one.restype = C.c_double
+        L.oracle_round_one.argtypes = [C.c_float, C.c_int]
+        L.oracle_round_one.restype = C.c_uint32
+        L.oracle_decode.argtypes = [p, C.c_int, i64, p]
+        L.oracle_round.argtypes = [p, i64, C.c_int, p]
+        L.oracle_assign.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
+        L.oracle_update.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p]
+        L.oracle_fit.argtypes = [p, C.c_int, p, i64, i64, i64, i64, p, C.c_int32,
+                                 p, p, p, p, p, p]
+        L.oracle_fit.restype = C.c_int
+        L.oracle_num_threads.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_num_threads())
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 values of stored elements (float32, or uint16 bits of fp16/bf16)."""
+    want = np.float32 if dtype == "f32" else np.uint16
+    bits = np.ascontiguousarray(bits, dtype=want)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib().oracle_decode(_ptr(bits), DTYPES[dtype], bits.size, _ptr(out))
+    return out
+
+
+def round_to(c: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> stored bits of dtype with IEEE round-to-nearest-even."""
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    out = np.empty(c.shape, dtype=np.float32 if dtype == "f32" else np.uint16)
+    lib().oracle_round(_ptr(c), c.size, DTYPES[dtype], _ptr(out))
+    return out
+
+
+def assign(X: np.ndarray, Chat: np.ndarray):
+    """Assignment stage.  X [B,N,d] fp64, Chat [B,K,d] fp64 (already in the
+    point dtype's values).  Returns labels int32 [B,N], d1 (nearest squared
+    distance) and d2 (second nearest; inf when K == 1), fp64 [B,N]."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    Chat = np.ascontiguousarray(Chat, dtype=np.float64)
+    B, N, d = X.shape
+    K = Chat.shape[1]
+    assert Chat.shape == (B, K, d)
+    labels = np.empty((B, N), np.int32)
+    d1 = np.empty((B, N), np.float64)
+    d2 = np.empty((B, N), np.float64)
+    lib().oracle_assign(_ptr(X), B, N, d, _ptr(Chat), K, _ptr(labels), _ptr(d1), _ptr(d2))
+    return labels, d1, d2
+
+
+def update(X: np.ndarray, w, labels: np.ndarray, c_old: np.ndarray):
+    """Update stage.  X [B,N,d] fp64, w [B,N] (or None), labels int32 [B,N],
+    c_old [B,K,d] fp32.  Returns (c_new fp32, counts int32 [B,K],
+    S fp64 [B,K,d], W fp64 [B,K])."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    B, N, d = X.shape
+    c_old = np.ascontiguousarray(c_old, dtype=np.float32)
+    K = c_old.shape[1]
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    assert labels.shape == (B, N)
+    if labels.size and (labels.min() < 0 or labels.max() >= K):
+        raise ValueError("label out of range")
+    wd = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
+    c_new = np.empty_like(c_old)
+    counts = np.empty((B, K), np.int32)
+    S = np.empty((B, K, d), np.float64)
+    W = np.empty((B, K), np.float64)
+    lib().oracle_update(_ptr(X), _ptr(wd), _ptr(labels), B, N, d, K, _ptr(c_old),
+                        _ptr(c_new), _ptr(counts), _ptr(S), _ptr(W))
+    return c_new, counts, S, W
+
+
+def fit(x_bits: np.ndarray, dtype: str, w, init: np.ndarray, n_iter: int) -> dict:
+    """n_iter Lloyd iterations.  x_bits [B,N,d] stored bits, w [B,N] fp32 or
+    None, init [B,K,d] fp32.  Returns centroids, labels and d1/d2 of the last
+    assignment, counts of the last update, and J [B, n_iter]."""
+    want = np.float32 if dtype == "f32" else np.uint16
+    x_bits = np.ascontiguousarray(x_bits, dtype=want)
+    B, N, d = x_bits.shape
+    init = np.ascontiguousarray(init, dtype=np.float32)
+    K = init.shape[1]
+    assert init.shape == (B, K, d)
+    w32 = None if w is None else np.ascontiguousarray(w, dtype=np.float32)
+    C_out = np.empty_like(init)
+    labels = np.empty((B, N), np.int32)
+    counts = np.empty((B, K), np.int32)
+    J = np.empty((B, n_iter), np.float64)
+    d1 = np.empty((B, N), np.float64)
+    d2 = np.empty((B, N), np.float64)
+    rc = lib().oracle_fit(_ptr(x_bits), DTYPES[dtype], _ptr(w32), B, N, d, K, _ptr(init),
+                          int(n_iter), _ptr(C_out), _ptr(labels), _ptr(counts), _ptr(J),
+                          _ptr(d1), _ptr(d2))
+    if rc != 0:
+        raise MemoryError("oracle_fit ran out of host memory")
+    return dict(centroids=C_out, labels=labels, counts=counts, J=J, d1=d1, d2=d2)
+
+
+def near_tie(d1: np.ndarray, d2: np.ndarray, rel: float = 1e-4) -> np.ndarray:
+    """Points whose top-2 gap is at most rel * nearest distance.
+
+    d1 == d2 (duplicate centroids, including both zero) is a near tie;
+    d1 == 0 < d2 is not; with one centroid (d2 = inf) nothing is."""
+    return (d2 - d1) <= rel * d1

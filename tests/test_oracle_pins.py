@@ -1,0 +1,346 @@
+"""Pins of the CPU oracle against facts fixed outside of it (no GPU needed).
+
+Each test checks the oracle against something it does not compute itself:
+a library routine that is a special case (scipy's cdist + argmin, numpy's
+bincount, numpy/torch IEEE conversions), a closed form, exhaustive search on
+tiny inputs, or the worked example printed on the pages.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.spatial.distance import cdist
+
+from oracle import brute
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _f32_bits(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- conversions
+
+def _interesting_f32(rng, n):
+    """Random float32 values plus the edge cases of the fp16/bf16 roundings."""
+    u = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    vals = [u.view(np.float32)]
+    vals.append(rng.standard_normal(n).astype(np.float32) * np.float32(3.0))
+    vals.append((rng.standard_normal(n) * 1e-5).astype(np.float32))   # fp16 subnormals
+    special = np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.996, 65520.0, 1e6, 6.1035156e-05,
+                        5.9604645e-08, 2.9802322e-08, 2.9802326e-08, 1.0009765625, 1.00048828125,
+                        1.000732421875, 1.00390625, 1.001953125, 3.4028235e38, 1.1754944e-38,
+                        1e-45, np.inf, -np.inf], dtype=np.float32)
+    vals.append(special)
+    # exact halfway cases for fp16 and bf16 at random exponents
+    m = rng.integers(0, 1 << 10, size=n).astype(np.uint32)
+    e = rng.integers(100, 140, size=n).astype(np.uint32)
+    halfway16 = ((e << 23) | (m << 13) | (1 << 12)).view(np.float32)
+    halfway_bf = ((e << 23) | ((m & 0x7F) << 16) | (1 << 15)).view(np.float32)
+    vals += [halfway16, halfway_bf]
+    out = np.concatenate(vals)
+    return out[np.isfinite(out) | np.isinf(out)]
+
+
+def test_fp16_round_matches_numpy(orc):
+    rng = np.random.default_rng(0)
+    x = _interesting_f32(rng, 20000)
+    x = x[~np.isnan(x)]
+    got = orc.round_to(x, "f16")
+    want = x.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_round_matches_torch(orc):
+    rng = np.random.default_rng(1)
+    x = _interesting_f32(rng, 20000)
+    x = x[~np.isnan(x)]
+    got = orc.round_to(x, "bf16")
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_decode_is_exact(orc):
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    h = allbits.view(np.float16).astype(np.float64)
+    got = orc.decode(allbits, "f16")
+    ok = ~np.isnan(h)
+    np.testing.assert_array_equal(got[ok], h[ok])
+    assert np.all(np.isnan(got[~ok]))
+    b = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = orc.decode(allbits, "bf16")
+    ok = ~np.isnan(b)
+    np.testing.assert_array_equal(got[ok], b[ok])
+    assert np.all(np.isnan(got[~ok]))
+
+
+# ------------------------------------------------------------- assignment
+
+def test_assign_matches_cdist_argmin(orc):
+    rng = np.random.default_rng(2)
+    B, N, d, K = 3, 300, 7, 13
+    X = rng.standard_normal((B, N, d))
+    Cc = rng.standard_normal((B, K, d))
+    labels, d1, d2 = orc.assign(X, Cc)
+    for b in range(B):
+        D = cdist(X[b], Cc[b], "sqeuclidean")
+        np.testing.assert_array_equal(labels[b], np.argmin(D, axis=1))
+        srt = np.sort(D, axis=1)
+        np.testing.assert_allclose(d1[b], srt[:, 0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(d2[b], srt[:, 1], rtol=1e-12, atol=1e-14)
+
+
+def test_assign_distance_table_exhaustive(orc):
+    """Every (point, centroid) distance of a small grid, against a direct table."""
+    pts = np.array(list(itertools.product([-1.0, 0.0, 0.5, 2.0], repeat=3)))  # 64 points
+    cen = np.array([[0.0, 0.0, 0.0], [1.0, -1.0, 0.5], [2.0, 2.0, 2.0], [-1.0, 0.5, 0.0]])
+    labels, d1, _ = orc.assign(pts[None], cen[None])
+    for i, p in enumerate(pts):
+        D = [float(sum((p[k] - c[k]) ** 2 for k in range(3))) for c in cen]
+        assert d1[0, i] == min(D)
+        assert labels[0, i] == D.index(min(D))  # list.index: first occurrence
+
+
+def test_tie_goes_to_smallest_index(orc):
+    X = np.array([[[0.0, 0.0], [1.0, 1.0], [5.0, 5.0]]])
+    Cc = np.array([[[3.0, 3.0], [1.0, 1.0], [1.0, 1.0], [-1.0, -1.0]]])
+    labels, d1, d2 = orc.assign(X, Cc)
+    # point 0 is equidistant from centroids 1, 2 (d=2) and 3 (d=2)
+    assert labels[0, 0] == 1 and d1[0, 0] == 2.0 and d2[0, 0] == 2.0
+    assert labels[0, 1] == 1 and d1[0, 1] == 0.0 and d2[0, 1] == 0.0
+    assert labels[0, 2] == 0
+    nt = orc.near_tie(d1, d2)
+    assert nt[0, 0] and nt[0, 1] and not nt[0, 2]
+
+
+def test_near_tie_rule(orc):
+    d1 = np.array([1.0, 1.0, 0.0, 0.0, 2.0])
+    d2 = np.array([1.0 + 0.5e-4, 1.0 + 2e-4, 0.0, 1e-9, np.inf])
+    np.testing.assert_array_equal(orc.near_tie(d1, d2), [True, False, True, False, False])
+
+
+# ----------------------------------------------------------------- update
+
+def test_update_matches_bincount(orc):
+    rng = np.random.default_rng(3)
+    B, N, d, K = 2, 500, 5, 11
+    X = rng.standard_normal((B, N, d))
+    w = rng.uniform(0.1, 1.0, size=(B, N))
+    labels = rng.integers(0, K - 2, size=(B, N)).astype(np.int32)  # clusters K-2, K-1 empty
+    c_old = rng.standard_normal((B, K, d)).astype(np.float32)
+    for weights in (None, w):
+        c_new, counts, S, W = orc.update(X, weights, labels, c_old)
+        for b in range(B):
+            wb = np.ones(N) if weights is None else weights[b]
+            cnt = np.bincount(labels[b], minlength=K)
+            Wb = np.bincount(labels[b], weights=wb, minlength=K)
+            np.testing.assert_array_equal(counts[b], cnt)
+            np.testing.assert_allclose(W[b], Wb, rtol=1e-13)
+            for k in range(d):
+                Sk = np.bincount(labels[b], weights=wb * X[b, :, k], minlength=K)
+                np.testing.assert_allclose(S[b, :, k], Sk, rtol=1e-12, atol=1e-12)
+                want = np.where(cnt > 0, Sk / np.where(Wb > 0, Wb, 1.0), c_old[b, :, k])
+                np.testing.assert_allclose(c_new[b, :, k], want.astype(np.float32), rtol=2e-7, atol=1e-7)
+            # conservation and empty clusters
+            np.testing.assert_allclose(S[b].sum(axis=0), (wb[:, None] * X[b]).sum(axis=0), rtol=1e-10, atol=1e-10)
+            assert counts[b].sum() == N
+            np.testing.assert_array_equal(c_new[b, K - 2:], c_old[b, K - 2:])
+
+
+# ------------------------------------------------------- whole iterations
+
+def _fit_f32(orc, X32, K_init, n_iter, w=None):
+    X32 = np.ascontiguousarray(X32, dtype=np.float32)
+    return orc.fit(X32, "f32", w, np.ascontiguousarray(K_init, dtype=np.float32), n_iter)
+
+
+def test_brute_force_tiny(orc):
+    """Oracle fits never beat the exhaustive optimum and reach it from a good start."""
+    rng = np.random.default_rng(4)
+    for trial in range(4):
+        n, K, d = 7, 3, 2
+        # three separated groups (sizes 3, 2, 2) with random jitter
+        centers = np.array([[0.0, 0.0], [5.0, 1.0], [1.0, 6.0]])
+        grp = np.array([0, 0, 0, 1, 1, 2, 2])
+        pts = (centers[grp] + 0.3 * rng.standard_normal((n, d))).astype(np.float32)
+        if trial % 2:
+            pts = pts[rng.permutation(n)]
+        P = [tuple(float(v) for v in p) for p in pts]
+        Jstar, lab_star = brute.best_partition(P, K)
+        # (i) every Lloyd run from every K-subset init ends at J >= J*
+        for sub in itertools.combinations(range(n), K):
+            r = _fit_f32(orc, pts[None], pts[list(sub)][None], 12)
+            assert r["J"][0, -1] >= Jstar - 1e-9 * max(1.0, Jstar)
+        # (iii) one point of each group as init reaches the optimum exactly
+        g = grp if trial % 2 == 0 else None
+        if g is not None:
+            init = pts[[0, 3, 5]]
+            r = _fit_f32(orc, pts[None], init[None], 10)
+            assert abs(r["J"][0, -1] - Jstar) <= 1e-6 * Jstar
+        # (ii) the optimal means are a fixed point of one iteration
+        lab_star = np.array(lab_star)
+        means = np.stack([pts[lab_star == j].astype(np.float64).mean(axis=0) for j in range(K)])
+        r = _fit_f32(orc, pts[None], means[None], 1)
+        np.testing.assert_array_equal(r["labels"][0], lab_star)
+        np.testing.assert_allclose(r["centroids"][0], means, rtol=1e-6, atol=1e-6)
+
+
+def test_brute_force_weighted_tiny(orc):
+    rng = np.random.default_rng(5)
+    n, K = 8, 2
+    pts = np.concatenate([rng.normal(0, 0.2, 4), rng.normal(3, 0.2, 4)]).astype(np.float32)[:, None]
+    w = rng.uniform(0.1, 1.0, n).astype(np.float32)
+    Jstar, lab = brute.best_partition([tuple(map(float, p)) for p in pts], K, [float(v) for v in w])
+    r = orc.fit(pts[None], "f32", w[None], pts[[0, 4]][None], 10)
+    assert abs(r["J"][0, -1] - Jstar) <= 1e-6 * Jstar
+    # weighted centroid of the optimal partition
+    lab = np.array(lab)
+    for j in range(K):
+        m = lab == j
+        want = (w[m].astype(np.float64) * pts[m, 0]).sum() / w[m].astype(np.float64).sum()
+        got = r["centroids"][0, r["labels"][0][m][0], 0]
+        assert abs(got - want) <= 1e-6 * max(1.0, abs(want))
+
+
+def test_worked_example_three_groups(orc):
+    """Pages' worked example: thirteen weights in three groups, grid init."""
+    g = json.load(open(os.path.join(HERE, "golden", "cache_aware_clustering_example.json")))
+    v = np.array(g["weights13"], dtype=np.float32)
+    K = 3
+    init = np.linspace(v.astype(np.float64).min(), v.astype(np.float64).max(), K).astype(np.float32)
+    r = _fit_f32(orc, v[None, :, None], init[None, :, None], 5)
+    c = np.sort(r["centroids"][0, :, 0])
+    printed = sorted(g["centroids13_printed"].values())
+    np.testing.assert_array_equal(np.round(c.astype(np.float64), g["decimals"]), printed)
+    # the partition is the three printed groups
+    lab = r["labels"][0]
+    for grp in g["groups13"]:
+        assert len(set(lab[grp])) == 1
+    assert len({lab[grp[0]] for grp in g["groups13"]}) == 3
+    # and it is the global 1D optimum
+    Jstar, _ = brute.best_1d_split([float(t) for t in v], K)
+    assert abs(r["J"][0, -1] - Jstar) <= 1e-9
+    # J is non-increasing along the fit
+    assert np.all(np.diff(r["J"][0]) <= 1e-15)
+
+
+def test_worked_example_two_clusters(orc):
+    """Pages' worked example: the first ten weights give indices 0x5, 1x5 and two values."""
+    g = json.load(open(os.path.join(HERE, "golden", "cache_aware_clustering_example.json")))
+    v = np.array(g["weights10"], dtype=np.float32)
+    r = _fit_f32(orc, v[None, :, None], v[None, :2, None], 10)  # first-K init
+    np.testing.assert_array_equal(r["labels"][0], g["labels10_printed"])
+    np.testing.assert_array_equal(np.round(r["centroids"][0, :, 0].astype(np.float64), 4),
+                                  g["centroids10_printed"])
+    Jstar, lab = brute.best_partition([(float(t),) for t in v], 2)
+    assert abs(r["J"][0, -1] - Jstar) <= 1e-9
+
+
+def test_worked_example_bad_init_is_local(orc):
+    """Lloyd only reaches a local optimum: first-K init on the thirteen weights
+    puts two centroids in the top group and gets stuck well above J*."""
+    g = json.load(open(os.path.join(HERE, "golden", "cache_aware_clustering_example.json")))
+    v = np.array(g["weights13"], dtype=np.float32)
+    r = _fit_f32(orc, v[None, :, None], v[None, :3, None], 20)
+    Jstar, _ = brute.best_1d_split([float(t) for t in v], 3)
+    assert r["J"][0, -1] > 1e4 * Jstar
+    assert abs(r["J"][0, -1] - r["J"][0, -2]) == 0.0  # a fixed point
+
+
+def test_1d_global_optimum_bound(orc):
+    rng = np.random.default_rng(6)
+    for trial in range(6):
+        n, K = 9, 3
+        v = (0.02 * rng.standard_t(4, n)).astype(np.float32)
+        w = rng.uniform(0.1, 1.0, n).astype(np.float32)
+        Jstar, means = brute.best_1d_split([float(t) for t in v], K, [float(t) for t in w])
+        init = np.linspace(float(v.min()), float(v.max()), K).astype(np.float32)
+        r = orc.fit(v[None, :, None], "f32", w[None], init[None, :, None], 30)
+        assert r["J"][0, -1] >= Jstar - 1e-12
+    # well-separated data with grid init reaches the optimum
+    v = np.concatenate([rng.normal(-1, 0.01, 3), rng.normal(0, 0.01, 3), rng.normal(1, 0.01, 3)]).astype(np.float32)
+    Jstar, means = brute.best_1d_split([float(t) for t in v], 3)
+    init = np.linspace(float(v.min()), float(v.max()), 3).astype(np.float32)
+    r = _fit_f32(orc, v[None, :, None], init[None, :, None], 10)
+    assert abs(r["J"][0, -1] - Jstar) <= 1e-9
+    np.testing.assert_allclose(np.sort(r["centroids"][0, :, 0]), means, rtol=1e-6)
+
+
+# ------------------------------------------------------ special cases
+
+def test_k1_is_weighted_mean(orc):
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((1, 400, 6)).astype(np.float32)
+    w = rng.uniform(0.1, 1, (1, 400)).astype(np.float32)
+    r = orc.fit(X, "f32", w, X[:, :1], 2)
+    Xd, wd = X[0].astype(np.float64), w[0].astype(np.float64)
+    mean = (wd[:, None] * Xd).sum(0) / wd.sum()
+    np.testing.assert_allclose(r["centroids"][0, 0], mean, rtol=1e-6, atol=1e-7)
+    m32 = mean.astype(np.float32).astype(np.float64)   # the state is fp32
+    J1 = (wd * ((Xd - m32) ** 2).sum(1)).sum()
+    assert abs(r["J"][0, 1] - J1) <= 1e-10 * J1
+    assert np.all(r["labels"] == 0) and r["counts"][0, 0] == 400
+    assert np.all(np.isinf(r["d2"]))
+
+
+def test_k_equals_n_identity(orc):
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((1, 50, 4)).astype(np.float32)
+    r = orc.fit(X, "f32", None, X.copy(), 3)
+    np.testing.assert_array_equal(r["labels"][0], np.arange(50))
+    assert np.all(r["J"] == 0.0)
+    np.testing.assert_array_equal(r["centroids"], X)
+    np.testing.assert_array_equal(r["counts"][0], np.ones(50))
+
+
+def test_batches_are_independent(orc):
+    rng = np.random.default_rng(9)
+    B, N, d, K = 4, 300, 8, 10
+    X = rng.standard_normal((B, N, d)).astype(np.float16)
+    bits = X.view(np.uint16)
+    init = X[:, :K].astype(np.float32)
+    r = orc.fit(bits, "f16", None, init, 5)
+    for b in range(B):
+        rb = orc.fit(bits[b:b + 1], "f16", None, init[b:b + 1], 5)
+        for key in ("centroids", "labels", "counts", "J", "d1", "d2"):
+            np.testing.assert_array_equal(r[key][b], rb[key][0])
+
+
+def test_duplicate_centroids_and_empty_keep_old(orc):
+    rng = np.random.default_rng(10)
+    X = rng.standard_normal((1, 200, 3)).astype(np.float32)
+    init = np.array([[[0, 0, 0], [0, 0, 0], [3, 3, 3], [50, 50, 50]]], dtype=np.float32)
+    r = orc.fit(X, "f32", None, init, 1)
+    assert r["counts"][0, 1] == 0 and r["counts"][0, 3] == 0
+    np.testing.assert_array_equal(r["centroids"][0, 1], init[0, 1])
+    np.testing.assert_array_equal(r["centroids"][0, 3], init[0, 3])
+    assert set(np.unique(r["labels"][0])) <= {0, 2}
+
+
+def test_lloyd_invariants_on_mixture(orc):
+    """Every label is the argmin, every centroid the mean of its points, J never increases."""
+    import workloads
+    for dt, slack in (("f32", 1e-12), ("f16", 1e-5), ("bf16", 1e-4)):
+        wl = workloads.small("gmm-b32-n65536-k1024-d128-f16", B=2, N=1500, d=12, K=24,
+                             n_iter=6, dtype=dt)
+        p = workloads.generate(wl)
+        bits = workloads.raw_bits(p.x)
+        init = p.init.numpy()
+        rn = orc.fit(bits, dt, None, init, wl.n_iter)
+        rp = orc.fit(bits, dt, None, init, wl.n_iter - 1)
+        J = rn["J"]
+        assert np.all(np.diff(J, axis=1) <= slack * J[:, :-1]), (dt, J)
+        X = orc.decode(bits, dt)
+        Chat = orc.decode(orc.round_to(rp["centroids"], dt), dt)
+        for b in range(wl.B):
+            D = cdist(X[b], Chat[b], "sqeuclidean")
+            np.testing.assert_array_equal(rn["labels"][b], np.argmin(D, axis=1))
+            cnt = np.bincount(rn["labels"][b], minlength=wl.K)
+            for k in range(wl.d):
+                s = np.bincount(rn["labels"][b], weights=X[b, :, k], minlength=wl.K)
+                want = np.where(cnt > 0, s / np.maximum(cnt, 1), rp["centroids"][b, :, k])
+                np.testing.assert_allclose(rn["centroids"][b, :, k], want, rtol=1e-6, atol=1e-7)
