@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of exact Lloyd k-means on one MI355X.
+
+A step is one Lloyd iteration over the whole workload: centroid prep, the
+fused assignment (with the objective), the counting argsort of the labels,
+the segmented reduction and the divide -- all in the HIP kernels behind the
+C ABI.  Inputs are resident in device memory before the timed region.
+
+Prints one JSON line: iterations/s, the assignment kernel against its
+roofline (HIP events around every assignment in the timed region), the
+update's bandwidth, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Lloyd iter/s at N=1M K=8192 d=128 fp16; assign TFLOP/s, update GB/s"
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense MI355X matrix-core peaks
+PEAK_HBM_GBS = 8000.0
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_traffic.json")
+ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_03_amd", "csrc", "assign_mfma.hip")
+
+
+def update_bytes(wl) -> float:
+    """Algorithmic bytes of one update: points gathered once, labels read once,
+    perm written and read once, weights (if any), old + new centroids, counts."""
+    B, N, d, K, s = wl.B, wl.N, wl.d, wl.K, ELEM_BYTES[wl.dtype]
+    w = 4 * B * N if wl.weighted else 0
+    return B * N * d * s + 4 * B * N + 8 * B * N + w + 8 * B * K * d + 4 * B * K
+
+
+def assign_bytes(wl) -> float:
+    """Algorithmic bytes of one assignment: points once, labels written, centroids once."""
+    B, N, d, K, s = wl.B, wl.N, wl.d, wl.K, ELEM_BYTES[wl.dtype]
+    w = 4 * B * N if wl.weighted else 0
+    return B * N * (d * s + 4) + w + B * K * d * 4
+
+
+def _src_hash(path) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(wl):
+    """HBM bytes per assignment launch from the committed rocprofv3 counter
+    summary, if it was taken on this workload with the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != wl.name or t.get("kernel_src_sha") != _src_hash(ASSIGN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(p, target_s: float):
+    """Time the CPU oracle on a bounded sample: n_s points against all K
+    centroids (assignment) and their update, extrapolated linearly in N."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    wl = p.wl
+    X_bits = workloads.raw_bits(p.x[0])
+    C = p.init[0:1].numpy()
+    Chat = oracle.decode(oracle.round_to(C, wl.dtype), wl.dtype)
+    rng = np.random.default_rng(12345)
+
+    def run(n):
+        idx = np.sort(rng.choice(wl.N, size=n, replace=False))
+        X = oracle.decode(X_bits[idx][None], wl.dtype)
+        w = None if p.w is None else p.w[0:1, idx].numpy()
+        t0 = time.perf_counter()
+        lab, d1, d2 = oracle.assign(X, Chat)
+        oracle.update(X, w, lab, C)
+        return time.perf_counter() - t0
+
+    n = min(wl.N, 256)
+    t = run(n)
+    while t < 0.5 and n < wl.N:
+        n = min(wl.N, n * 4)
+        t = run(n)
+    if n < wl.N:
+        n = int(min(wl.N, max(n, n * target_s / max(t, 1e-9))))
+        t = run(n)
+    per_iter = t * (wl.N / n) * wl.B
+    return {
+        "value": 1.0 / per_iter,
+        "unit": "iter/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{n} of {wl.N} points of batch 0 (of {wl.B}): one oracle assignment against all "
+                   f"K={wl.K} centroids plus the update of those points, {t:.2f} s, extrapolated "
+                   f"linearly to all {wl.B * wl.N} points"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the batched problems are independent per GPU, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_lloyd_means_03_amd as km
+    import workloads
+
+    km.load()  # raises if the HIP library is missing
+    name = args.workload or workloads.HEADLINE
+    wl = workloads.WORKLOADS[name]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    p = workloads.generate(wl)
+    x = p.x.to(dev)
+    w = None if p.w is None else p.w.to(dev)
+    C = p.init.to(dev).clone()
+    B, N, d, K = wl.B, wl.N, wl.d, wl.K
+    ws = km.workspace(B, N, d, K, x.dtype, dev)
+    labels = torch.empty((B, N), dtype=torch.int32, device=dev)
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    obj = torch.empty((max(args.steps, args.warmup, 1), B), dtype=torch.float64, device=dev)
+
+    def step(k):
+        km.kmeans_assign(x, C, weights=w, labels=labels, objective=obj[k], ws=ws)
+
+    for k in range(args.warmup):
+        step(k)
+        km.kmeans_update(x, labels, C, weights=w, c_new=C, counts=counts, ws=ws)
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K_steps):
+        ev[k][0].record()
+        step(k)
+        ev[k][1].record()
+        km.kmeans_update(x, labels, C, weights=w, c_new=C, counts=counts, ws=ws)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    elapsed = t1 - t0
+    assign_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K_steps
+    update_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K_steps
+    if d == 1:
+        bound, unit = "hbm", "GB/s"
+        algo = assign_bytes(wl)
+        achieved = algo / (assign_ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+    else:
+        bound, unit = "mfma", "TFLOP/s"
+        algo = 2.0 * B * N * K * d
+        achieved = algo / (assign_ms * 1e-3) / 1e12
+        peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    ub = update_bytes(wl)
+    out = {
+        "metric": METRIC,
+        "value": K_steps / elapsed,
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / K_steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "N": N, "d": d, "K": K, "point_dtype": wl.dtype,
+                   "weighted": wl.weighted, "init": wl.init},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": _traffic(wl),
+                     "kernel": "k_assign_1d" if d == 1 else "k_assign_mfma",
+                     "algorithmic_per_launch": algo, "avg_launch_ms": assign_ms},
+        "update": {"avg_ms": update_ms, "algorithmic_bytes": ub, "GB/s": ub / (update_ms * 1e-3) / 1e9,
+                   "frac_hbm": ub / (update_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+"""Python entry points with the C ABI's names (argument marshalling only).
+
+Tensors are torch tensors on the GPU: torch provides the device memory and
+the stream (the current stream of the tensors' device).  Every step of the
+computation runs in the HIP kernels of libkmeans_mi355x.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.KM_F32, torch.float16: _lib.KM_F16, torch.bfloat16: _lib.KM_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _points(x):
+    _dev_tensor(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, d]")
+    if x.dtype not in _DT:
+        raise TypeError(f"x dtype {x.dtype} is not float32 / float16 / bfloat16")
+    return x.shape
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def workspace_bytes(B: int, N: int, d: int, K: int, dtype: torch.dtype) -> int:
+    n = _lib.load().kmeans_workspace_bytes(B, N, d, K, _DT[dtype])
+    if n == 0 and B * N * d * K > 0:
+        _lib.check(2, "kmeans_workspace_bytes")
+    return int(n)
+
+
+def workspace(B: int, N: int, d: int, K: int, dtype: torch.dtype, device) -> torch.Tensor:
+    """A device workspace large enough for every entry point at these shapes."""
+    n = workspace_bytes(B, N, d, K, dtype)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws, B, N, d, K, dtype, device):
+    if ws is None:
+        ws = workspace(B, N, d, K, dtype, device)
+    _dev_tensor(ws, "workspace", torch.uint8)
+    return ws
+
+
+def kmeans_assign(x, centroids, weights=None, labels=None, min_dist=None, objective=None, ws=None):
+    """Nearest centroid of every point.  Returns (labels, min_dist, objective);
+    min_dist / objective are None unless tensors are passed in (or True)."""
+    B, N, d = _points(x)
+    _dev_tensor(centroids, "centroids", torch.float32)
+    if centroids.dim() != 3 or centroids.shape[0] != B or centroids.shape[2] != d:
+        raise ValueError("centroids must be [B, K, d] float32")
+    K = centroids.shape[1]
+    dev = x.device
+    if weights is not None:
+        _dev_tensor(weights, "weights", torch.float32, (B, N))
+    labels = torch.empty((B, N), dtype=torch.int32, device=dev) if labels is None else \
+        _dev_tensor(labels, "labels", torch.int32, (B, N))
+    if min_dist is True:
+        min_dist = torch.empty((B, N), dtype=torch.float32, device=dev)
+    elif min_dist is not None:
+        _dev_tensor(min_dist, "min_dist", torch.float32, (B, N))
+    if objective is True:
+        objective = torch.empty((B,), dtype=torch.float64, device=dev)
+    elif objective is not None:
+        _dev_tensor(objective, "objective", torch.float64, (B,))
+    ws = _ws(ws, B, N, d, K, x.dtype, dev)
+    st = _lib.load().kmeans_assign(_ptr(x), _DT[x.dtype], B, N, d, _ptr(centroids), K, _ptr(weights),
+                                   _ptr(labels), _ptr(min_dist), _ptr(objective), _ptr(ws), ws.numel(),
+                                   _stream(dev))
+    _lib.check(st, "kmeans_assign")
+    return labels, min_dist, objective
+
+
+def kmeans_sort_labels(labels, K: int, ws=None):
+    """Counting argsort of labels [B, N] int32.  Returns (counts, offsets, perm)."""
+    _dev_tensor(labels, "labels", torch.int32)
+    if labels.dim() != 2:
+        raise ValueError("labels must be [B, N]")
+    B, N = labels.shape
+    dev = labels.device
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    offsets = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    perm = torch.empty((B, N), dtype=torch.int32, device=dev)
+    ws = _ws(ws, B, N, 2, K, torch.float32, dev)
+    st = _lib.load().kmeans_sort_labels(_ptr(labels), B, N, K, _ptr(counts), _ptr(offsets), _ptr(perm),
+                                        _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_sort_labels")
+    return counts, offsets, perm
+
+
+def kmeans_update(x, labels, c_old, weights=None, c_new=None, counts=None, ws=None):
+    """Centroids as the (weighted) means of their points; empty clusters keep
+    c_old.  Returns (c_new, counts)."""
+    B, N, d = _points(x)
+    _dev_tensor(labels, "labels", torch.int32, (B, N))
+    _dev_tensor(c_old, "c_old", torch.float32)
+    if c_old.dim() != 3 or c_old.shape[0] != B or c_old.shape[2] != d:
+        raise ValueError("c_old must be [B, K, d] float32")
+    K = c_old.shape[1]
+    dev = x.device
+    if weights is not None:
+        _dev_tensor(weights, "weights", torch.float32, (B, N))
+    c_new = torch.empty_like(c_old) if c_new is None else _dev_tensor(c_new, "c_new", torch.float32, c_old.shape)
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev) if counts is None else \
+        _dev_tensor(counts, "counts", torch.int32, (B, K))
+    ws = _ws(ws, B, N, d, K, x.dtype, dev)
+    st = _lib.load().kmeans_update(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, d, _ptr(labels), K,
+                                   _ptr(c_old), _ptr(c_new), _ptr(counts), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_update")
+    return c_new, counts
+
+
+def kmeans_fit(x, init, n_iter: int, weights=None, centroids=None, labels=None, counts=None,
+               objective=None, ws=None):
+    """n_iter Lloyd iterations from init.  Returns (centroids, labels, counts,
+    objective [B, n_iter] float64)."""
+    B, N, d = _points(x)
+    _dev_tensor(init, "init", torch.float32)
+    if init.dim() != 3 or init.shape[0] != B or init.shape[2] != d:
+        raise ValueError("init must be [B, K, d] float32")
+    K = init.shape[1]
+    dev = x.device
+    if weights is not None:
+        _dev_tensor(weights, "weights", torch.float32, (B, N))
+    centroids = torch.empty_like(init) if centroids is None else \
+        _dev_tensor(centroids, "centroids", torch.float32, init.shape)
+    labels = torch.empty((B, N), dtype=torch.int32, device=dev) if labels is None else \
+        _dev_tensor(labels, "labels", torch.int32, (B, N))
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev) if counts is None else \
+        _dev_tensor(counts, "counts", torch.int32, (B, K))
+    objective = torch.empty((B, max(n_iter, 0)), dtype=torch.float64, device=dev) if objective is None else \
+        _dev_tensor(objective, "objective", torch.float64, (B, n_iter))
+    ws = _ws(ws, B, N, d, K, x.dtype, dev)
+    st = _lib.load().kmeans_fit(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, d, K, _ptr(init), int(n_iter),
+                                _ptr(centroids), _ptr(labels), _ptr(counts), _ptr(objective), _ptr(ws),
+                                ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_fit")
+    return centroids, labels, counts, objective

@@ -1,0 +1,273 @@
+// Host side of the C ABI declared in include/kmeans.h: argument checks,
+// the workspace plan and the per-iteration kernel sequence.  Every check
+// happens before the first enqueue; nothing here allocates device memory or
+// synchronizes the stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/kmeans.h"
+#include "common.h"
+
+namespace km {
+
+static thread_local std::string g_last_error;
+
+static km_status fail(km_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static km_status fail(km_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+static km_status hip_fail(hipError_t e, const char* where) {
+    return fail(KM_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static bool use_assign_1d(int64_t d, int64_t K) { return d == 1 && assign_1d_supports(K); }
+static bool use_update_1d(int64_t d, int64_t N, int64_t K) { return d == 1 && update_1d_row_fits(N, K); }
+
+Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
+    Workspace w{};
+    w.DP = padded_dim(d);
+    w.Kp = padded_k(K);
+    const bool a1d = use_assign_1d(d, K);
+    w.nblk_assign = a1d ? assign_1d_blocks(N) : assign_mfma_blocks(N, w.DP, xt);
+    if (w.nblk_assign < 1) w.nblk_assign = 1;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    const size_t Bz = (size_t)B;
+    w.chat = take(a1d ? 0 : Bz * w.Kp * w.DP * dtype_bytes(xt));
+    w.hnorm = take(a1d ? 0 : Bz * w.Kp * sizeof(float));
+    w.obj_part = take(Bz * w.nblk_assign * sizeof(double));
+    w.labels = take(Bz * N * sizeof(int32_t));
+    w.counts = take(Bz * K * sizeof(int32_t));
+    w.sums = take(Bz * K * d * sizeof(float));
+    w.wsum = take(Bz * K * sizeof(float));
+    w.offsets = take(Bz * (K + 1) * sizeof(int32_t));
+    w.cursor = take(Bz * K * sizeof(int32_t));
+    w.perm = take(Bz * N * sizeof(int32_t));
+    w.piece_seg = take(Bz * segreduce_pieces(B, N) * sizeof(int32_t));
+    w.total = off;
+    return w;
+}
+
+}  // namespace km
+
+using namespace km;
+
+namespace {
+
+constexpr int64_t kMaxD = 256;
+constexpr int64_t kMaxK = 32768;
+constexpr int64_t kMaxB = 65535;
+constexpr int64_t kMaxN = 0x7fffffff;
+
+km_status check_shape(int64_t B, int64_t N, int64_t d, int64_t K, int xt) {
+    if (B < 0 || N < 0) return fail(KM_EINVAL, "negative size: B=%lld N=%lld", (long long)B, (long long)N);
+    if (d < 1 || K < 1) return fail(KM_EINVAL, "d and K must be >= 1 (d=%lld K=%lld)", (long long)d, (long long)K);
+    if (xt != KM_F32 && xt != KM_F16 && xt != KM_BF16) return fail(KM_EUNSUPPORTED, "unknown dtype %d", xt);
+    if (d > kMaxD) return fail(KM_EUNSUPPORTED, "d=%lld > %lld is not supported", (long long)d, (long long)kMaxD);
+    if (K > kMaxK) return fail(KM_EUNSUPPORTED, "K=%lld > %lld is not supported", (long long)K, (long long)kMaxK);
+    if (B > kMaxB) return fail(KM_EUNSUPPORTED, "B=%lld > %lld is not supported", (long long)B, (long long)kMaxB);
+    if (N > kMaxN) return fail(KM_EUNSUPPORTED, "N=%lld >= 2^31 is not supported", (long long)N);
+    int64_t bn, bnd;
+    if (__builtin_mul_overflow(B, N, &bn) || __builtin_mul_overflow(bn, d, &bnd) || bnd > ((int64_t)1 << 46))
+        return fail(KM_EUNSUPPORTED, "B*N*d too large");
+    return KM_OK;
+}
+
+km_status need(const void* p, int64_t n, const char* name) {
+    if (n > 0 && p == nullptr) return fail(KM_EINVAL, "%s is NULL", name);
+    return KM_OK;
+}
+
+km_status check_ws(const Workspace& w, const void* ws, size_t bytes) {
+    if (w.total == 0) return KM_OK;
+    if (ws == nullptr) return fail(KM_EINVAL, "workspace is NULL (%zu bytes needed)", w.total);
+    if ((uintptr_t)ws % 256 != 0) return fail(KM_EINVAL, "workspace must be 256-byte aligned");
+    if (bytes < w.total)
+        return fail(KM_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", bytes, w.total);
+    return KM_OK;
+}
+
+#define KM_TRY(expr)                       \
+    do {                                   \
+        km_status _st = (expr);            \
+        if (_st != KM_OK) return _st;      \
+    } while (0)
+
+#define KM_HIP(expr, where)                              \
+    do {                                                 \
+        hipError_t _e = (expr);                          \
+        if (_e != hipSuccess) return hip_fail(_e, where); \
+    } while (0)
+
+template <typename P>
+P* at(void* ws, size_t off) {
+    return (P*)((char*)ws + off);
+}
+
+// Assignment of all B*N points against C; optional per-block objective
+// partials reduced into obj_out[b * obj_stride].
+km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, const float* C, int64_t K,
+                     const float* w, int32_t* labels, float* min_dist, double* obj_out, int64_t obj_stride,
+                     const Workspace& W, void* ws, hipStream_t s) {
+    double* part = obj_out ? at<double>(ws, W.obj_part) : nullptr;
+    if (use_assign_1d(d, K)) {
+        KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, part, W.nblk_assign, s), "assign_1d");
+    } else {
+        void* chat = at<void>(ws, W.chat);
+        float* hn = at<float>(ws, W.hnorm);
+        KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, chat, hn, s), "prep");
+        KM_HIP(launch_assign_mfma(xt, x, B, N, (int)d, W.DP, chat, hn, K, W.Kp, w, labels, min_dist, part,
+                                  W.nblk_assign, s),
+               "assign_mfma");
+    }
+    if (obj_out) {
+        if (N == 0) {
+            KM_HIP(launch_zero(part, (size_t)B * W.nblk_assign * sizeof(double), s), "zero");
+        }
+        KM_HIP(launch_obj_reduce(part, B, W.nblk_assign, obj_out, obj_stride, s), "obj_reduce");
+    }
+    return KM_OK;
+}
+
+km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts, int32_t* offsets,
+                   int32_t* perm, const Workspace& W, void* ws, hipStream_t s) {
+    KM_HIP(launch_zero(counts, (size_t)B * K * sizeof(int32_t), s), "zero");
+    KM_HIP(launch_sort(labels, B, N, K, counts, offsets, at<int32_t>(ws, W.cursor), perm, s), "sort");
+    return KM_OK;
+}
+
+km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t N, int64_t d,
+                     const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
+                     const Workspace& W, void* ws, hipStream_t s) {
+    int32_t* cnt = counts ? counts : at<int32_t>(ws, W.counts);
+    if (use_update_1d(d, N, K)) {
+        KM_HIP(launch_update_1d_row(xt, x, w, B, N, labels, K, c_old, c_new, cnt, s), "update_1d_row");
+        return KM_OK;
+    }
+    float* sums = at<float>(ws, W.sums);
+    float* wsum = at<float>(ws, W.wsum);
+    // sums and wsum are adjacent in the plan: clear both with one fill
+    KM_HIP(launch_zero(sums, W.offsets - W.sums, s), "zero");
+    int32_t* offsets = at<int32_t>(ws, W.offsets);
+    int32_t* perm = at<int32_t>(ws, W.perm);
+    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, W, ws, s));
+    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr,
+                            at<int32_t>(ws, W.piece_seg), s),
+           "segreduce");
+    KM_HIP(launch_divide(sums, w ? wsum : nullptr, cnt, B, K, (int)d, c_old, c_new, s), "divide");
+    return KM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kmeans_workspace_bytes(int64_t B, int64_t N, int64_t d, int64_t K, km_dtype xt) {
+    if (check_shape(B, N, d, K, (int)xt) != KM_OK) return 0;
+    return plan_workspace(B, N, d, K, (DType)xt).total;
+}
+
+km_status kmeans_assign(const void* x, km_dtype xt, int64_t B, int64_t N, int64_t d, const float* centroids,
+                        int64_t K, const float* weights, int32_t* labels, float* min_dist, double* objective,
+                        void* workspace, size_t workspace_bytes, km_stream stream) {
+    KM_TRY(check_shape(B, N, d, K, (int)xt));
+    KM_TRY(need(x, B * N, "x"));
+    KM_TRY(need(centroids, B, "centroids"));
+    KM_TRY(need(labels, B * N, "labels"));
+    const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
+    KM_TRY(check_ws(W, workspace, workspace_bytes));
+    return run_assign(x, (DType)xt, B, N, d, centroids, K, weights, labels, min_dist, objective, 1, W,
+                      workspace, (hipStream_t)stream);
+}
+
+km_status kmeans_sort_labels(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts,
+                             int32_t* offsets, int32_t* perm, void* workspace, size_t workspace_bytes,
+                             km_stream stream) {
+    KM_TRY(check_shape(B, N, 2, K, KM_F32));
+    KM_TRY(need(labels, B * N, "labels"));
+    // cursors, then whichever outputs the caller left to the workspace; this
+    // never exceeds kmeans_workspace_bytes() of the same B, N, K for any d
+    Workspace W{};
+    size_t off = 0;
+    W.cursor = off;
+    off += align_up((size_t)B * K * sizeof(int32_t));
+    if (!counts) { W.counts = off; off += align_up((size_t)B * K * sizeof(int32_t)); }
+    if (!offsets) { W.offsets = off; off += align_up((size_t)B * (K + 1) * sizeof(int32_t)); }
+    if (!perm) { W.perm = off; off += align_up((size_t)B * N * sizeof(int32_t)); }
+    W.total = off;
+    KM_TRY(check_ws(W, workspace, workspace_bytes));
+    int32_t* cnt = counts ? counts : at<int32_t>(workspace, W.counts);
+    int32_t* ofs = offsets ? offsets : at<int32_t>(workspace, W.offsets);
+    int32_t* pm = perm ? perm : at<int32_t>(workspace, W.perm);
+    return run_sort(labels, B, N, K, cnt, ofs, pm, W, workspace, (hipStream_t)stream);
+}
+
+km_status kmeans_update(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d,
+                        const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
+                        void* workspace, size_t workspace_bytes, km_stream stream) {
+    KM_TRY(check_shape(B, N, d, K, (int)xt));
+    KM_TRY(need(x, B * N, "x"));
+    KM_TRY(need(labels, B * N, "labels"));
+    KM_TRY(need(c_old, B, "c_old"));
+    KM_TRY(need(c_new, B, "c_new"));
+    const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
+    KM_TRY(check_ws(W, workspace, workspace_bytes));
+    return run_update(x, (DType)xt, weights, B, N, d, labels, K, c_old, c_new, counts, W, workspace,
+                      (hipStream_t)stream);
+}
+
+km_status kmeans_fit(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d, int64_t K,
+                     const float* init, int32_t n_iter, float* centroids, int32_t* labels, int32_t* counts,
+                     double* objective, void* workspace, size_t workspace_bytes, km_stream stream) {
+    KM_TRY(check_shape(B, N, d, K, (int)xt));
+    if (n_iter < 0) return fail(KM_EINVAL, "n_iter=%d < 0", n_iter);
+    KM_TRY(need(x, B * N, "x"));
+    KM_TRY(need(init, B, "init"));
+    KM_TRY(need(centroids, B, "centroids"));
+    const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
+    KM_TRY(check_ws(W, workspace, workspace_bytes));
+    hipStream_t s = (hipStream_t)stream;
+    if (init != centroids && B > 0)
+        KM_HIP(hipMemcpyAsync(centroids, init, (size_t)B * K * d * sizeof(float), hipMemcpyDeviceToDevice, s),
+               "copy init");
+    int32_t* lab = labels ? labels : at<int32_t>(workspace, W.labels);
+    for (int32_t t = 0; t < n_iter; ++t) {
+        KM_TRY(run_assign(x, (DType)xt, B, N, d, centroids, K, weights, lab, nullptr,
+                          objective ? objective + t : nullptr, n_iter, W, workspace, s));
+        KM_TRY(run_update(x, (DType)xt, weights, B, N, d, lab, K, centroids, centroids, counts, W, workspace, s));
+    }
+    return KM_OK;
+}
+
+const char* kmeans_status_str(km_status st) {
+    switch (st) {
+        case KM_OK: return "ok";
+        case KM_EINVAL: return "invalid argument";
+        case KM_EUNSUPPORTED: return "unsupported shape or dtype";
+        case KM_EWORKSPACE: return "workspace too small";
+        case KM_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kmeans_last_error(void) { return g_last_error.c_str(); }
+
+int kmeans_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the kernels and the host entry points of
+// the gfx950 k-means library.  Not part of the public ABI (include/kmeans.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace km {
+
+// Storage types of the points.
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+inline int dtype_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bf16_t;  // bfloat16 bits in memory
+
+constexpr int kWave = 64;
+
+// Padded point dimension used by the matrix-core assignment for a given d.
+inline int padded_dim(int64_t d) {
+    if (d <= 16) return 16;
+    if (d <= 32) return 32;
+    if (d <= 64) return 64;
+    if (d <= 128) return 128;
+    return 256;
+}
+
+// Rows of the padded centroid matrix: K rounded up to the centroid tile.
+inline int64_t padded_k(int64_t K) { return (K + 63) / 64 * 64; }
+
+// Element conversions -------------------------------------------------------
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Workspace layout ----------------------------------------------------------
+// One layout serves every entry point; all regions are 256-byte aligned.
+struct Workspace {
+    size_t chat;       // [B][Kp][DP] centroids in the point dtype (zero padded)
+    size_t hnorm;      // [B][Kp] float: -0.5 * ||c_hat||^2 (-inf for padding rows)
+    size_t obj_part;   // [B][nblk_assign] double: per-block objective partials
+    size_t labels;     // [B][N] int32: labels of the current assignment (fit)
+    size_t counts;     // [B][K] int32
+    size_t offsets;    // [B][K+1] int32
+    size_t cursor;     // [B][K] int32: scatter cursors
+    size_t perm;       // [B][N] int32
+    size_t sums;       // [B][K][d] float: segment sums
+    size_t wsum;       // [B][K] float: segment weight sums (weighted update)
+    size_t piece_seg;  // [B][npieces] int32: first segment of each reduction piece
+    size_t total;
+    int DP;
+    int64_t Kp;
+    int64_t nblk_assign;
+};
+
+Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt);
+
+// Launchers (one per kernel family).  All take the caller's stream and
+// return the launch status.
+hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,
+                       void* chat, float* hnorm, hipStream_t s);
+
+hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
+                              const void* chat, const float* hnorm, int64_t K, int64_t Kp,
+                              const float* w, int32_t* labels, float* min_dist,
+                              double* obj_part, int64_t nblk, hipStream_t s);
+int64_t assign_mfma_blocks(int64_t N, int DP, DType xt);
+
+hipError_t launch_assign_1d(DType xt, const void* x, int64_t B, int64_t N, const float* C,
+                            int64_t K, const float* w, int32_t* labels, float* min_dist,
+                            double* obj_part, int64_t nblk, hipStream_t s);
+int64_t assign_1d_blocks(int64_t N);
+bool assign_1d_supports(int64_t K);
+
+hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double* out,
+                             int64_t out_stride, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
+                       int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* perm,
+                       hipStream_t s);
+
+hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
+                            const int32_t* perm, const int32_t* offsets, int64_t K,
+                            float* sums, float* wsum, int32_t* piece_seg, hipStream_t s);
+int64_t segreduce_pieces(int64_t B, int64_t N);
+
+hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* counts,
+                         int64_t B, int64_t K, int d, const float* c_old, float* c_new,
+                         hipStream_t s);
+
+// Scalar points: whole-row on-chip update (sort-inverse in LDS).
+bool update_1d_row_fits(int64_t N, int64_t K);
+hipError_t launch_update_1d_row(DType xt, const void* x, const float* w, int64_t B, int64_t N,
+                                const int32_t* labels, int64_t K, const float* c_old,
+                                float* c_new, int32_t* counts, hipStream_t s);
+
+}  // namespace km

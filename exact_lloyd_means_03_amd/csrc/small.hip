@@ -1,0 +1,133 @@
+// Small per-centroid kernels of the Lloyd iteration on gfx950:
+//   - centroid prep: round the float32 centroids to the point dtype (the
+//     matrix-core operand) and precompute -||c_hat||^2 / 2, the centroid term
+//     of ||x||^2 - 2 x.c + ||c||^2 (technologypulse.uk "Flash-KMeans"
+//     article, bottleneck 1: distances fused with the argmin);
+//   - the divide: centroid = segment sum / segment weight, and an empty
+//     cluster keeps its previous centroid (daily.steinslab.io "e-means"
+//     article, "Breaking 70 Years of Full-Batch Inertia": centroid S_j / N_j);
+//   - the deterministic per-batch sum of the per-block objective partials;
+//   - a fill kernel (used instead of memset so the enqueued work can be
+//     captured into a graph).
+#include "common.h"
+
+namespace km {
+
+// One wave per padded centroid row; 4 rows per 256-thread block.
+template <typename T>
+__global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64_t BKp, int64_t K,
+                                              int64_t Kp, int d, int DP, T* __restrict__ chat,
+                                              float* __restrict__ hnorm) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= BKp) return;
+    const int64_t b = row / Kp, j = row - b * Kp;
+    const bool real = j < K;
+    const float* c = C + (b * K + j) * (int64_t)d;
+    T* out = chat + row * (int64_t)DP;
+    float ss = 0.f;
+    for (int k = lane; k < DP; k += 64) {
+        float v = (real && k < d) ? c[k] : 0.f;
+        float r;
+        if constexpr (sizeof(T) == 4) {
+            r = v;
+            out[k] = v;
+        } else if constexpr (__is_same(T, _Float16)) {
+            _Float16 h = (_Float16)v;  // v_cvt_f16_f32: round to nearest even
+            r = (float)h;
+            out[k] = h;
+        } else {
+            uint16_t h = f32_to_bf16_rne(v);
+            r = bf16_to_f32(h);
+            out[k] = h;
+        }
+        ss = fmaf(r, r, ss);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) hnorm[row] = real ? -0.5f * ss : -INFINITY;
+}
+
+hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,
+                       void* chat, float* hnorm, hipStream_t s) {
+    const int64_t rows = B * Kp;
+    if (rows == 0) return hipSuccess;
+    dim3 grid((unsigned)((rows + 3) / 4));
+    if (xt == DType::F32)
+        hipLaunchKernelGGL(k_prep<float>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, (float*)chat, hnorm);
+    else if (xt == DType::F16)
+        hipLaunchKernelGGL(k_prep<_Float16>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, (_Float16*)chat, hnorm);
+    else
+        hipLaunchKernelGGL(k_prep<bf16_t>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, (bf16_t*)chat, hnorm);
+    return hipGetLastError();
+}
+
+// c_new = S / W for non-empty clusters, c_old otherwise.  W is the weight sum
+// (weighted) or the count.  IEEE float32 division (no fast-math).
+__global__ __launch_bounds__(256) void k_divide(const float* __restrict__ sums,
+                                                const float* __restrict__ wsum,
+                                                const int32_t* __restrict__ counts, int64_t BK, int d,
+                                                const float* c_old, float* c_new) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = BK * d;
+    if (i >= total) return;
+    const int64_t bj = i / d;
+    const int32_t n = counts[bj];
+    float v;
+    if (n > 0) {
+        const float W = wsum ? wsum[bj] : (float)n;
+        v = sums[i] / W;
+    } else {
+        v = c_old[i];
+    }
+    c_new[i] = v;
+}
+
+hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* counts, int64_t B,
+                         int64_t K, int d, const float* c_old, float* c_new, hipStream_t s) {
+    const int64_t total = B * K * d;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_divide, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, sums, wsum,
+                       counts, B * K, d, c_old, c_new);
+    return hipGetLastError();
+}
+
+// One block per batch: fixed-order strided sums, then a fixed-order tree.
+__global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t nblk,
+                                                    double* __restrict__ out, int64_t out_stride) {
+    __shared__ double red[256];
+    const int64_t b = blockIdx.x;
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < nblk; i += 256) acc += part[b * nblk + i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[b * out_stride] = red[0];
+}
+
+hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double* out,
+                             int64_t out_stride, hipStream_t s) {
+    if (B == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_obj_reduce, dim3((unsigned)B), dim3(256), 0, s, part, nblk, out, out_stride);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ p, int64_t n_words) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (; i < n_words; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+    const int64_t words = (int64_t)(bytes / 4);
+    if (words == 0) return hipSuccess;
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, words);
+    return hipGetLastError();
+}
+
+}  // namespace km

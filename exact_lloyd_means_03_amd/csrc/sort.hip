@@ -1,0 +1,156 @@
+// Argsort of the label vector by cluster id: the first half of the
+// sort-inverse update (technologypulse.uk "Flash-KMeans" article,
+// bottleneck 2; wispaper.ai "Flash-KMeans" blog, "Sort-Inverse Update").
+// After it, the indices of the points of cluster j form the contiguous
+// segment perm[offsets[j] .. offsets[j+1]); the points themselves are never
+// moved.
+//
+// Labels are small integers (< K), so a counting sort replaces the general
+// argsort:
+//   1. k_count   -- each block histograms a chunk of labels in LDS and adds
+//                   its non-zero bins to counts[b][.] (one global atomic per
+//                   non-empty bin per chunk);
+//   2. k_scan    -- exclusive prefix of counts -> offsets, and scatter cursors;
+//   3. k_scatter -- each block re-histograms its chunk, reserves one
+//                   contiguous run per non-empty bin with a single global
+//                   atomic on that bin's cursor, then places its indices in
+//                   the run with LDS atomics.
+// Runs of different chunks land in a segment in arrival order, so the order
+// inside a segment is unspecified; the set of indices is exact.
+// Labels outside [0, K) are skipped by every pass.
+#include "common.h"
+
+namespace km {
+
+constexpr int kSortThreads = 256;
+
+static int64_t sort_chunk(int64_t B, int64_t N, int64_t K) {
+    int64_t ch = 4096;
+    while (ch < K) ch *= 2;
+    while (ch < (1 << 20) && B * ((N + ch - 1) / ch) > 2048) ch *= 2;
+    return ch;
+}
+
+__device__ __forceinline__ void lds_histogram(const int32_t* __restrict__ L, int64_t i0, int64_t i1,
+                                              int K, int32_t* s_h) {
+    const int tid = threadIdx.x;
+    int64_t i = i0 + tid;
+    for (; i + 3 * kSortThreads < i1; i += 4 * kSortThreads) {
+        const int32_t l0 = L[i], l1 = L[i + kSortThreads], l2 = L[i + 2 * kSortThreads],
+                      l3 = L[i + 3 * kSortThreads];
+        if ((uint32_t)l0 < (uint32_t)K) atomicAdd(&s_h[l0], 1);
+        if ((uint32_t)l1 < (uint32_t)K) atomicAdd(&s_h[l1], 1);
+        if ((uint32_t)l2 < (uint32_t)K) atomicAdd(&s_h[l2], 1);
+        if ((uint32_t)l3 < (uint32_t)K) atomicAdd(&s_h[l3], 1);
+    }
+    for (; i < i1; i += kSortThreads) {
+        const int32_t l = L[i];
+        if ((uint32_t)l < (uint32_t)K) atomicAdd(&s_h[l], 1);
+    }
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_count(const int32_t* __restrict__ labels, int64_t N,
+                                                        int K, int64_t CH, int32_t* __restrict__ counts) {
+    extern __shared__ int32_t s_h[];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t i0 = (int64_t)blockIdx.x * CH;
+    const int64_t i1 = (i0 + CH < N) ? i0 + CH : N;
+    for (int j = tid; j < K; j += kSortThreads) s_h[j] = 0;
+    __syncthreads();
+    lds_histogram(labels + b * N, i0, i1, K, s_h);
+    __syncthreads();
+    for (int j = tid; j < K; j += kSortThreads) {
+        const int32_t v = s_h[j];
+        if (v) atomicAdd(&counts[b * K + j], v);
+    }
+}
+
+// One block per batch: exclusive scan of K counts.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ counts, int K,
+                                               int32_t* __restrict__ offsets, int32_t* __restrict__ cursor) {
+    __shared__ int32_t s_part[1024];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int per = (K + 1023) / 1024;
+    const int j0 = tid * per;
+    const int j1 = (j0 + per < K) ? j0 + per : K;
+    int32_t s = 0;
+    for (int j = j0; j < j1; ++j) s += counts[b * K + j];
+    s_part[tid] = s;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the 1024 partial sums
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int32_t v = tid >= o ? s_part[tid - o] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    int32_t run = s_part[tid] - s;  // exclusive prefix of this thread's range
+    for (int j = j0; j < j1; ++j) {
+        offsets[b * (K + 1) + j] = run;
+        cursor[b * K + j] = run;
+        run += counts[b * K + j];
+    }
+    if (tid == 1023) offsets[b * (K + 1) + K] = s_part[1023];
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_scatter(const int32_t* __restrict__ labels, int64_t N,
+                                                          int K, int64_t CH, int32_t* __restrict__ cursor,
+                                                          int32_t* __restrict__ perm) {
+    extern __shared__ int32_t s_h[];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t i0 = (int64_t)blockIdx.x * CH;
+    const int64_t i1 = (i0 + CH < N) ? i0 + CH : N;
+    const int32_t* L = labels + b * N;
+    for (int j = tid; j < K; j += kSortThreads) s_h[j] = 0;
+    __syncthreads();
+    lds_histogram(L, i0, i1, K, s_h);
+    __syncthreads();
+    // reserve this chunk's run in every non-empty segment
+    for (int j = tid; j < K; j += kSortThreads) {
+        const int32_t v = s_h[j];
+        if (v) s_h[j] = atomicAdd(&cursor[b * K + j], v);
+    }
+    __syncthreads();
+    int32_t* P = perm + b * N;
+    for (int64_t i = i0 + tid; i < i1; i += kSortThreads) {
+        const int32_t l = L[i];
+        if ((uint32_t)l < (uint32_t)K) {
+            const int32_t pos = atomicAdd(&s_h[l], 1);
+            P[pos] = (int32_t)i;
+        }
+    }
+}
+
+hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts,
+                       int32_t* offsets, int32_t* cursor, int32_t* perm, hipStream_t s) {
+    // counts must be zero on entry (the caller clears it with the other accumulators)
+    if (B == 0) return hipSuccess;
+    const size_t lds = (size_t)K * sizeof(int32_t);
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)k_count, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        (void)hipFuncSetAttribute((const void*)k_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr_set = true;
+    }
+    hipError_t e;
+    if (N > 0) {
+        const int64_t CH = sort_chunk(B, N, K);
+        dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
+        hipLaunchKernelGGL(k_count, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, counts);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), 0, s, counts, (int)K, offsets, cursor);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (N > 0) {
+        const int64_t CH = sort_chunk(B, N, K);
+        dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
+        hipLaunchKernelGGL(k_scatter, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, cursor, perm);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace km

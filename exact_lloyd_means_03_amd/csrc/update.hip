@@ -1,0 +1,315 @@
+// Second half of the sort-inverse update: reduce each cluster's contiguous
+// segment of perm on chip and add it to the cluster's sums with one atomic
+// per coordinate per reduced piece (technologypulse.uk "Flash-KMeans"
+// article, bottleneck 2: one atomic per segment, O((K + N/B) d) atomics
+// instead of O(N d); wispaper.ai "Flash-KMeans" blog, "Sort-Inverse
+// Update": segmented reductions instead of scattered writes).
+//
+// gfx950 layout (ours): the sorted positions are cut into pieces of TW rows,
+// one piece per 64-lane wave.  A point row is read with 16-byte loads by LPR
+// lanes (d=128 bf16: 16 lanes), so one wave gathers 64/LPR rows per step and
+// keeps 4 steps of loads in flight.  At a segment boundary the wave reduces
+// its row groups with cross-lane shuffles and issues d float atomics.  The
+// first segment of every piece is precomputed by the scan, and the following
+// segment boundaries come from a 64-entry window of offsets held one per
+// lane, so a wave never searches device memory serially.
+//
+// Scalar points (d == 1) with a row that fits in LDS take a whole-row kernel
+// instead: the row's (x, w) pairs are placed in cluster order in LDS and each
+// segment is summed by one wave in float64.
+#include "common.h"
+
+namespace km {
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p) {
+    if constexpr (sizeof(T) == 4) return *p;
+    else if constexpr (__is_same(T, _Float16)) return (float)*p;
+    else return bf16_to_f32(*p);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a row -> EPL floats.
+template <typename T>
+__device__ __forceinline__ void ld_vec(const T* p, float* out) {
+    const u32x4 u = *(const u32x4*)p;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(u[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint16_t lo = (uint16_t)(u[e] & 0xffffu), hi = (uint16_t)(u[e] >> 16);
+            if constexpr (__is_same(T, _Float16)) {
+                out[2 * e] = (float)__builtin_bit_cast(_Float16, lo);
+                out[2 * e + 1] = (float)__builtin_bit_cast(_Float16, hi);
+            } else {
+                out[2 * e] = bf16_to_f32(lo);
+                out[2 * e + 1] = bf16_to_f32(hi);
+            }
+        }
+    }
+}
+
+// VEC: lane li of a row group reads elements [li*EPL, li*EPL + EPL) with one
+// 16-byte load; otherwise it reads elements li + LPR*m, m < 4.
+template <typename T, bool VEC, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, const float* __restrict__ w,
+                                                   int64_t N, int d, int lpr_shift,
+                                                   const int32_t* __restrict__ perm,
+                                                   const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ piece_seg, int64_t npieces,
+                                                   int K, int TW, float* __restrict__ sums,
+                                                   float* __restrict__ wsum) {
+    constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 4;
+    constexpr int U = 4;  // row steps in flight
+    const int lane = threadIdx.x & 63;
+    const int64_t piece = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t b = blockIdx.y;
+    if (piece >= npieces) return;
+    const int32_t* offb = offsets + b * (K + 1);
+    const int32_t total = offb[K];
+    const int64_t q0 = piece * (int64_t)TW;
+    if (q0 >= total) return;
+    const int32_t q1 = (int32_t)((q0 + TW < total) ? q0 + TW : total);
+    const int LPR = 1 << lpr_shift, RPW = 64 >> lpr_shift;
+    const int gl = lane >> lpr_shift, li = lane & (LPR - 1);
+    const int nvec = VEC ? d / EPL : 0;
+    const bool active = VEC ? (li < nvec) : true;
+    const T* Xb = X + b * N * (int64_t)d;
+    const float* wb = WEIGHTED ? w + b * N : nullptr;
+    const int32_t* pb = perm + b * N;
+
+    // window of offsets: lane l holds offsets[wbase + l] (INT_MAX past K)
+    int wbase = piece_seg[b * npieces + piece];
+    int32_t win = (wbase + lane <= K) ? offb[wbase + lane] : 0x7fffffff;
+    int32_t q = (int32_t)q0;
+    while (q < q1) {
+        // segment containing q: the last j with offsets[j] <= q
+        unsigned long long m = __ballot(win > q);
+        while (m == 0ull) {
+            wbase += 63;
+            win = (wbase + lane <= K) ? offb[wbase + lane] : 0x7fffffff;
+            m = __ballot(win > q);
+        }
+        const int l = __ffsll((long long)m) - 1;  // first lane with offsets > q (l >= 1)
+        const int j = wbase + l - 1;
+        const int32_t send = __shfl(win, l, 64);
+        const int32_t e = send < q1 ? send : q1;
+
+        float acc[EPL];
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
+        float wacc = 0.f;
+        for (int32_t r = q + gl; r < e; r += RPW * U) {
+            int32_t idx[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t rr = r + u * RPW;
+                idx[u] = rr < e ? pb[rr] : -1;
+            }
+            float v[U][EPL];
+            float wi[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = idx[u] >= 0;
+                const T* row = Xb + (int64_t)(ok ? idx[u] : 0) * d;
+                if constexpr (VEC) {
+                    if (ok && active) ld_vec<T>(row + li * EPL, v[u]);
+                    else {
+#pragma unroll
+                        for (int t = 0; t < EPL; ++t) v[u][t] = 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < EPL; ++t) {
+                        const int k = li + LPR * t;
+                        v[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
+                    }
+                }
+                if constexpr (WEIGHTED) wi[u] = ok ? wb[idx[u]] : 0.f;
+                else wi[u] = ok ? 1.f : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) {
+                    if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[u][t], acc[t]);
+                    else acc[t] += v[u][t];
+                }
+                wacc += wi[u];
+            }
+        }
+        if (e > q) {
+            // reduce the row groups of the wave, then one atomic per coordinate
+            for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
+                if constexpr (WEIGHTED) wacc += __shfl_xor(wacc, o, 64);
+            }
+            float* sj = sums + (b * K + j) * (int64_t)d;
+            if (gl == 0 && active) {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) {
+                    const int k = VEC ? li * EPL + t : li + LPR * t;
+                    if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
+                }
+            }
+            if constexpr (WEIGHTED) {
+                if (lane == 0) unsafeAtomicAdd(wsum + b * K + j, wacc);
+            }
+        }
+        q = e;
+    }
+}
+
+// Rows per wave piece: enough pieces to fill the chip, and long pieces when
+// there is plenty of work (fewer atomics on the largest clusters).
+int segreduce_tw(int64_t B, int64_t N) {
+    int64_t tw = 256;
+    while (tw < 4096 && B * N / (tw * 2) >= 8192) tw *= 2;
+    return (int)tw;
+}
+
+// Also used by the scan: first segment of every piece.
+__global__ __launch_bounds__(256) void k_piece_seg(const int32_t* __restrict__ offsets, int K, int TW,
+                                                   int64_t npieces, int32_t* __restrict__ piece_seg) {
+    const int64_t b = blockIdx.y;
+    const int32_t* offb = offsets + b * (K + 1);
+    for (int j = blockIdx.x * 256 + threadIdx.x; j < K; j += gridDim.x * 256) {
+        const int64_t lo = offb[j], hi = offb[j + 1];
+        // pieces whose first row lies in [lo, hi)
+        for (int64_t p = (lo + TW - 1) / TW; p * TW < hi && p < npieces; ++p) piece_seg[b * npieces + p] = j;
+    }
+}
+
+hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
+                            const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
+                            float* wsum, int32_t* piece_seg, hipStream_t s) {
+    if (B == 0 || N == 0) return hipSuccess;
+    const int TW = segreduce_tw(B, N);
+    const int64_t npieces = (N + TW - 1) / TW;
+    hipLaunchKernelGGL(k_piece_seg, dim3((unsigned)((K + 255) / 256 < 1024 ? (K + 255) / 256 : 1024), (unsigned)B),
+                       dim3(256), 0, s, offsets, (int)K, TW, npieces, piece_seg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int esz = dtype_bytes(xt);
+    const int epl = 16 / esz;
+    const bool vec = (d % epl == 0) && ((uintptr_t)x % 16 == 0) && (d / epl <= 64);
+    int lanes = vec ? d / epl : (d < 64 ? d : 64);
+    int shift = 0;
+    while ((1 << shift) < lanes) ++shift;
+    dim3 grid((unsigned)((npieces + 3) / 4), (unsigned)B);
+#define KM_SEG(T, V, W)                                                                                   \
+    hipLaunchKernelGGL((k_segreduce<T, V, W>), grid, dim3(256), 0, s, (const T*)x, w, N, d, shift, perm, \
+                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum)
+#define KM_SEG_T(T)                      \
+    if (vec) {                           \
+        if (w) KM_SEG(T, true, true);    \
+        else KM_SEG(T, true, false);     \
+    } else {                             \
+        if (w) KM_SEG(T, false, true);   \
+        else KM_SEG(T, false, false);    \
+    }
+    if (xt == DType::F32) { KM_SEG_T(float) }
+    else if (xt == DType::F16) { KM_SEG_T(_Float16) }
+    else { KM_SEG_T(bf16_t) }
+#undef KM_SEG_T
+#undef KM_SEG
+    return hipGetLastError();
+}
+
+int64_t segreduce_pieces(int64_t B, int64_t N) {
+    const int TW = segreduce_tw(B, N);
+    return (N + TW - 1) / TW;
+}
+
+// ---------------------------------------------------------------------------
+// d == 1, whole row on chip.
+constexpr int kRow1DMaxN = 8192;
+constexpr int kRow1DMaxK = 256;
+
+bool update_1d_row_fits(int64_t N, int64_t K) { return N <= kRow1DMaxN && K <= kRow1DMaxK; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_update_1d_row(const T* __restrict__ X, const float* __restrict__ w,
+                                                       int N, const int32_t* __restrict__ labels, int K,
+                                                       const float* c_old, float* c_new,
+                                                       int32_t* __restrict__ counts) {
+    __shared__ int32_t s_cnt[kRow1DMaxK];
+    __shared__ int32_t s_off[kRow1DMaxK + 1];
+    __shared__ int32_t s_cur[kRow1DMaxK];
+    __shared__ float s_x[kRow1DMaxN];
+    __shared__ float s_w[kRow1DMaxN];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t b = blockIdx.x;
+    const int32_t* L = labels + b * N;
+    const T* Xb = X + b * N;
+    for (int j = tid; j < K; j += 256) s_cnt[j] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += 256) {
+        const int32_t l = L[i];
+        if ((uint32_t)l < (uint32_t)K) atomicAdd(&s_cnt[l], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int32_t run = 0;
+        for (int j = 0; j < K; ++j) {
+            s_off[j] = run;
+            s_cur[j] = run;
+            run += s_cnt[j];
+        }
+        s_off[K] = run;
+    }
+    __syncthreads();
+    // place (x, w) in cluster order
+    for (int i = tid; i < N; i += 256) {
+        const int32_t l = L[i];
+        if ((uint32_t)l < (uint32_t)K) {
+            const int32_t pos = atomicAdd(&s_cur[l], 1);
+            s_x[pos] = ld_elem<T>(Xb + i);
+            s_w[pos] = w ? w[b * N + i] : 1.f;
+        }
+    }
+    __syncthreads();
+    // one wave per segment: float64 sums (order-insensitive to float32 output precision)
+    for (int j = wave; j < K; j += 4) {
+        const int32_t lo = s_off[j], hi = s_off[j + 1];
+        double S = 0.0, W = 0.0;
+        for (int32_t r = lo + lane; r < hi; r += 64) {
+            const double wi = s_w[r];
+            S += wi * (double)s_x[r];
+            W += wi;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            S += __shfl_xor(S, o, 64);
+            W += __shfl_xor(W, o, 64);
+        }
+        if (lane == 0) {
+            const int32_t n = hi - lo;
+            c_new[b * K + j] = n > 0 ? (float)(S / W) : c_old[b * K + j];
+            if (counts) counts[b * K + j] = n;
+        }
+    }
+}
+
+hipError_t launch_update_1d_row(DType xt, const void* x, const float* w, int64_t B, int64_t N,
+                                const int32_t* labels, int64_t K, const float* c_old, float* c_new,
+                                int32_t* counts, hipStream_t s) {
+    if (B == 0) return hipSuccess;
+    if (!update_1d_row_fits(N, K)) return hipErrorInvalidValue;
+    if (xt == DType::F32)
+        hipLaunchKernelGGL(k_update_1d_row<float>, dim3((unsigned)B), dim3(256), 0, s, (const float*)x, w,
+                           (int)N, labels, (int)K, c_old, c_new, counts);
+    else if (xt == DType::F16)
+        hipLaunchKernelGGL(k_update_1d_row<_Float16>, dim3((unsigned)B), dim3(256), 0, s, (const _Float16*)x,
+                           w, (int)N, labels, (int)K, c_old, c_new, counts);
+    else
+        hipLaunchKernelGGL(k_update_1d_row<bf16_t>, dim3((unsigned)B), dim3(256), 0, s, (const bf16_t*)x, w,
+                           (int)N, labels, (int)K, c_old, c_new, counts);
+    return hipGetLastError();
+}
+
+}  // namespace km

@@ -1,0 +1,150 @@
+/*
+ * kmeans.h -- C ABI of the MI355X (gfx950) exact Lloyd k-means library.
+ *
+ * One Lloyd iteration is an assignment stage followed by an update stage
+ * (technologypulse.uk "Flash-KMeans" article, section "math unchanged,
+ * dataflow changed").  The library computes the textbook result; only the
+ * data flow differs:
+ *
+ *   - assignment: the squared distance ||x||^2 - 2 x.c + ||c||^2 is computed
+ *     tile by tile on the matrix cores and reduced on the fly to the running
+ *     nearest centroid, so the N x K distance matrix never reaches device
+ *     memory (same article, "bottleneck 1"; wispaper.ai "Flash-KMeans" blog,
+ *     "FlashAssign: Materialization-Free Assignment").  Scalar points (d = 1)
+ *     take a binary search over the sorted centroids instead.
+ *   - update: the label vector is argsorted by cluster id so that each cluster
+ *     is a contiguous segment, every segment is reduced on chip, and each
+ *     reduced piece issues one atomic add per coordinate; the point matrix is
+ *     never permuted in memory (technologypulse.uk article, "bottleneck 2";
+ *     wispaper.ai blog, "Sort-Inverse Update").  The new centroid is the mean
+ *     of its points (daily.steinslab.io "e-means" article, "Breaking 70 Years
+ *     of Full-Batch Inertia": centroid = S_j / N_j); a cluster with no points
+ *     keeps its previous centroid.
+ *   - optional per-point sample weights, as in the per-row weighted 1D
+ *     clustering of github LeanModels/LeanQuant issue #1 ("1D k-means"):
+ *     the assignment ignores them, the centroid is sum(w x) / sum(w) and the
+ *     objective is sum(w * distance).
+ *
+ * Conventions shared by every entry point:
+ *   - Layouts are row-major and contiguous: points x [B, N, d] of dtype xt,
+ *     centroids [B, K, d] float32, labels [B, N] int32, counts [B, K] int32,
+ *     weights [B, N] float32.  B independent problems are solved in one call.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates or frees device memory: scratch space is the
+ *     caller's workspace of at least kmeans_workspace_bytes() bytes, aligned
+ *     to 256 bytes.  Calls that share one workspace must not overlap in time.
+ *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL is the
+ *     default stream) and return without synchronizing.  Arguments are
+ *     checked on the host before anything is enqueued; on an error nothing is
+ *     enqueued and the status says why (kmeans_last_error() has the detail).
+ *     Faults inside kernels surface at the caller's next synchronization.
+ *   - Supported shapes: d == 1 (scalar path), or 2 <= d <= 256 (matrix-core
+ *     path; d is zero-padded internally to 16, 32, 64, 128 or 256, which does
+ *     not change any distance).  1 <= K <= 32768.  N < 2^31.  B, N may be 0.
+ *   - Centroids are float32 state.  Distances use the centroids rounded
+ *     (IEEE round-to-nearest-even) to the point dtype, because that is the
+ *     matrix-core operand; products accumulate in float32.  Ties between
+ *     equally near centroids go to the smallest index.
+ *   - Inputs must be finite; weights, when given, must be positive.
+ */
+#ifndef KMEANS_MI355X_H
+#define KMEANS_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KM_API __attribute__((visibility("default")))
+#else
+#define KM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KM_F32 = 0, KM_F16 = 1, KM_BF16 = 2 } km_dtype;
+
+typedef enum {
+    KM_OK = 0,
+    KM_EINVAL = 1,        /* null pointer, negative size, misaligned workspace, ... */
+    KM_EUNSUPPORTED = 2,  /* a shape or dtype outside the supported set */
+    KM_EWORKSPACE = 3,    /* workspace smaller than kmeans_workspace_bytes() */
+    KM_EHIP = 4           /* the HIP runtime refused a launch */
+} km_status;
+
+typedef void *km_stream; /* hipStream_t */
+
+/* Bytes of workspace any entry point needs for these shapes (0 on invalid
+ * shapes).  One workspace of this size serves kmeans_assign, kmeans_update,
+ * kmeans_sort_labels and kmeans_fit. */
+KM_API size_t kmeans_workspace_bytes(int64_t B, int64_t N, int64_t d, int64_t K, km_dtype xt);
+
+/* Assignment stage (fused distance + running argmin).
+ *   x          [B,N,d] points of dtype xt.
+ *   centroids  [B,K,d] float32.
+ *   weights    [B,N] float32 or NULL; used only for the objective.
+ *   labels     out [B,N] int32: index of the nearest centroid.
+ *   min_dist   out [B,N] float32 or NULL: squared distance to it, clamped at 0.
+ *   objective  out [B] float64 or NULL: sum_i w_i * min_dist_i per batch.
+ * Reads x once; writes no N x K data. */
+KM_API km_status kmeans_assign(const void *x, km_dtype xt, int64_t B, int64_t N, int64_t d,
+                        const float *centroids, int64_t K, const float *weights,
+                        int32_t *labels, float *min_dist, double *objective,
+                        void *workspace, size_t workspace_bytes, km_stream stream);
+
+/* Argsort step of the update: groups the point indices of each batch by
+ * label.
+ *   labels   [B,N] int32; a label outside [0, K) belongs to no cluster.
+ *   counts   out [B,K] int32: points per cluster.
+ *   offsets  out [B,K+1] int32: exclusive prefix of counts; offsets[b][K] is
+ *            the number of labelled points.
+ *   perm     out [B,N] int32: perm[b][offsets[b][j] .. offsets[b][j+1]) are
+ *            the indices i of batch b with labels[b][i] == j, in an
+ *            unspecified order; entries from offsets[b][K] on are not written.
+ * May be NULL: none of counts / offsets / perm (they then live in the
+ * workspace, which makes the call a no-op for the caller). */
+KM_API km_status kmeans_sort_labels(const int32_t *labels, int64_t B, int64_t N, int64_t K,
+                             int32_t *counts, int32_t *offsets, int32_t *perm,
+                             void *workspace, size_t workspace_bytes, km_stream stream);
+
+/* Update stage (sort-inverse segmented reduction, then the divide).
+ *   x        [B,N,d] points of dtype xt; weights [B,N] float32 or NULL.
+ *   labels   [B,N] int32 (labels outside [0, K) are skipped).
+ *   c_old    [B,K,d] float32: kept for clusters with no point.
+ *   c_new    out [B,K,d] float32; may alias c_old.
+ *   counts   out [B,K] int32 or NULL: points per cluster. */
+KM_API km_status kmeans_update(const void *x, km_dtype xt, const float *weights,
+                        int64_t B, int64_t N, int64_t d, const int32_t *labels, int64_t K,
+                        const float *c_old, float *c_new, int32_t *counts,
+                        void *workspace, size_t workspace_bytes, km_stream stream);
+
+/* n_iter Lloyd iterations (assignment, then update) from init.
+ *   init       [B,K,d] float32 (may alias centroids).
+ *   centroids  out [B,K,d] float32: after the last update.
+ *   labels     out [B,N] int32 or NULL: the last assignment.
+ *   counts     out [B,K] int32 or NULL: the last update.
+ *   objective  out [B,n_iter] float64 or NULL: objective of assignment t
+ *              (computed with the centroids that assignment used).
+ * No tolerance, no early stop, no host synchronization.  n_iter == 0 copies
+ * init to centroids. */
+KM_API km_status kmeans_fit(const void *x, km_dtype xt, const float *weights,
+                     int64_t B, int64_t N, int64_t d, int64_t K,
+                     const float *init, int32_t n_iter,
+                     float *centroids, int32_t *labels, int32_t *counts, double *objective,
+                     void *workspace, size_t workspace_bytes, km_stream stream);
+
+/* Static description of a status code. */
+KM_API const char *kmeans_status_str(km_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+KM_API const char *kmeans_last_error(void);
+
+/* ABI version, major * 10000 + minor * 100 + patch. */
+KM_API int kmeans_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KMEANS_MI355X_H */

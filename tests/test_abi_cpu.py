@@ -1,0 +1,98 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every
+symbol the header declares, and rejects invalid arguments on the host before
+any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_lloyd_means_03_amd import _lib
+    return _lib.load()
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "kmeans.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kmeans_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from exact_lloyd_means_03_amd import _lib
+    names = _header_functions()
+    assert names == sorted(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.kmeans_status_str(0) == b"ok"
+    assert lib.kmeans_status_str(3) == b"workspace too small"
+    assert lib.kmeans_version() >= 100
+
+
+def test_workspace_bytes(lib):
+    n = lib.kmeans_workspace_bytes(1, 1 << 20, 128, 8192, 1)
+    # at least labels, perm, sums and the padded fp16 centroids
+    assert n >= (1 << 20) * 8 + 8192 * 128 * 4 + 8192 * 128 * 2
+    assert n % 256 == 0
+    assert lib.kmeans_workspace_bytes(1, 100, 0, 4, 1) == 0       # d < 1
+    assert lib.kmeans_workspace_bytes(1, 100, 300, 4, 1) == 0     # d > 256
+    assert lib.kmeans_workspace_bytes(1, 100, 8, 40000, 1) == 0   # K > 32768
+    assert lib.kmeans_workspace_bytes(-1, 100, 8, 4, 1) == 0
+    assert lib.kmeans_workspace_bytes(1, 100, 8, 4, 7) == 0       # dtype
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every case fails before any HIP call
+
+
+@pytest.mark.parametrize("args,status", [
+    # x NULL
+    (dict(x=None), 1),
+    # K = 0
+    (dict(K=0), 1),
+    # d = 300
+    (dict(d=300), 2),
+    # unsupported dtype
+    (dict(xt=5), 2),
+    # workspace too small
+    (dict(ws_bytes=16), 3),
+    # misaligned workspace
+    (dict(ws=C.c_void_p(0x1008)), 1),
+    # negative N
+    (dict(N=-3), 1),
+])
+def test_assign_rejects(lib, args, status):
+    a = dict(x=FAKE, xt=1, B=1, N=100, d=8, C=FAKE, K=4, w=None, labels=FAKE, md=None, obj=None,
+             ws=C.c_void_p(0x100000), ws_bytes=1 << 30, stream=None)
+    a.update(args)
+    st = lib.kmeans_assign(a["x"], a["xt"], a["B"], a["N"], a["d"], a["C"], a["K"], a["w"], a["labels"],
+                           a["md"], a["obj"], a["ws"], a["ws_bytes"], a["stream"])
+    assert st == status
+    assert lib.kmeans_last_error() != b""
+
+
+def test_update_and_fit_reject(lib):
+    ws = C.c_void_p(0x100000)
+    assert lib.kmeans_update(FAKE, 1, None, 1, 10, 8, None, 4, FAKE, FAKE, None, ws, 1 << 30, None) == 1
+    assert lib.kmeans_update(FAKE, 1, None, 1, 10, 8, FAKE, 40000, FAKE, FAKE, None, ws, 1 << 30, None) == 2
+    assert lib.kmeans_fit(FAKE, 1, None, 1, 10, 8, 4, FAKE, -1, FAKE, None, None, None, ws, 1 << 30, None) == 1
+    assert lib.kmeans_fit(FAKE, 2, None, 1, 10, 8, 4, FAKE, 3, FAKE, None, None, None, ws, 100, None) == 3
+    assert lib.kmeans_sort_labels(None, 1, 10, 4, None, None, None, ws, 1 << 30, None) == 1
+    assert b"labels" in lib.kmeans_last_error()
+    # B*N*d beyond the 64-bit guard
+    assert lib.kmeans_fit(FAKE, 1, None, 65535, 0x7fffffff, 256, 4, FAKE, 1, FAKE, None, None, None,
+                          ws, 1 << 62, None) == 2
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    import exact_lloyd_means_03_amd as km
+    x = torch.zeros(1, 10, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        km.kmeans_assign(x, torch.zeros(1, 4, 8))

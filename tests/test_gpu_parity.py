@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Teacher-forced step parity: the GPU assignment and the oracle assignment get
+the same centroids; the GPU update and the oracle update get the same
+labels.  Free-running fits are compared where the oracle finishes quickly.
+Inputs are the seeded workloads (reduced sizes, several tiles and ragged
+tails) plus edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def km():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_lloyd_means_03_amd as km
+    km.load()
+    return km
+
+
+def _rand_problem(B, N, d, K, dtype, seed, spread=1.0):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(B, N, d, generator=g) * spread).to(DT[dtype])
+    C = torch.randn(B, K, d, generator=g) * spread
+    return x, C
+
+
+def _assign_case(km, x, C, w=None, what=""):
+    xd, Cd = x.cuda(), C.cuda()
+    wd = None if w is None else w.cuda()
+    labels, md, obj = km.kmeans_assign(xd, Cd, weights=wd, min_dist=True, objective=True)
+    torch.cuda.synchronize()
+    dt = workloads.dtype_name(x)
+    X, Chat, lab_ref, d1, d2 = parity.oracle_assign(workloads.raw_bits(x), dt, C.numpy())
+    gl = labels.cpu().numpy()
+    parity.check_labels(gl, lab_ref, d1, d2, what)
+    parity.check_min_dist(md.cpu().numpy(), X, Chat, lab_ref, d1, what)
+    wn = np.ones(d1.shape) if w is None else w.numpy().astype(np.float64)
+    parity.check_objective(obj.cpu().numpy(), (wn * d1).sum(-1), what)
+    return gl
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("B,N,d,K", [
+    (1, 1, 8, 1), (1, 300, 128, 64), (2, 1000, 128, 65), (1, 513, 100, 300),
+    (3, 257, 16, 7), (1, 700, 2, 5), (1, 400, 33, 130), (1, 300, 200, 40), (1, 260, 256, 70),
+    (1, 2049, 64, 1000),
+])
+def test_assign_parity(km, dtype, B, N, d, K):
+    x, C = _rand_problem(B, N, d, K, dtype, seed=B * 1000 + N + d + K)
+    _assign_case(km, x, C, what=f"{dtype} B{B} N{N} d{d} K{K}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 8, 16, 100, 1024, 1500])
+def test_assign_1d_parity(km, dtype, K):
+    x, C = _rand_problem(3, 5000, 1, K, dtype, seed=K, spread=0.05)
+    w = torch.rand(3, 5000) * 0.9 + 0.1
+    _assign_case(km, x, C, w=w, what=f"1d {dtype} K{K}")
+
+
+def test_assign_1d_exact_ties(km):
+    # x exactly halfway between two centroids; duplicated centroid values
+    C = torch.tensor([[[0.0], [1.0], [1.0], [-1.0], [0.5]]])
+    x = torch.tensor([[[0.25], [0.75], [-0.5], [1.0], [2.0], [-3.0], [0.5]]])
+    labels, md, _ = km.kmeans_assign(x.cuda(), C.cuda(), min_dist=True)
+    np.testing.assert_array_equal(labels.cpu().numpy()[0], [0, 1, 0, 1, 1, 3, 4])
+
+
+def test_duplicate_centroids_smallest_index(km):
+    for dtype in ("f32", "f16", "bf16"):
+        x, C = _rand_problem(1, 600, 128, 40, dtype, seed=7)
+        C[0, 33] = C[0, 5]
+        C[0, 39] = C[0, 5]
+        gl = _assign_case(km, x, C, what=f"dup {dtype}")
+        assert not np.any(gl == 33) and not np.any(gl == 39)
+
+
+def test_points_equal_centroids(km):
+    # every point is exactly a centroid (d = 0 up to rounding): labels are the identity
+    for dtype in ("f32", "f16", "bf16"):
+        x, _ = _rand_problem(1, 200, 64, 1, dtype, seed=3)
+        C = x.float().clone()
+        labels, md, _ = km.kmeans_assign(x.cuda(), C.cuda(), min_dist=True)
+        np.testing.assert_array_equal(labels.cpu().numpy()[0], np.arange(200))
+        assert torch.all(md >= 0)
+
+
+def test_empty_inputs(km):
+    x = torch.zeros(2, 0, 16, device="cuda", dtype=torch.float16)
+    C = torch.randn(2, 5, 16, device="cuda")
+    labels, _, obj = km.kmeans_assign(x, C, objective=True)
+    assert labels.shape == (2, 0)
+    assert torch.all(obj == 0)
+    c_new, counts = km.kmeans_update(x, labels, C)
+    assert torch.equal(c_new, C) and torch.all(counts == 0)
+    cen, lab, cnt, J = km.kmeans_fit(x, C, 3)
+    assert torch.equal(cen, C) and torch.all(J == 0)
+    xb = torch.zeros(0, 10, 16, device="cuda", dtype=torch.float16)
+    km.kmeans_fit(xb, torch.zeros(0, 4, 16, device="cuda"), 2)
+    torch.cuda.synchronize()
+
+
+def test_misaligned_points(km):
+    # a view that starts one element into its storage: the kernels fall back to element loads
+    for dtype in ("f16", "bf16", "f32"):
+        base, C = _rand_problem(1, 300 * 64 + 1, 1, 20, dtype, seed=11)
+        x = base.reshape(-1)[1:].reshape(1, 300, 64)
+        xd = base.cuda().reshape(-1)[1:].reshape(1, 300, 64)
+        assert xd.data_ptr() % 16 != 0
+        C = torch.randn(1, 20, 64)
+        labels, md, _ = km.kmeans_assign(xd, C.cuda(), min_dist=True)
+        X, Chat, lab_ref, d1, d2 = parity.oracle_assign(workloads.raw_bits(x.contiguous()), dtype, C.numpy())
+        parity.check_labels(labels.cpu().numpy(), lab_ref, d1, d2, "misaligned " + dtype)
+        w = torch.ones(1, 300, device="cuda")
+        c_new, counts = km.kmeans_update(xd, labels, C.cuda(), weights=w)
+        ref_c, ref_n, _, _ = oracle.update(X, None, labels.cpu().numpy(), C.numpy())
+        np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+        parity.check_centroids(c_new.cpu().numpy(), ref_c, "misaligned update " + dtype)
+
+
+def test_sort_labels(km):
+    rng = np.random.default_rng(0)
+    for (B, N, K) in [(1, 1, 1), (2, 5000, 7), (1, 70000, 3000), (3, 40000, 16), (1, 100, 5000)]:
+        lab = rng.integers(0, K, size=(B, N)).astype(np.int32)
+        lab[:, ::97] = -1            # unlabeled points
+        lab[:, 5::101] = K + 3       # out of range
+        counts, offsets, perm = km.kmeans_sort_labels(torch.from_numpy(lab).cuda(), K)
+        parity.check_perm(lab, K, counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy())
+
+
+def test_sort_labels_skewed(km):
+    # Zipf-like sizes: most points in a few segments
+    rng = np.random.default_rng(1)
+    K = 4096
+    p = np.arange(1, K + 1, dtype=np.float64) ** -1.2
+    p /= p.sum()
+    lab = rng.choice(K, size=(1, 300000), p=p).astype(np.int32)
+    counts, offsets, perm = km.kmeans_sort_labels(torch.from_numpy(lab).cuda(), K)
+    parity.check_perm(lab, K, counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("B,N,d,K,weighted", [
+    (1, 5000, 128, 64, False), (2, 3000, 128, 300, True), (1, 20000, 16, 5, False),
+    (1, 1000, 33, 50, True), (1, 4000, 2, 3, False), (1, 2000, 256, 17, False),
+    (1, 100, 64, 500, False), (2, 9000, 1, 12, True), (1, 20000, 1, 300, False),
+])
+def test_update_parity(km, dtype, B, N, d, K, weighted):
+    x, C = _rand_problem(B, N, d, K, dtype, seed=N + K + d)
+    rng = np.random.default_rng(N + K)
+    lab = rng.integers(0, max(1, K - K // 5), size=(B, N)).astype(np.int32)  # top clusters empty
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, (B, N)).astype(np.float32)) if weighted else None
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(lab).cuda(), C.cuda(),
+                                     weights=None if w is None else w.cuda())
+    X = oracle.decode(workloads.raw_bits(x), dtype)
+    ref_c, ref_n, _, _ = oracle.update(X, None if w is None else w.numpy(), lab, C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    parity.check_centroids(c_new.cpu().numpy(), ref_c, f"update {dtype} B{B} N{N} d{d} K{K} w{weighted}")
+    # empty clusters keep the old centroid bit for bit
+    empty = ref_n == 0
+    np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
+
+
+def test_update_in_place_and_invalid_labels(km):
+    x, C = _rand_problem(1, 3000, 64, 20, "f16", seed=5)
+    rng = np.random.default_rng(5)
+    lab = rng.integers(0, 20, size=(1, 3000)).astype(np.int32)
+    lab[0, ::7] = -2
+    lab[0, 3::11] = 99
+    Cd = C.cuda()
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(lab).cuda(), Cd, c_new=Cd)
+    valid = (lab >= 0) & (lab < 20)
+    X = oracle.decode(workloads.raw_bits(x), "f16")
+    keep = np.nonzero(valid[0])[0]
+    ref_c, ref_n, _, _ = oracle.update(X[:, keep], None, lab[:, keep], C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    parity.check_centroids(Cd.cpu().numpy(), ref_c, "in place")
+
+
+def _fit_compare(km, p, n_iter=None, what=""):
+    wl = p.wl
+    n_iter = wl.n_iter if n_iter is None else n_iter
+    x, w, init = parity.to_device(p)
+    cen, lab, cnt, J = km.kmeans_fit(x, init, n_iter, weights=w)
+    torch.cuda.synchronize()
+    ref = oracle.fit(workloads.raw_bits(p.x), wl.dtype, None if p.w is None else p.w.numpy(),
+                     p.init.numpy(), n_iter)
+    nt = oracle.near_tie(ref["d1"], ref["d2"])
+    gl = lab.cpu().numpy()
+    flips = int(((gl != ref["labels"]) & nt).sum())
+    parity.check_objective(J.cpu().numpy(), ref["J"], what)
+    parity.check_labels(gl, ref["labels"], ref["d1"], ref["d2"], what)
+    if flips == 0:
+        np.testing.assert_array_equal(cnt.cpu().numpy(), ref["counts"])
+    parity.check_centroids(cen.cpu().numpy(), ref["centroids"], what)
+    return flips
+
+
+def test_fit_parity_gmm_fp32_full(km):
+    """The 8192-point, K=256, d=128 float32 mixture, all 10 iterations."""
+    p = workloads.generate(workloads.WORKLOADS["gmm-n8192-k256-d128-f32"])
+    _fit_compare(km, p, what="gmm-n8192 f32")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fit_parity_gmm_half(km, dtype):
+    wl = workloads.small("gmm-b32-n65536-k1024-d128-f16", B=3, N=6000, K=96, dtype=dtype, n_iter=8)
+    _fit_compare(km, workloads.generate(wl), what=f"gmm small {dtype}")
+
+
+def test_fit_parity_rows1d(km):
+    wl = workloads.small("rows1d-b4096-n4096-k16-f32", B=64)
+    _fit_compare(km, workloads.generate(wl), what="rows1d K16")
+    wl = workloads.small("rows1d-b4096-n4096-k8-f32", B=64)
+    _fit_compare(km, workloads.generate(wl), what="rows1d K8")
+
+
+def test_fit_resume_and_batch_independence(km):
+    wl = workloads.small("gmm-b32-n65536-k1024-d128-f16", B=4, N=3000, K=40, n_iter=6)
+    p = workloads.generate(wl)
+    x, w, init = parity.to_device(p)
+    c6, l6, n6, J6 = km.kmeans_fit(x, init, 6)
+    c2, _, _, J2 = km.kmeans_fit(x, init, 2)
+    c4, l4, n4, J4 = km.kmeans_fit(x, c2, 4)
+    parity.check_centroids(c4.cpu().numpy(), c6.cpu().numpy(), "resume")
+    parity.check_objective(torch.cat([J2, J4], 1).cpu().numpy(), J6.cpu().numpy(), "resume J")
+    perm = torch.tensor([2, 0, 3, 1])
+    cp, lp, np_, Jp = km.kmeans_fit(x[perm].contiguous(), init[perm].contiguous(), 6)
+    parity.check_centroids(cp.cpu().numpy(), c6[perm.cuda()].cpu().numpy(), "batch permutation")
+    parity.check_objective(Jp.cpu().numpy(), J6[perm.cuda()].cpu().numpy(), "batch permutation J")
+
+
+def test_k_greater_than_n(km):
+    x, C = _rand_problem(1, 50, 32, 200, "f16", seed=9)
+    cen, lab, cnt, J = km.kmeans_fit(x.cuda(), C.cuda(), 3)
+    ref = oracle.fit(workloads.raw_bits(x), "f16", None, C.numpy(), 3)
+    parity.check_labels(lab.cpu().numpy(), ref["labels"], ref["d1"], ref["d2"], "K>N")
+    parity.check_centroids(cen.cpu().numpy(), ref["centroids"], "K>N")
+    assert int(cnt.sum()) == 50
