@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -123,6 +125,15 @@ def main():
     import exact_lloyd_means_03_amd as km
     import workloads
 
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
     km.load()  # raises if the HIP library is missing
     name = args.workload or workloads.HEADLINE
     wl = workloads.WORKLOADS[name]

@@ -49,8 +49,7 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
         return at;
     };
     const size_t Bz = (size_t)B;
-    w.chat = take(a1d ? 0 : Bz * w.Kp * w.DP * dtype_bytes(xt));
-    w.hnorm = take(a1d ? 0 : Bz * w.Kp * sizeof(float));
+    w.chat = take(a1d ? 0 : Bz * (w.Kp / kTileRows) * (size_t)tile_bytes(w.DP, dtype_bytes(xt)));
     w.obj_part = take(Bz * w.nblk_assign * sizeof(double));
     w.labels = take(Bz * N * sizeof(int32_t));
     w.counts = take(Bz * K * sizeof(int32_t));
@@ -86,6 +85,15 @@ km_status check_shape(int64_t B, int64_t N, int64_t d, int64_t K, int xt) {
     int64_t bn, bnd;
     if (__builtin_mul_overflow(B, N, &bn) || __builtin_mul_overflow(bn, d, &bnd) || bnd > ((int64_t)1 << 46))
         return fail(KM_EUNSUPPORTED, "B*N*d too large");
+    return KM_OK;
+}
+
+// Scalar points are always assigned by the binary search: the expanded form
+// ||x||^2 - 2xc + c^2 cancels catastrophically when many centroids are packed
+// closely on a line.
+km_status check_scalar_k(int64_t d, int64_t K) {
+    if (d == 1 && !assign_1d_supports(K))
+        return fail(KM_EUNSUPPORTED, "d=1 assignment supports K <= 16384 (K=%lld)", (long long)K);
     return KM_OK;
 }
 
@@ -129,10 +137,9 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
     if (use_assign_1d(d, K)) {
         KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, part, W.nblk_assign, s), "assign_1d");
     } else {
-        void* chat = at<void>(ws, W.chat);
-        float* hn = at<float>(ws, W.hnorm);
-        KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, chat, hn, s), "prep");
-        KM_HIP(launch_assign_mfma(xt, x, B, N, (int)d, W.DP, chat, hn, K, W.Kp, w, labels, min_dist, part,
+        void* blob = at<void>(ws, W.chat);
+        KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, blob, s), "prep");
+        KM_HIP(launch_assign_mfma(xt, x, B, N, (int)d, W.DP, blob, W.Kp, w, labels, min_dist, part,
                                   W.nblk_assign, s),
                "assign_mfma");
     }
@@ -187,6 +194,7 @@ km_status kmeans_assign(const void* x, km_dtype xt, int64_t B, int64_t N, int64_
                         int64_t K, const float* weights, int32_t* labels, float* min_dist, double* objective,
                         void* workspace, size_t workspace_bytes, km_stream stream) {
     KM_TRY(check_shape(B, N, d, K, (int)xt));
+    KM_TRY(check_scalar_k(d, K));
     KM_TRY(need(x, B * N, "x"));
     KM_TRY(need(centroids, B, "centroids"));
     KM_TRY(need(labels, B * N, "labels"));
@@ -237,6 +245,7 @@ km_status kmeans_fit(const void* x, km_dtype xt, const float* weights, int64_t B
                      double* objective, void* workspace, size_t workspace_bytes, km_stream stream) {
     KM_TRY(check_shape(B, N, d, K, (int)xt));
     if (n_iter < 0) return fail(KM_EINVAL, "n_iter=%d < 0", n_iter);
+    KM_TRY(check_scalar_k(d, K));
     KM_TRY(need(x, B * N, "x"));
     KM_TRY(need(init, B, "init"));
     KM_TRY(need(centroids, B, "centroids"));

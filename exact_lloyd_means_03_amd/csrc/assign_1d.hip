@@ -7,15 +7,17 @@
 // that bracket x in sorted order, because (x - c)^2 grows with |x - c| (and
 // float rounding is monotone, so the same holds for the float32 distances).
 //
-// Each block sorts its row's K centroids in LDS by (value, index).  Runs of
-// equal centroid values are represented by their smallest index, so exact
-// ties keep the smallest index as in the matrix-core path.
+// Each block sorts its row's K centroids in LDS by (value, index) with a
+// bitonic network.  The first centroid of a run of equal values carries the
+// smallest index of that value, so exact ties keep the smallest index as in
+// the matrix-core path.  The distance (x - c)^2 is formed directly, with no
+// cancellation, which is why every scalar problem stays on this path.
 #include "common.h"
 
 namespace km {
 
-constexpr int kMaxK1D = 1024;
-constexpr int kPts1D = 4096;  // points per block
+constexpr int kMaxK1D = 16384;  // (value, index) keys of a row fit in 128 KB of LDS
+constexpr int kPts1D = 4096;    // points per block
 
 template <typename T>
 __device__ __forceinline__ float round_as_point(float v) {
@@ -31,11 +33,19 @@ __device__ __forceinline__ float load_point(const T* p) {
     else return bf16_to_f32(*p);
 }
 
-__device__ __forceinline__ int lower_bound(const float* v, int n, float x) {
+// Order-preserving map of a float to uint32 (-0 is canonicalized to +0 first,
+// so values that compare equal get equal keys).
+__device__ __forceinline__ uint32_t orderable(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// First position p in keys[0, n) with keys[p] >= k.
+__device__ __forceinline__ int lower_bound_u64(const uint64_t* keys, int n, uint64_t k) {
     int lo = 0, len = n;
     while (len > 0) {
         const int h = len >> 1;
-        if (v[lo + h] < x) {
+        if (keys[lo + h] < k) {
             lo += h + 1;
             len -= h + 1;
         } else {
@@ -45,37 +55,42 @@ __device__ __forceinline__ int lower_bound(const float* v, int n, float x) {
     return lo;
 }
 
+// keys: (orderable(value) << 32) | index, sorted ascending, so equal values
+// are ordered by index and the first key of a run of equal values carries
+// the smallest index of that value.
 template <typename T>
 __global__ __launch_bounds__(256) void k_assign_1d(const T* __restrict__ X, int64_t N,
-                                                   const float* __restrict__ C, int K,
+                                                   const float* __restrict__ C, int K, int Kpow2,
                                                    const float* __restrict__ w,
                                                    int32_t* __restrict__ labels,
                                                    float* __restrict__ min_dist,
                                                    double* __restrict__ obj_part) {
-    __shared__ float s_raw[kMaxK1D];
-    __shared__ float s_v[kMaxK1D];
-    __shared__ int32_t s_i[kMaxK1D];
-    __shared__ int32_t s_rep[kMaxK1D];
+    extern __shared__ uint64_t s_key[];
     __shared__ double s_obj[4];
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.y;
 
-    for (int j = tid; j < K; j += 256) s_raw[j] = round_as_point<T>(C[b * K + j]);
-    __syncthreads();
-    // rank of each centroid under (value, index) order
-    for (int j = tid; j < K; j += 256) {
-        const float v = s_raw[j];
-        int rank = 0;
-        for (int i = 0; i < K; ++i) {
-            const float u = s_raw[i];
-            rank += (u < v) || (u == v && i < j);
-        }
-        s_v[rank] = v;
-        s_i[rank] = j;
+    for (int j = tid; j < Kpow2; j += 256) {
+        s_key[j] = j < K ? ((uint64_t)orderable(round_as_point<T>(C[b * K + j])) << 32) | (uint32_t)j
+                         : ~(uint64_t)0;
     }
     __syncthreads();
-    for (int p = tid; p < K; p += 256) s_rep[p] = s_i[lower_bound(s_v, K, s_v[p])];
-    __syncthreads();
+    // bitonic sort of Kpow2 keys
+    for (int size = 2; size <= Kpow2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < (Kpow2 >> 1); t += 256) {
+                const int i = 2 * t - (t & (stride - 1));  // first element of the pair
+                const int k = i + stride;
+                const bool up = (i & size) == 0;
+                const uint64_t a = s_key[i], c = s_key[k];
+                if ((a > c) == up) {
+                    s_key[i] = c;
+                    s_key[k] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
 
     const T* Xb = X + b * N;
     const int64_t i0 = (int64_t)blockIdx.x * kPts1D;
@@ -83,18 +98,26 @@ __global__ __launch_bounds__(256) void k_assign_1d(const T* __restrict__ X, int6
     double obj = 0.0;
     for (int64_t i = i0 + tid; i < i1; i += 256) {
         const float x = load_point<T>(Xb + i);
-        const int m = lower_bound(s_v, K, x);
+        const int m = lower_bound_u64(s_key, K, (uint64_t)orderable(x) << 32);
         float dl = INFINITY, dh = INFINITY;
         int32_t il = 0x7fffffff, ih = 0x7fffffff;
         if (m > 0) {
-            const float t = x - s_v[m - 1];
+            // first key of the run holding the largest value below x
+            const uint64_t kl = s_key[m - 1] & 0xffffffff00000000ull;
+            const uint64_t first = s_key[lower_bound_u64(s_key, m, kl)];
+            const float t = x - __uint_as_float(((uint32_t)(kl >> 32) & 0x80000000u)
+                                                    ? ((uint32_t)(kl >> 32) & 0x7fffffffu)
+                                                    : ~(uint32_t)(kl >> 32));
             dl = t * t;
-            il = s_rep[m - 1];
+            il = (int32_t)(first & 0xffffffffu);
         }
         if (m < K) {
-            const float t = s_v[m] - x;
+            const uint64_t kh = s_key[m];
+            const uint32_t o = (uint32_t)(kh >> 32);
+            const float v = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+            const float t = v - x;
             dh = t * t;
-            ih = s_rep[m];
+            ih = (int32_t)(kh & 0xffffffffu);
         }
         const bool lo = (dl < dh) || (dl == dh && il < ih);
         const float dist = lo ? dl : dh;
@@ -120,16 +143,29 @@ hipError_t launch_assign_1d(DType xt, const void* x, int64_t B, int64_t N, const
                             double* obj_part, int64_t nblk, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
     if (K > kMaxK1D) return hipErrorInvalidValue;
+    int kp = 1;
+    while (kp < K) kp <<= 1;
+    const size_t lds = (size_t)kp * sizeof(uint64_t);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipSuccess;
+        if (xt == DType::F32)
+            e = hipFuncSetAttribute((const void*)k_assign_1d<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        else if (xt == DType::F16)
+            e = hipFuncSetAttribute((const void*)k_assign_1d<_Float16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        else
+            e = hipFuncSetAttribute((const void*)k_assign_1d<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
     dim3 grid((unsigned)nblk, (unsigned)B);
     if (xt == DType::F32)
-        hipLaunchKernelGGL(k_assign_1d<float>, grid, dim3(256), 0, s, (const float*)x, N, C, (int)K, w,
+        hipLaunchKernelGGL(k_assign_1d<float>, grid, dim3(256), lds, s, (const float*)x, N, C, (int)K, kp, w,
                            labels, min_dist, obj_part);
     else if (xt == DType::F16)
-        hipLaunchKernelGGL(k_assign_1d<_Float16>, grid, dim3(256), 0, s, (const _Float16*)x, N, C, (int)K,
-                           w, labels, min_dist, obj_part);
+        hipLaunchKernelGGL(k_assign_1d<_Float16>, grid, dim3(256), lds, s, (const _Float16*)x, N, C, (int)K,
+                           kp, w, labels, min_dist, obj_part);
     else
-        hipLaunchKernelGGL(k_assign_1d<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, N, C, (int)K, w,
-                           labels, min_dist, obj_part);
+        hipLaunchKernelGGL(k_assign_1d<bf16_t>, grid, dim3(256), lds, s, (const bf16_t*)x, N, C, (int)K, kp,
+                           w, labels, min_dist, obj_part);
     return hipGetLastError();
 }
 

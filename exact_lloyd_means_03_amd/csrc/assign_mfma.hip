@@ -11,17 +11,26 @@
 //   * one 64-lane wave owns NCB column blocks of 32 points; their coordinates
 //     stay in VGPRs for the whole kernel as the B operand of
 //     v_mfma_f32_32x32x16_{f16,bf16} (v_mfma_f32_32x32x2_f32 for float32);
-//   * centroid tiles of TK rows are double buffered in LDS and shared by the
-//     4 waves of the block; rows are padded by 16 bytes so the 32 A-operand
-//     rows read by one instruction fall in distinct banks;
+//   * centroid tiles of 64 rows (with their -|c|^2/2 values appended) move
+//     from device memory to LDS by direct DMA (global_load_lds_dwordx4), up to
+//     three buffers deep, and are shared by the 4 waves of the block; rows are
+//     XOR-swizzled in 16-byte chunks so the 32 A-operand rows read by one
+//     instruction fall in distinct banks;
+//   * software pipeline over 32-row blocks: the MFMAs of block s are issued
+//     next to the epilogue of block s-1, so the matrix core and the vector
+//     ALU work at the same time;
 //   * the accumulator starts at -||c||^2 / 2 (precomputed per centroid), so
 //     the matrix core produces x.c - ||c||^2 / 2 = (||x||^2 - D(x,c)) / 2 and
-//     the nearest centroid is the running MAXIMUM -- no VALU work per
-//     distance besides the compare and two selects;
-//   * each lane holds 16 centroid rows of one point per 32x32 block and
-//     scans them in ascending index order with a strict '>', so ties keep the
-//     smallest index; the two half-waves that share a point merge at the end
-//     by (value, then smaller index);
+//     the nearest centroid is the running MAXIMUM;
+//   * online argmax at block granularity: each lane holds 16 centroid rows of
+//     one point per 32x32 block; it reduces them with a v_max3 chain, compares
+//     once against its running best (strict '>', so the earliest block wins
+//     ties) and keeps the winning block's 16 values, from which the smallest
+//     row holding the maximum is recovered after the last tile.  About 1.6
+//     VALU instructions per distance instead of a compare and two selects
+//     each;
+//   * the two half-waves that share a point merge at the end by (value, then
+//     smaller index);
 //   * padding centroids (K..Kp-1) start at -inf and never win.
 #include "common.h"
 
@@ -115,35 +124,78 @@ struct AssignCfg {
     static constexpr int NCB = (DP * (int)sizeof(T) <= 512) ? 2 : 1;   // 32-point blocks per wave
     static constexpr int WAVES = 4;
     static constexpr int PTS = WAVES * NCB * 32;                         // points per block
-    static constexpr int TK = (DP * (int)sizeof(T) <= 256) ? 64 : 32;    // centroid rows per tile
-    static constexpr int PAD = sizeof(T) == 4 ? 1 : 8;                   // LDS row padding (elements)
-    static constexpr int LDR = DP + PAD;                                  // LDS row stride (elements)
+    static constexpr int TK = kTileRows;                                  // centroid rows per tile (2 blocks)
+    static constexpr int RB = DP * (int)sizeof(T);                       // bytes per centroid row
+    static constexpr int CPR = RB / 16;                                   // 16-byte chunks per row
+    static constexpr int SW = CPR < 32 ? CPR : 32;                        // XOR swizzle period (rows)
+    static constexpr int TILE = tile_bytes(DP, sizeof(T));                // rows + the -|c|^2/2 segment
+    static constexpr int NI = TILE / 1024;                                // 1 KB DMA instructions per tile
+    static constexpr int NIW = NI / WAVES;                                // ... per wave
+    static constexpr int NBUF = 3 * TILE <= 150 * 1024 ? 3 : 2;           // LDS tile buffers
     static constexpr int KSTEPS = DP / Mf<T>::KS;
-    static constexpr int CH_PER_ROW = DP * (int)sizeof(T) / 16;          // 16-byte chunks per row
-    static constexpr int TILE_CH = TK * CH_PER_ROW;                       // 16-byte chunks per tile
-    static constexpr int CH_PER_THR = (TILE_CH + 255) / 256;
 };
+
+constexpr uint32_t vmcnt_imm(int n) {  // s_waitcnt with only vmcnt <= n
+    return (uint32_t)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One global_load_lds_dwordx4: lane l copies 16 bytes from g to LDS byte
+// lds + 16 l (lds must be the same for the whole wave).  Written as a
+// one-instruction asm statement so the compiler does not treat the in-flight
+// LDS write as aliasing every later LDS read (it would wait for the copy
+// right after issuing it); the kernel waits on vmcnt explicitly before the
+// barrier that publishes a tile.  The instruction has no register results.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(l)) : "memory");
+}
+
+// Copy tile t of this batch's blob into LDS buffer `dst` with 1 KB DMA
+// instructions (lane l of instruction i writes LDS bytes i*1024 + 16 l).
+// Row chunks are XOR-swizzled: LDS chunk position p of row r holds global
+// chunk p ^ (r % SW), SW = min(chunks per row, 32), so the 32 rows read by one
+// A-operand instruction hit distinct banks without padding, and the swizzle
+// of row r depends only on r % 32 (the same for both 32-row blocks).
+template <typename T, int DP>
+__device__ __forceinline__ void dma_tile(const char* __restrict__ tile_g, char* dst, int wave, int lane) {
+    typedef AssignCfg<T, DP> Cfg;
+    static_assert(Cfg::NI % Cfg::WAVES == 0, "tile must split evenly over the waves");
+#pragma unroll
+    for (int n = 0; n < Cfg::NIW; ++n) {
+        const int i = n * Cfg::WAVES + wave;
+        const int p = i * 1024 + lane * 16;
+        int src = p;
+        if (p < Cfg::TK * Cfg::RB) {
+            const int r = p / Cfg::RB, q = (p % Cfg::RB) / 16;
+            src = r * Cfg::RB + ((q ^ (r % Cfg::SW)) * 16);
+        }
+        dma16(tile_g + src, dst + i * 1024);
+    }
+}
 
 template <typename T, int DP, bool VEC>
 __global__ __launch_bounds__(256) void k_assign_mfma(
-    const T* __restrict__ X, int64_t N, int d, const T* __restrict__ chat,
-    const float* __restrict__ hnorm, int64_t Kp, const float* __restrict__ w,
-    int32_t* __restrict__ labels, float* __restrict__ min_dist, double* __restrict__ obj_part) {
+    const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int64_t ntiles,
+    const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
+    double* __restrict__ obj_part) {
     typedef AssignCfg<T, DP> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
-    constexpr int NCB = Cfg::NCB, TK = Cfg::TK, LDR = Cfg::LDR, KSTEPS = Cfg::KSTEPS;
+    constexpr int NCB = Cfg::NCB, TK = Cfg::TK, RB = Cfg::RB, KSTEPS = Cfg::KSTEPS, NBUF = Cfg::NBUF;
 
-    __shared__ __attribute__((aligned(16))) T s_c[2][TK * LDR];
-    __shared__ __attribute__((aligned(16))) float s_hn[2][TK];
+    __shared__ __attribute__((aligned(1024))) char s_tile[NBUF][Cfg::TILE];
     __shared__ double s_obj[Cfg::WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int64_t b = blockIdx.y;
     const T* Xb = X + b * N * (int64_t)d;
-    const T* Cb = chat + b * Kp * (int64_t)DP;
-    const float* Hb = hnorm + b * Kp;
+    const char* Bb = blob + b * ntiles * (int64_t)Cfg::TILE;
+
+    // start the first tiles' DMA before the point loads
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+        if (t < ntiles) dma_tile<T, DP>(Bb + (int64_t)t * Cfg::TILE, s_tile[t], wave, lane);
 
     // ---- points of this wave: B operand fragments + squared norms -------
     F bx[NCB][KSTEPS];
@@ -164,113 +216,168 @@ __global__ __launch_bounds__(256) void k_assign_mfma(
         xx[cb] = s + __shfl_xor(s, 32, 64);
     }
 
+    // running best per point: value, 32-row block that holds it, and that
+    // block's 16 values of this lane (to recover the row at the end)
     float best[NCB];
-    int32_t bidx[NCB];
+    int32_t bblk[NCB];
+    f32x16 saved[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         best[cb] = -INFINITY;
-        bidx[cb] = 0;
+        bblk[cb] = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) saved[cb][r] = -INFINITY;
     }
 
-    // ---- centroid tile pipeline (global -> registers -> LDS) ------------
-    const int64_t ntiles = Kp / TK;
-    u32x4 pre[Cfg::CH_PER_THR];
-    float pre_hn = 0.f;
-    auto gload = [&](int64_t t) {
-        const u32x4* src = (const u32x4*)(Cb + t * TK * (int64_t)DP);
+    // per-lane byte offsets of the A operand in a tile (row col of block 0)
+    int aoff[KSTEPS];
 #pragma unroll
-        for (int i = 0; i < Cfg::CH_PER_THR; ++i) {
-            const int c = tid + i * 256;
-            if (c < Cfg::TILE_CH) pre[i] = src[c];
-        }
-        if (tid < TK) pre_hn = Hb[t * TK + tid];
-    };
-    auto lstore = [&](int buf) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int ob = (ks * M::KS + half * M::EPL) * (int)sizeof(T);
+        aoff[ks] = col * RB + (((ob / 16) ^ (col % Cfg::SW)) * 16) + (ob % 16);
+    }
+
+    // Epilogue of a finished 32-row block, cut into 8 pieces of 3-4 VALU
+    // instructions per column block: max of the lane's 16 rows (v_max3
+    // chain), one compare against the running best (strict '>', so the
+    // earliest block wins ties), and a select that keeps the winning block's
+    // 16 values (the row is recovered from them after the last tile).
+    float pm[NCB];
+    bool pimp[NCB];
+    auto epi_piece = [&](int piece, const f32x16* v, int32_t blk) {
 #pragma unroll
-        for (int i = 0; i < Cfg::CH_PER_THR; ++i) {
-            const int c = tid + i * 256;
-            if (c < Cfg::TILE_CH) {
-                const int r = c / Cfg::CH_PER_ROW, q = c % Cfg::CH_PER_ROW;
-                T* dst = &s_c[buf][r * LDR] + q * (16 / (int)sizeof(T));
-                if constexpr (sizeof(T) == 4) {
-                    // padded float rows are only 4-byte aligned
-                    float* df = (float*)dst;
-                    df[0] = __uint_as_float(pre[i][0]);
-                    df[1] = __uint_as_float(pre[i][1]);
-                    df[2] = __uint_as_float(pre[i][2]);
-                    df[3] = __uint_as_float(pre[i][3]);
-                } else {
-                    *(u32x4*)dst = pre[i];
+        for (int cb = 0; cb < NCB; ++cb) {
+            const f32x16& a = v[cb];
+            switch (piece) {
+                case 0:
+                    pm[cb] = fmaxf(fmaxf(a[0], a[1]), a[2]);
+                    pm[cb] = fmaxf(fmaxf(pm[cb], a[3]), a[4]);
+                    pm[cb] = fmaxf(fmaxf(pm[cb], a[5]), a[6]);
+                    break;
+                case 1:
+                    pm[cb] = fmaxf(fmaxf(pm[cb], a[7]), a[8]);
+                    pm[cb] = fmaxf(fmaxf(pm[cb], a[9]), a[10]);
+                    pm[cb] = fmaxf(fmaxf(pm[cb], a[11]), a[12]);
+                    break;
+                case 2:
+                    pm[cb] = fmaxf(fmaxf(pm[cb], a[13]), a[14]);
+                    pm[cb] = fmaxf(pm[cb], a[15]);
+                    pimp[cb] = pm[cb] > best[cb];
+                    break;
+                case 3: case 4: case 5: case 6: {
+                    const int r0 = 4 * (piece - 3);
+#pragma unroll
+                    for (int r = r0; r < r0 + 4; ++r) saved[cb][r] = pimp[cb] ? a[r] : saved[cb][r];
+                    break;
                 }
+                default:
+                    best[cb] = pimp[cb] ? pm[cb] : best[cb];
+                    bblk[cb] = pimp[cb] ? blk : bblk[cb];
+                    break;
             }
         }
-        if (tid < TK) s_hn[buf][tid] = pre_hn;
     };
 
-    gload(0);
-    lstore(0);
+    // One 32-row block: the first MFMA of each column block takes -|c|^2/2 of
+    // the lane's 16 rows as its C operand (one LDS read shared by the column
+    // blocks); A operands are loaded two k-steps ahead.  After the MFMAs of
+    // each k-step comes one piece of the previous block's epilogue, and a
+    // scheduling fence keeps that order, so the matrix core and the vector
+    // ALU are busy at the same time.
+    auto mma_block = [&](const char* tile, int rb, f32x16* acc, const f32x16* prev, int32_t pblk) {
+        const float* hn = (const float*)(tile + TK * RB);
+        f32x16 h;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *(const f32x4*)&hn[rb * 32 + 8 * g + 4 * half];
+            h[4 * g + 0] = v[0];
+            h[4 * g + 1] = v[1];
+            h[4 * g + 2] = v[2];
+            h[4 * g + 3] = v[3];
+        }
+        const char* arow = tile + rb * 32 * RB;
+        auto lda = [&](int ks) -> F {
+            if constexpr (sizeof(T) == 4) return *(const float*)(arow + aoff[ks]);
+            else return __builtin_bit_cast(F, *(const u32x4*)(arow + aoff[ks]));
+        };
+        F a0 = lda(0);
+        F a1 = KSTEPS > 1 ? lda(1) : a0;
+        constexpr int PER = (KSTEPS + 7) / 8;  // k-steps per epilogue piece
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const F a = a0;
+            a0 = a1;
+            if (ks + 2 < KSTEPS) a1 = lda(ks + 2);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) acc[cb] = M::mma(a, bx[cb][ks], ks == 0 ? h : acc[cb]);
+            if (ks % PER == PER - 1 || ks == KSTEPS - 1) {
+                // pieces not reached by short blocks are finished on the last k-step
+                const int piece = ks / PER;
+                if (ks == KSTEPS - 1) {
+#pragma unroll
+                    for (int pc = piece; pc < 8; ++pc) epi_piece(pc, prev, pblk);
+                }
+                else
+                    epi_piece(piece, prev, pblk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto epilogue = [&](const f32x16* v, int32_t blk) {
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) epi_piece(pc, v, blk);
+    };
+
+    // wait for tile 0 (tile 1 may still be in flight), then make it visible
+    if (NBUF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(Cfg::NIW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
+    // Software pipeline over 32-row blocks (acc0 / acc1 alternate).  The loop
+    // body is one basic block: every iteration issues the DMA of tile
+    // t + NBUF - 1 (past the end it re-reads the last tile into the buffer no
+    // one reads), so the vmcnt bookkeeping is the same on every iteration.
+    f32x16 acc0[NCB], acc1[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc1[cb][r] = -INFINITY;
+    int32_t blk1 = 0;
     for (int64_t t = 0; t < ntiles; ++t) {
-        const int buf = (int)(t & 1);
-        if (t + 1 < ntiles) gload(t + 1);
-
-#pragma unroll
-        for (int rb = 0; rb < TK / 32; ++rb) {
-            // accumulator init: -||c||^2/2 of this lane's 16 rows
-            f32x16 cinit;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 h = *(const f32x4*)&s_hn[buf][rb * 32 + 8 * g + 4 * half];
-                cinit[4 * g + 0] = h[0];
-                cinit[4 * g + 1] = h[1];
-                cinit[4 * g + 2] = h[2];
-                cinit[4 * g + 3] = h[3];
-            }
-            f32x16 acc[NCB];
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) acc[cb] = cinit;
-            const T* arow = &s_c[buf][(rb * 32 + col) * LDR + half * M::EPL];
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                F a;
-                if constexpr (sizeof(T) == 4) a = arow[ks * M::KS];
-                else a = __builtin_bit_cast(F, *(const u32x4*)(arow + ks * M::KS));
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb] = M::mma(a, bx[cb][ks], acc[cb]);
-            }
-            const int32_t jbase = (int32_t)(t * TK) + rb * 32 + 4 * half;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = acc[cb][r];
-                    const int32_t j = jbase + 8 * (r >> 2) + (r & 3);
-                    const bool gt = v > best[cb];
-                    best[cb] = gt ? v : best[cb];
-                    bidx[cb] = gt ? j : bidx[cb];
-                }
-            }
-        }
-
-        if (t + 1 < ntiles) lstore(buf ^ 1);
+        const char* tile = s_tile[t % NBUF];
+        const int64_t tn = (t + NBUF - 1 < ntiles) ? t + NBUF - 1 : ntiles - 1;
+        dma_tile<T, DP>(Bb + tn * (int64_t)Cfg::TILE, s_tile[(t + NBUF - 1) % NBUF], wave, lane);
+        const int32_t blk0 = (int32_t)(2 * t);
+        mma_block(tile, 0, acc0, acc1, blk1);
+        mma_block(tile, 1, acc1, acc0, blk0);
+        blk1 = blk0 + 1;
+        // tile t+1 must have landed before the barrier that publishes it
+        if (NBUF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * Cfg::NIW));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
+    // no DMA may still be writing this block's LDS when it exits
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    epilogue(acc1, blk1);
 
-    // ---- merge the two half-waves that share a point; write results ----
+    // ---- recover the row, merge the two half-waves that share a point ----
     double obj = 0.0;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
+        int rs = 15;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) rs = (saved[cb][r] == best[cb]) ? r : rs;  // first (smallest) row
+        int32_t bidx = bblk[cb] * 32 + 8 * (rs >> 2) + 4 * half + (rs & 3);
         const float ob = __shfl_xor(best[cb], 32, 64);
-        const int32_t oi = __shfl_xor(bidx[cb], 32, 64);
-        if (ob > best[cb] || (ob == best[cb] && oi < bidx[cb])) {
+        const int32_t oi = __shfl_xor(bidx, 32, 64);
+        if (ob > best[cb] || (ob == best[cb] && oi < bidx)) {
             best[cb] = ob;
-            bidx[cb] = oi;
+            bidx = oi;
         }
         const int64_t p = pidx[cb];
         if (half == 0 && p < N) {
             const float dist = fmaxf(xx[cb] - 2.f * best[cb], 0.f);
-            labels[b * N + p] = bidx[cb];
+            labels[b * N + p] = bidx;
             if (min_dist) min_dist[b * N + p] = dist;
             obj += (double)(w ? w[b * N + p] : 1.f) * (double)dist;
         }
@@ -309,45 +416,44 @@ int64_t assign_mfma_blocks(int64_t N, int DP, DType xt) {
 }
 
 template <typename T, int DP>
-static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* chat,
-                           const float* hnorm, int64_t Kp, const float* w, int32_t* labels,
-                           float* min_dist, double* obj_part, int64_t nblk, hipStream_t s) {
+static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
+                           int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
+                           double* obj_part, int64_t nblk, hipStream_t s) {
     dim3 grid((unsigned)nblk, (unsigned)B);
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
     if (vec)
         hipLaunchKernelGGL((k_assign_mfma<T, DP, true>), grid, dim3(256), 0, s, (const T*)x, N, d,
-                           (const T*)chat, hnorm, Kp, w, labels, min_dist, obj_part);
+                           (const char*)blob, ntiles, w, labels, min_dist, obj_part);
     else
         hipLaunchKernelGGL((k_assign_mfma<T, DP, false>), grid, dim3(256), 0, s, (const T*)x, N, d,
-                           (const T*)chat, hnorm, Kp, w, labels, min_dist, obj_part);
+                           (const char*)blob, ntiles, w, labels, min_dist, obj_part);
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, const void* chat,
-                            const float* hnorm, int64_t Kp, const float* w, int32_t* labels,
-                            float* min_dist, double* obj_part, int64_t nblk, hipStream_t s) {
+static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, const void* blob,
+                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
+                            double* obj_part, int64_t nblk, hipStream_t s) {
     switch (DP) {
-        case 16: return launch_t<T, 16>(x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
-        case 32: return launch_t<T, 32>(x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
-        case 64: return launch_t<T, 64>(x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
-        case 128: return launch_t<T, 128>(x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
-        case 256: return launch_t<T, 256>(x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
+        case 16: return launch_t<T, 16>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 32: return launch_t<T, 32>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 64: return launch_t<T, 64>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 128: return launch_t<T, 128>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 256: return launch_t<T, 256>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
-                              const void* chat, const float* hnorm, int64_t K, int64_t Kp,
-                              const float* w, int32_t* labels, float* min_dist, double* obj_part,
-                              int64_t nblk, hipStream_t s) {
-    (void)K;
+                              const void* blob, int64_t Kp, const float* w, int32_t* labels,
+                              float* min_dist, double* obj_part, int64_t nblk, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
+    const int64_t ntiles = Kp / kTileRows;
     if (xt == DType::F32)
-        return launch_dp<float>(DP, x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
+        return launch_dp<float>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
     if (xt == DType::F16)
-        return launch_dp<_Float16>(DP, x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
-    return launch_dp<bf16_t>(DP, x, B, N, d, chat, hnorm, Kp, w, labels, min_dist, obj_part, nblk, s);
+        return launch_dp<_Float16>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+    return launch_dp<bf16_t>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
 }
 
 }  // namespace km

@@ -29,8 +29,18 @@ inline int padded_dim(int64_t d) {
     return 256;
 }
 
+// Centroid tiles of the matrix-core assignment: kTileRows rows in the point
+// dtype, followed by a 1 KB segment holding -|c|^2/2 of those rows four
+// times (one copy per column block of points, [4][kTileRows] floats),
+// padded to a multiple of 4 KB so the four waves of a block copy equal
+// shares of it.
+constexpr int kTileRows = 64;
+constexpr int tile_bytes(int DP, int elem_bytes) {
+    return (kTileRows * DP * elem_bytes + 1024 + 4095) / 4096 * 4096;
+}
+
 // Rows of the padded centroid matrix: K rounded up to the centroid tile.
-inline int64_t padded_k(int64_t K) { return (K + 63) / 64 * 64; }
+inline int64_t padded_k(int64_t K) { return (K + kTileRows - 1) / kTileRows * kTileRows; }
 
 // Element conversions -------------------------------------------------------
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -48,8 +58,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Workspace layout ----------------------------------------------------------
 // One layout serves every entry point; all regions are 256-byte aligned.
 struct Workspace {
-    size_t chat;       // [B][Kp][DP] centroids in the point dtype (zero padded)
-    size_t hnorm;      // [B][Kp] float: -0.5 * ||c_hat||^2 (-inf for padding rows)
+    size_t chat;       // [B][Kp/64] tiles: 64 rows x DP in the point dtype + -|c|^2/2 segment
     size_t obj_part;   // [B][nblk_assign] double: per-block objective partials
     size_t labels;     // [B][N] int32: labels of the current assignment (fit)
     size_t counts;     // [B][K] int32
@@ -70,12 +79,11 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt);
 // Launchers (one per kernel family).  All take the caller's stream and
 // return the launch status.
 hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,
-                       void* chat, float* hnorm, hipStream_t s);
+                       void* blob, hipStream_t s);
 
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
-                              const void* chat, const float* hnorm, int64_t K, int64_t Kp,
-                              const float* w, int32_t* labels, float* min_dist,
-                              double* obj_part, int64_t nblk, hipStream_t s);
+                              const void* blob, int64_t Kp, const float* w, int32_t* labels,
+                              float* min_dist, double* obj_part, int64_t nblk, hipStream_t s);
 int64_t assign_mfma_blocks(int64_t N, int DP, DType xt);
 
 hipError_t launch_assign_1d(DType xt, const void* x, int64_t B, int64_t N, const float* C,

@@ -13,18 +13,24 @@
 
 namespace km {
 
-// One wave per padded centroid row; 4 rows per 256-thread block.
+// One wave per padded centroid row; 4 rows per 256-thread block.  Writes the
+// tile layout the matrix-core assignment copies to LDS: per 64-row tile, the
+// rows in the point dtype (zero padded to DP), then -|c|^2/2 of each row
+// stored four times (-inf for the padding rows K..Kp-1, which never win).
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64_t BKp, int64_t K,
-                                              int64_t Kp, int d, int DP, T* __restrict__ chat,
-                                              float* __restrict__ hnorm) {
+                                              int64_t Kp, int d, int DP, char* __restrict__ blob) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= BKp) return;
     const int64_t b = row / Kp, j = row - b * Kp;
     const bool real = j < K;
     const float* c = C + (b * K + j) * (int64_t)d;
-    T* out = chat + row * (int64_t)DP;
+    const int64_t tile = row / kTileRows;  // batches hold whole tiles (Kp % kTileRows == 0)
+    const int i = (int)(row % kTileRows);
+    const int tb = tile_bytes(DP, (int)sizeof(T));
+    char* tbase = blob + tile * tb;
+    T* out = (T*)(tbase + (int64_t)i * DP * (int)sizeof(T));
     float ss = 0.f;
     for (int k = lane; k < DP; k += 64) {
         float v = (real && k < d) ? c[k] : 0.f;
@@ -45,20 +51,22 @@ __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    if (lane == 0) hnorm[row] = real ? -0.5f * ss : -INFINITY;
+    float* hn = (float*)(tbase + kTileRows * DP * (int)sizeof(T));
+    if (lane < 4) hn[lane * kTileRows + i] = real ? -0.5f * ss : -INFINITY;
 }
 
 hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,
-                       void* chat, float* hnorm, hipStream_t s) {
+                       void* blob, hipStream_t s) {
     const int64_t rows = B * Kp;
     if (rows == 0) return hipSuccess;
     dim3 grid((unsigned)((rows + 3) / 4));
+    char* p = (char*)blob;
     if (xt == DType::F32)
-        hipLaunchKernelGGL(k_prep<float>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, (float*)chat, hnorm);
+        hipLaunchKernelGGL(k_prep<float>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, p);
     else if (xt == DType::F16)
-        hipLaunchKernelGGL(k_prep<_Float16>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, (_Float16*)chat, hnorm);
+        hipLaunchKernelGGL(k_prep<_Float16>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, p);
     else
-        hipLaunchKernelGGL(k_prep<bf16_t>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, (bf16_t*)chat, hnorm);
+        hipLaunchKernelGGL(k_prep<bf16_t>, grid, dim3(256), 0, s, C, rows, K, Kp, d, DP, p);
     return hipGetLastError();
 }
 

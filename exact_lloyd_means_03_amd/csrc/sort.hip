@@ -129,13 +129,13 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, i
     // counts must be zero on entry (the caller clears it with the other accumulators)
     if (B == 0) return hipSuccess;
     const size_t lds = (size_t)K * sizeof(int32_t);
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)k_count, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        (void)hipFuncSetAttribute((const void*)k_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
-    }
     hipError_t e;
+    if (lds > 64 * 1024) {
+        if ((e = hipFuncSetAttribute((const void*)k_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+            return e;
+        if ((e = hipFuncSetAttribute((const void*)k_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+            return e;
+    }
     if (N > 0) {
         const int64_t CH = sort_chunk(B, N, K);
         dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);

@@ -54,6 +54,15 @@ __device__ __forceinline__ void ld_vec(const T* p, float* out) {
 
 // VEC: lane li of a row group reads elements [li*EPL, li*EPL + EPL) with one
 // 16-byte load; otherwise it reads elements li + LPR*m, m < 4.
+//
+// A wave walks its piece in chunks of kSegChunk sorted rows.  The chunk's
+// point indices are first copied to LDS with coalesced loads, so the row
+// gathers that follow depend only on an LDS read, and U row steps (U*64/LPR
+// rows) are kept in flight.  The running sums survive chunk boundaries and
+// are flushed with one atomic per coordinate whenever a segment ends and at
+// the end of the piece.
+constexpr int kSegChunk = 512;
+
 template <typename T, bool VEC, bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, const float* __restrict__ w,
                                                    int64_t N, int d, int lpr_shift,
@@ -63,9 +72,10 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                                                    int K, int TW, float* __restrict__ sums,
                                                    float* __restrict__ wsum) {
     constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 4;
-    constexpr int U = 4;  // row steps in flight
-    const int lane = threadIdx.x & 63;
-    const int64_t piece = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int U = 8;  // row steps in flight
+    __shared__ int32_t s_idx[4][kSegChunk];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t piece = (int64_t)blockIdx.x * 4 + wv;
     const int64_t b = blockIdx.y;
     if (piece >= npieces) return;
     const int32_t* offb = offsets + b * (K + 1);
@@ -80,13 +90,14 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
     const T* Xb = X + b * N * (int64_t)d;
     const float* wb = WEIGHTED ? w + b * N : nullptr;
     const int32_t* pb = perm + b * N;
+    int32_t* sidx = s_idx[wv];
 
     // window of offsets: lane l holds offsets[wbase + l] (INT_MAX past K)
     int wbase = piece_seg[b * npieces + piece];
     int32_t win = (wbase + lane <= K) ? offb[wbase + lane] : 0x7fffffff;
-    int32_t q = (int32_t)q0;
-    while (q < q1) {
-        // segment containing q: the last j with offsets[j] <= q
+    // segment containing q: the last j with offsets[j] <= q; returns its end
+    int j = 0;
+    auto locate = [&](int32_t q) -> int32_t {
         unsigned long long m = __ballot(win > q);
         while (m == 0ull) {
             wbase += 63;
@@ -94,74 +105,97 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
             m = __ballot(win > q);
         }
         const int l = __ffsll((long long)m) - 1;  // first lane with offsets > q (l >= 1)
-        const int j = wbase + l - 1;
-        const int32_t send = __shfl(win, l, 64);
-        const int32_t e = send < q1 ? send : q1;
+        j = wbase + l - 1;
+        return __shfl(win, l, 64);
+    };
 
-        float acc[EPL];
+    float acc[EPL];
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
+    float wacc = 0.f;
+    auto flush = [&]() {
+        for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+            for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
+            if constexpr (WEIGHTED) wacc += __shfl_xor(wacc, o, 64);
+        }
+        float* sj = sums + (b * K + j) * (int64_t)d;
+        if (gl == 0 && active) {
+#pragma unroll
+            for (int t = 0; t < EPL; ++t) {
+                const int k = VEC ? li * EPL + t : li + LPR * t;
+                if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
+            }
+        }
+        if constexpr (WEIGHTED) {
+            if (lane == 0) unsafeAtomicAdd(wsum + b * K + j, wacc);
+        }
 #pragma unroll
         for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
-        float wacc = 0.f;
-        for (int32_t r = q + gl; r < e; r += RPW * U) {
-            int32_t idx[U];
+        wacc = 0.f;
+    };
+
+    int32_t send = locate((int32_t)q0);
+    bool pending = false;  // rows accumulated since the last flush
+    for (int32_t c0 = (int32_t)q0; c0 < q1; c0 += kSegChunk) {
+        const int32_t c1 = (c0 + kSegChunk < q1) ? c0 + kSegChunk : q1;
+        // stage this chunk's point indices in LDS
+        for (int32_t r = c0 + lane; r < c1; r += 64) sidx[r - c0] = pb[r];
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        int32_t q = c0;
+        while (q < c1) {
+            const int32_t e = send < c1 ? send : c1;
+            for (int32_t r = q + gl; r < e; r += RPW * U) {
+                int32_t idx[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t rr = r + u * RPW;
-                idx[u] = rr < e ? pb[rr] : -1;
-            }
-            float v[U][EPL];
-            float wi[U];
+                for (int u = 0; u < U; ++u) {
+                    const int32_t rr = r + u * RPW;
+                    idx[u] = rr < e ? sidx[rr - c0] : -1;
+                }
+                float v[U][EPL];
+                float wi[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool ok = idx[u] >= 0;
-                const T* row = Xb + (int64_t)(ok ? idx[u] : 0) * d;
-                if constexpr (VEC) {
-                    if (ok && active) ld_vec<T>(row + li * EPL, v[u]);
-                    else {
+                for (int u = 0; u < U; ++u) {
+                    const bool ok = idx[u] >= 0;
+                    const T* row = Xb + (int64_t)(ok ? idx[u] : 0) * d;
+                    if constexpr (VEC) {
+                        if (ok && active) ld_vec<T>(row + li * EPL, v[u]);
+                        else {
 #pragma unroll
-                        for (int t = 0; t < EPL; ++t) v[u][t] = 0.f;
+                            for (int t = 0; t < EPL; ++t) v[u][t] = 0.f;
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < EPL; ++t) {
+                            const int k = li + LPR * t;
+                            v[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
+                        }
                     }
-                } else {
+                    if constexpr (WEIGHTED) wi[u] = ok ? wb[idx[u]] : 0.f;
+                    else wi[u] = ok ? 1.f : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int t = 0; t < EPL; ++t) {
-                        const int k = li + LPR * t;
-                        v[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
+                        if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[u][t], acc[t]);
+                        else acc[t] += v[u][t];
                     }
+                    wacc += wi[u];
                 }
-                if constexpr (WEIGHTED) wi[u] = ok ? wb[idx[u]] : 0.f;
-                else wi[u] = ok ? 1.f : 0.f;
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int t = 0; t < EPL; ++t) {
-                    if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[u][t], acc[t]);
-                    else acc[t] += v[u][t];
-                }
-                wacc += wi[u];
+            pending = pending || (e > q);
+            q = e;
+            if (q == send) {  // the segment ends here
+                if (pending) flush();
+                pending = false;
+                if (q < q1) send = locate(q);
             }
         }
-        if (e > q) {
-            // reduce the row groups of the wave, then one atomic per coordinate
-            for (int o = LPR; o < 64; o <<= 1) {
-#pragma unroll
-                for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
-                if constexpr (WEIGHTED) wacc += __shfl_xor(wacc, o, 64);
-            }
-            float* sj = sums + (b * K + j) * (int64_t)d;
-            if (gl == 0 && active) {
-#pragma unroll
-                for (int t = 0; t < EPL; ++t) {
-                    const int k = VEC ? li * EPL + t : li + LPR * t;
-                    if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
-                }
-            }
-            if constexpr (WEIGHTED) {
-                if (lane == 0) unsafeAtomicAdd(wsum + b * K + j, wacc);
-            }
-        }
-        q = e;
+        __builtin_amdgcn_wave_barrier();
     }
+    if (pending) flush();
 }
 
 // Rows per wave piece: enough pieces to fill the chip, and long pieces when

@@ -62,11 +62,17 @@ def test_assign_parity(km, dtype, B, N, d, K):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("K", [1, 2, 8, 16, 100, 1024, 1500])
+@pytest.mark.parametrize("K", [1, 2, 8, 16, 100, 1024, 1500, 16384])
 def test_assign_1d_parity(km, dtype, K):
     x, C = _rand_problem(3, 5000, 1, K, dtype, seed=K, spread=0.05)
     w = torch.rand(3, 5000) * 0.9 + 0.1
     _assign_case(km, x, C, w=w, what=f"1d {dtype} K{K}")
+
+
+def test_assign_1d_rejects_huge_k(km):
+    x = torch.zeros(1, 10, 1, device="cuda")
+    with pytest.raises(km.KMeansError, match="K <= 16384"):
+        km.kmeans_assign(x, torch.zeros(1, 16385, 1, device="cuda"))
 
 
 def test_assign_1d_exact_ties(km):
@@ -75,6 +81,11 @@ def test_assign_1d_exact_ties(km):
     x = torch.tensor([[[0.25], [0.75], [-0.5], [1.0], [2.0], [-3.0], [0.5]]])
     labels, md, _ = km.kmeans_assign(x.cuda(), C.cuda(), min_dist=True)
     np.testing.assert_array_equal(labels.cpu().numpy()[0], [0, 1, 0, 1, 1, 3, 4])
+    # -0 and +0 are the same value: the smaller index wins among all equidistant centroids
+    C = torch.tensor([[[2.0], [-0.0], [0.0], [-2.0]]])
+    x = torch.tensor([[[1.0], [-1.0], [0.0], [-0.0]]])
+    labels, _, _ = km.kmeans_assign(x.cuda(), C.cuda())
+    np.testing.assert_array_equal(labels.cpu().numpy()[0], [0, 1, 1, 1])
 
 
 def test_duplicate_centroids_smallest_index(km):
