@@ -49,7 +49,8 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
         return at;
     };
     const size_t Bz = (size_t)B;
-    w.chat = take(a1d ? 0 : Bz * (w.Kp / kTileRows) * (size_t)tile_bytes(w.DP, dtype_bytes(xt)));
+    w.chat = take(a1d ? 0 : Bz * (w.Kp / tile_rows(w.DP, dtype_bytes(xt))) *
+                                (size_t)tile_bytes(w.DP, dtype_bytes(xt)));
     w.obj_part = take(Bz * w.nblk_assign * sizeof(double));
     w.labels = take(Bz * N * sizeof(int32_t));
     w.counts = take(Bz * K * sizeof(int32_t));

@@ -11,7 +11,7 @@
 //   * one 64-lane wave owns NCB column blocks of 32 points; their coordinates
 //     stay in VGPRs for the whole kernel as the B operand of
 //     v_mfma_f32_32x32x16_{f16,bf16} (v_mfma_f32_32x32x2_f32 for float32);
-//   * centroid tiles of 64 rows (with their -|c|^2/2 values appended) move
+//   * centroid tiles of 64 or 128 rows (with their -|c|^2/2 values appended) move
 //     from device memory to LDS by direct DMA (global_load_lds_dwordx4), up to
 //     three buffers deep, and are shared by the 4 waves of the block; rows are
 //     XOR-swizzled in 16-byte chunks so the 32 A-operand rows read by one
@@ -121,17 +121,25 @@ __device__ __forceinline__ typename Mf<T>::frag load_point_frag(const T* row, in
 
 template <typename T, int DP>
 struct AssignCfg {
+#ifdef KM_NCB
+    static constexpr int NCB = (DP * (int)sizeof(T) <= 256) ? KM_NCB : ((DP * (int)sizeof(T) <= 512) ? 2 : 1);
+#else
     static constexpr int NCB = (DP * (int)sizeof(T) <= 512) ? 2 : 1;   // 32-point blocks per wave
-    static constexpr int WAVES = 4;
+#endif
+    static constexpr int WAVES = assign_waves(DP, sizeof(T));
     static constexpr int PTS = WAVES * NCB * 32;                         // points per block
-    static constexpr int TK = kTileRows;                                  // centroid rows per tile (2 blocks)
+    static constexpr int TK = tile_rows(DP, sizeof(T));                   // centroid rows per tile
+    static_assert(TK % 64 == 0, "tiles hold an even number of 32-row blocks");
     static constexpr int RB = DP * (int)sizeof(T);                       // bytes per centroid row
     static constexpr int CPR = RB / 16;                                   // 16-byte chunks per row
     static constexpr int SW = CPR < 32 ? CPR : 32;                        // XOR swizzle period (rows)
     static constexpr int TILE = tile_bytes(DP, sizeof(T));                // rows + the -|c|^2/2 segment
     static constexpr int NI = TILE / 1024;                                // 1 KB DMA instructions per tile
     static constexpr int NIW = NI / WAVES;                                // ... per wave
-    static constexpr int NBUF = 3 * TILE <= 150 * 1024 ? 3 : 2;           // LDS tile buffers
+#ifndef KM_NBUF
+#define KM_NBUF 2
+#endif
+    static constexpr int NBUF = KM_NBUF * TILE <= 150 * 1024 ? KM_NBUF : 2;  // LDS tile buffers
     static constexpr int KSTEPS = DP / Mf<T>::KS;
 };
 
@@ -139,42 +147,47 @@ constexpr uint32_t vmcnt_imm(int n) {  // s_waitcnt with only vmcnt <= n
     return (uint32_t)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One global_load_lds_dwordx4: lane l copies 16 bytes from g to LDS byte
-// lds + 16 l (lds must be the same for the whole wave).  Written as a
-// one-instruction asm statement so the compiler does not treat the in-flight
-// LDS write as aliasing every later LDS read (it would wait for the copy
-// right after issuing it); the kernel waits on vmcnt explicitly before the
-// barrier that publishes a tile.  The instruction has no register results.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
+// One global_load_lds_dwordx4: lane l copies 16 bytes from sbase + voff to
+// LDS byte lds + 16 l (sbase and lds are wave-uniform: an SGPR pair and M0).
+// Written as a one-instruction asm statement so the compiler does not treat
+// the in-flight LDS write as aliasing every later LDS read (it would wait for
+// the copy right after issuing it); the kernel waits on vmcnt explicitly
+// before the barrier that publishes a tile.  The instruction has no register
+// results.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, const void* lds) {
     const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(l)) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(l))
+                 : "memory");
 }
 
-// Copy tile t of this batch's blob into LDS buffer `dst` with 1 KB DMA
-// instructions (lane l of instruction i writes LDS bytes i*1024 + 16 l).
-// Row chunks are XOR-swizzled: LDS chunk position p of row r holds global
-// chunk p ^ (r % SW), SW = min(chunks per row, 32), so the 32 rows read by one
-// A-operand instruction hit distinct banks without padding, and the swizzle
-// of row r depends only on r % 32 (the same for both 32-row blocks).
+// Source offset (within a tile) of the 16 bytes lane `lane` copies with the
+// DMA instruction i.  Row chunks are XOR-swizzled: LDS chunk position q of
+// row r holds global chunk q ^ (r % SW), SW = min(chunks per row, 32), so the
+// 32 rows read by one A-operand instruction hit distinct banks without
+// padding, and the swizzle of row r depends only on r % 32.  Bytes past the
+// rows (the -|c|^2/2 segment and padding) are copied unchanged.
 template <typename T, int DP>
-__device__ __forceinline__ void dma_tile(const char* __restrict__ tile_g, char* dst, int wave, int lane) {
+__device__ __forceinline__ uint32_t dma_src(int i, int lane) {
+    typedef AssignCfg<T, DP> Cfg;
+    const int p = i * 1024 + lane * 16;
+    if (p >= Cfg::TK * Cfg::RB) return (uint32_t)p;
+    const int r = p / Cfg::RB, q = (p % Cfg::RB) / 16;
+    return (uint32_t)(r * Cfg::RB + ((q ^ (r % Cfg::SW)) * 16));
+}
+
+// Copy one tile (global bytes tile_g) into LDS buffer dst: wave w issues the
+// 1 KB instructions i = n * WAVES + w, with precomputed source offsets.
+template <typename T, int DP>
+__device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave, const uint32_t* voff) {
     typedef AssignCfg<T, DP> Cfg;
     static_assert(Cfg::NI % Cfg::WAVES == 0, "tile must split evenly over the waves");
 #pragma unroll
-    for (int n = 0; n < Cfg::NIW; ++n) {
-        const int i = n * Cfg::WAVES + wave;
-        const int p = i * 1024 + lane * 16;
-        int src = p;
-        if (p < Cfg::TK * Cfg::RB) {
-            const int r = p / Cfg::RB, q = (p % Cfg::RB) / 16;
-            src = r * Cfg::RB + ((q ^ (r % Cfg::SW)) * 16);
-        }
-        dma16(tile_g + src, dst + i * 1024);
-    }
+    for (int n = 0; n < Cfg::NIW; ++n) dma16(tile_g, voff[n], dst + (n * Cfg::WAVES + wave) * 1024);
 }
 
 template <typename T, int DP, bool VEC>
-__global__ __launch_bounds__(256) void k_assign_mfma(
+__global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfma(
     const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int64_t ntiles,
     const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
     double* __restrict__ obj_part) {
@@ -192,10 +205,14 @@ __global__ __launch_bounds__(256) void k_assign_mfma(
     const T* Xb = X + b * N * (int64_t)d;
     const char* Bb = blob + b * ntiles * (int64_t)Cfg::TILE;
 
+    // per-lane DMA source offsets (the same for every tile)
+    uint32_t voff[Cfg::NIW];
+#pragma unroll
+    for (int n = 0; n < Cfg::NIW; ++n) voff[n] = dma_src<T, DP>(n * Cfg::WAVES + wave, lane);
     // start the first tiles' DMA before the point loads
 #pragma unroll
     for (int t = 0; t < NBUF - 1; ++t)
-        if (t < ntiles) dma_tile<T, DP>(Bb + (int64_t)t * Cfg::TILE, s_tile[t], wave, lane);
+        if (t < ntiles) dma_tile<T, DP>(Bb + (int64_t)t * Cfg::TILE, s_tile[t], wave, voff);
 
     // ---- points of this wave: B operand fragments + squared norms -------
     F bx[NCB][KSTEPS];
@@ -346,11 +363,14 @@ __global__ __launch_bounds__(256) void k_assign_mfma(
     for (int64_t t = 0; t < ntiles; ++t) {
         const char* tile = s_tile[t % NBUF];
         const int64_t tn = (t + NBUF - 1 < ntiles) ? t + NBUF - 1 : ntiles - 1;
-        dma_tile<T, DP>(Bb + tn * (int64_t)Cfg::TILE, s_tile[(t + NBUF - 1) % NBUF], wave, lane);
-        const int32_t blk0 = (int32_t)(2 * t);
-        mma_block(tile, 0, acc0, acc1, blk1);
-        mma_block(tile, 1, acc1, acc0, blk0);
-        blk1 = blk0 + 1;
+        dma_tile<T, DP>(Bb + tn * (int64_t)Cfg::TILE, s_tile[(t + NBUF - 1) % NBUF], wave, voff);
+#pragma unroll
+        for (int rb = 0; rb < TK / 32; rb += 2) {
+            const int32_t blk0 = (int32_t)(t * (TK / 32)) + rb;
+            mma_block(tile, rb, acc0, acc1, blk1);
+            mma_block(tile, rb + 1, acc1, acc0, blk0);
+            blk1 = blk0 + 1;
+        }
         // tile t+1 must have landed before the barrier that publishes it
         if (NBUF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * Cfg::NIW));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -422,10 +442,10 @@ static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const voi
     dim3 grid((unsigned)nblk, (unsigned)B);
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
     if (vec)
-        hipLaunchKernelGGL((k_assign_mfma<T, DP, true>), grid, dim3(256), 0, s, (const T*)x, N, d,
+        hipLaunchKernelGGL((k_assign_mfma<T, DP, true>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s, (const T*)x, N, d,
                            (const char*)blob, ntiles, w, labels, min_dist, obj_part);
     else
-        hipLaunchKernelGGL((k_assign_mfma<T, DP, false>), grid, dim3(256), 0, s, (const T*)x, N, d,
+        hipLaunchKernelGGL((k_assign_mfma<T, DP, false>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s, (const T*)x, N, d,
                            (const char*)blob, ntiles, w, labels, min_dist, obj_part);
     return hipGetLastError();
 }
@@ -448,12 +468,11 @@ hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
                               float* min_dist, double* obj_part, int64_t nblk, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
-    const int64_t ntiles = Kp / kTileRows;
     if (xt == DType::F32)
-        return launch_dp<float>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        return launch_dp<float>(DP, x, B, N, d, blob, Kp / tile_rows(DP, 4), w, labels, min_dist, obj_part, nblk, s);
     if (xt == DType::F16)
-        return launch_dp<_Float16>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
-    return launch_dp<bf16_t>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        return launch_dp<_Float16>(DP, x, B, N, d, blob, Kp / tile_rows(DP, 2), w, labels, min_dist, obj_part, nblk, s);
+    return launch_dp<bf16_t>(DP, x, B, N, d, blob, Kp / tile_rows(DP, 2), w, labels, min_dist, obj_part, nblk, s);
 }
 
 }  // namespace km

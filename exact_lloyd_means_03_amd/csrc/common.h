@@ -29,18 +29,32 @@ inline int padded_dim(int64_t d) {
     return 256;
 }
 
-// Centroid tiles of the matrix-core assignment: kTileRows rows in the point
-// dtype, followed by a 1 KB segment holding -|c|^2/2 of those rows four
-// times (one copy per column block of points, [4][kTileRows] floats),
-// padded to a multiple of 4 KB so the four waves of a block copy equal
-// shares of it.
-constexpr int kTileRows = 64;
+// Centroid tiles of the matrix-core assignment: tile_rows() rows in the point
+// dtype, followed by a 1 KB segment holding -|c|^2/2 of those rows (first
+// tile_rows() floats), padded so that every wave of an assignment block
+// copies an equal number of 1 KB pieces.  Large rows get 64-row tiles so two tile
+// buffers fit in LDS.
+#ifndef KM_TILE_ROWS
+#define KM_TILE_ROWS 128
+#endif
+constexpr int kTileRowsMax = 128;
+constexpr int tile_rows(int DP, int elem_bytes) {
+    return (KM_TILE_ROWS * DP * elem_bytes <= 32 * 1024) ? KM_TILE_ROWS : 64;
+}
+#ifndef KM_WAVES
+#define KM_WAVES 8
+#endif
+// Waves per assignment block: rows of up to 256 bytes keep their points in
+// few enough registers for 8 waves (two per SIMD); larger rows use 4 waves so
+// each wave may use the whole register file.
+constexpr int assign_waves(int DP, int elem_bytes) { return DP * elem_bytes <= 256 ? KM_WAVES : 4; }
 constexpr int tile_bytes(int DP, int elem_bytes) {
-    return (kTileRows * DP * elem_bytes + 1024 + 4095) / 4096 * 4096;
+    return (tile_rows(DP, elem_bytes) * DP * elem_bytes + 1024 + assign_waves(DP, elem_bytes) * 1024 - 1) /
+           (assign_waves(DP, elem_bytes) * 1024) * (assign_waves(DP, elem_bytes) * 1024);
 }
 
-// Rows of the padded centroid matrix: K rounded up to the centroid tile.
-inline int64_t padded_k(int64_t K) { return (K + kTileRows - 1) / kTileRows * kTileRows; }
+// Rows of the padded centroid matrix: K rounded up to the largest tile.
+inline int64_t padded_k(int64_t K) { return (K + kTileRowsMax - 1) / kTileRowsMax * kTileRowsMax; }
 
 // Element conversions -------------------------------------------------------
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -58,7 +72,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Workspace layout ----------------------------------------------------------
 // One layout serves every entry point; all regions are 256-byte aligned.
 struct Workspace {
-    size_t chat;       // [B][Kp/64] tiles: 64 rows x DP in the point dtype + -|c|^2/2 segment
+    size_t chat;       // [B][Kp/tile_rows] tiles: rows x DP in the point dtype + -|c|^2/2 segment
     size_t obj_part;   // [B][nblk_assign] double: per-block objective partials
     size_t labels;     // [B][N] int32: labels of the current assignment (fit)
     size_t counts;     // [B][K] int32

@@ -14,9 +14,9 @@
 namespace km {
 
 // One wave per padded centroid row; 4 rows per 256-thread block.  Writes the
-// tile layout the matrix-core assignment copies to LDS: per 64-row tile, the
-// rows in the point dtype (zero padded to DP), then -|c|^2/2 of each row
-// stored four times (-inf for the padding rows K..Kp-1, which never win).
+// tile layout the matrix-core assignment copies to LDS: per tile, the rows in
+// the point dtype (zero padded to DP), then -|c|^2/2 of each row (-inf for
+// the padding rows K..Kp-1, which never win).
 template <typename T>
 __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64_t BKp, int64_t K,
                                               int64_t Kp, int d, int DP, char* __restrict__ blob) {
@@ -26,8 +26,9 @@ __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64
     const int64_t b = row / Kp, j = row - b * Kp;
     const bool real = j < K;
     const float* c = C + (b * K + j) * (int64_t)d;
-    const int64_t tile = row / kTileRows;  // batches hold whole tiles (Kp % kTileRows == 0)
-    const int i = (int)(row % kTileRows);
+    const int TR = tile_rows(DP, (int)sizeof(T));
+    const int64_t tile = row / TR;  // batches hold whole tiles (Kp is a multiple of every tile size)
+    const int i = (int)(row % TR);
     const int tb = tile_bytes(DP, (int)sizeof(T));
     char* tbase = blob + tile * tb;
     T* out = (T*)(tbase + (int64_t)i * DP * (int)sizeof(T));
@@ -51,8 +52,8 @@ __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    float* hn = (float*)(tbase + kTileRows * DP * (int)sizeof(T));
-    if (lane < 4) hn[lane * kTileRows + i] = real ? -0.5f * ss : -INFINITY;
+    float* hn = (float*)(tbase + (int64_t)TR * DP * (int)sizeof(T));
+    if (lane == 0) hn[i] = real ? -0.5f * ss : -INFINITY;
 }
 
 hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,

@@ -228,6 +228,35 @@ void oracle_update(const double *X, const double *w, const int32_t *labels,
 }
 
 /* ----------------------------------------------------------------------- *
+ * Objective of given labels: J_b = sum_i w_i * sum_k (x_ik - c_{l_i,k})^2,
+ * i ascending, fp64.  With the labels of the assignment stage this is the
+ * objective of that iteration.  C [B,K,d] fp64 (centroids in the point
+ * dtype), w may be NULL.  Labels outside [0, K) contribute nothing.
+ * ----------------------------------------------------------------------- */
+void oracle_objective(const double *X, const double *w, const int32_t *labels,
+                      int64_t B, int64_t N, int64_t d, const double *C, int64_t K,
+                      double *J)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        double s = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            const int64_t j = labels[b * N + i];
+            if (j < 0 || j >= K) continue;
+            const double *x = X + (b * N + i) * d;
+            const double *c = C + (b * K + j) * d;
+            double D = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                const double t = x[k] - c[k];
+                D += t * t;
+            }
+            s += (w ? w[b * N + i] : 1.0) * D;
+        }
+        J[b] = s;
+    }
+}
+
+/* ----------------------------------------------------------------------- *
  * n_iter Lloyd iterations from init [B,K,d] fp32.  x holds the stored bits
  * (float32, or uint16 for fp16/bf16).  w [B,N] fp32 or NULL.
  * Outputs: C_out [B,K,d] (centroids after the last update), labels_out and

@@ -39,6 +39,7 @@ def lib():
         L.oracle_round.argtypes = [p, i64, C.c_int, p]
         L.oracle_assign.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
         L.oracle_update.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p]
+        L.oracle_objective.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
         L.oracle_fit.argtypes = [p, C.c_int, p, i64, i64, i64, i64, p, C.c_int32,
                                  p, p, p, p, p, p]
         L.oracle_fit.restype = C.c_int
@@ -109,6 +110,19 @@ def update(X: np.ndarray, w, labels: np.ndarray, c_old: np.ndarray):
     lib().oracle_update(_ptr(X), _ptr(wd), _ptr(labels), B, N, d, K, _ptr(c_old),
                         _ptr(c_new), _ptr(counts), _ptr(S), _ptr(W))
     return c_new, counts, S, W
+
+
+def objective(X: np.ndarray, w, labels: np.ndarray, Chat: np.ndarray) -> np.ndarray:
+    """J [B] = sum_i w_i |x_i - c_{l_i}|^2 of given labels (fp64)."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    B, N, d = X.shape
+    Chat = np.ascontiguousarray(Chat, dtype=np.float64)
+    K = Chat.shape[1]
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    wd = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
+    J = np.empty(B, np.float64)
+    lib().oracle_objective(_ptr(X), _ptr(wd), _ptr(labels), B, N, d, _ptr(Chat), K, _ptr(J))
+    return J
 
 
 def fit(x_bits: np.ndarray, dtype: str, w, init: np.ndarray, n_iter: int) -> dict:

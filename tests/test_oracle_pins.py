@@ -344,3 +344,21 @@ def test_lloyd_invariants_on_mixture(orc):
                 s = np.bincount(rn["labels"][b], weights=X[b, :, k], minlength=wl.K)
                 want = np.where(cnt > 0, s / np.maximum(cnt, 1), rp["centroids"][b, :, k])
                 np.testing.assert_allclose(rn["centroids"][b, :, k], want, rtol=1e-6, atol=1e-7)
+
+
+def test_objective_of_labels(orc):
+    """J of the assignment's labels equals the fit's J; J of other labels is larger."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((2, 300, 5)).astype(np.float32)
+    w = rng.uniform(0.1, 1, (2, 300)).astype(np.float32)
+    init = X[:, :7].copy()
+    r = orc.fit(X, "f32", w, init, 1)
+    Xd = X.astype(np.float64)
+    J = orc.objective(Xd, w, r["labels"], init.astype(np.float64))
+    np.testing.assert_allclose(J, r["J"][:, 0], rtol=1e-12)
+    # direct formula on one batch
+    lab = r["labels"][1]
+    want = (w[1].astype(np.float64) * ((Xd[1] - init[1][lab].astype(np.float64)) ** 2).sum(1)).sum()
+    assert abs(J[1] - want) <= 1e-10 * want
+    worse = orc.objective(Xd, w, (r["labels"] + 1) % 7, init.astype(np.float64))
+    assert np.all(worse > J)
