@@ -153,10 +153,13 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
     return KM_OK;
 }
 
+// piece_seg (may be NULL): also record the first segment of every reduction piece.
 km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts, int32_t* offsets,
-                   int32_t* perm, const Workspace& W, void* ws, hipStream_t s) {
+                   int32_t* perm, int32_t* piece_seg, const Workspace& W, void* ws, hipStream_t s) {
     KM_HIP(launch_zero(counts, (size_t)B * K * sizeof(int32_t), s), "zero");
-    KM_HIP(launch_sort(labels, B, N, K, counts, offsets, at<int32_t>(ws, W.cursor), perm, s), "sort");
+    KM_HIP(launch_sort(labels, B, N, K, counts, offsets, at<int32_t>(ws, W.cursor), perm, segreduce_tw(B, N),
+                       segreduce_pieces(B, N), piece_seg, s),
+           "sort");
     return KM_OK;
 }
 
@@ -174,9 +177,9 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
     KM_HIP(launch_zero(sums, W.offsets - W.sums, s), "zero");
     int32_t* offsets = at<int32_t>(ws, W.offsets);
     int32_t* perm = at<int32_t>(ws, W.perm);
-    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, W, ws, s));
-    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr,
-                            at<int32_t>(ws, W.piece_seg), s),
+    int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
+    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, W, ws, s));
+    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr, piece_seg, s),
            "segreduce");
     KM_HIP(launch_divide(sums, w ? wsum : nullptr, cnt, B, K, (int)d, c_old, c_new, s), "divide");
     return KM_OK;
@@ -224,7 +227,7 @@ km_status kmeans_sort_labels(const int32_t* labels, int64_t B, int64_t N, int64_
     int32_t* cnt = counts ? counts : at<int32_t>(workspace, W.counts);
     int32_t* ofs = offsets ? offsets : at<int32_t>(workspace, W.offsets);
     int32_t* pm = perm ? perm : at<int32_t>(workspace, W.perm);
-    return run_sort(labels, B, N, K, cnt, ofs, pm, W, workspace, (hipStream_t)stream);
+    return run_sort(labels, B, N, K, cnt, ofs, pm, nullptr, W, workspace, (hipStream_t)stream);
 }
 
 km_status kmeans_update(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d,

@@ -111,14 +111,16 @@ hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// piece_seg may be NULL (then TW and npieces are ignored).
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
                        int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* perm,
-                       hipStream_t s);
+                       int TW, int64_t npieces, int32_t* piece_seg, hipStream_t s);
 
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K,
-                            float* sums, float* wsum, int32_t* piece_seg, hipStream_t s);
+                            float* sums, float* wsum, const int32_t* piece_seg, hipStream_t s);
 int64_t segreduce_pieces(int64_t B, int64_t N);
+int segreduce_tw(int64_t B, int64_t N);
 
 hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* counts,
                          int64_t B, int64_t K, int d, const float* c_old, float* c_new,

@@ -101,16 +101,26 @@ hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* co
     return hipGetLastError();
 }
 
-// One block per batch: fixed-order strided sums, then a fixed-order tree.
-__global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t nblk,
-                                                    double* __restrict__ out, int64_t out_stride) {
-    __shared__ double red[256];
+// One block per batch: 1024 threads, each summing a fixed strided subset with
+// 8 independent accumulators (loads stay in flight), then a fixed-order tree,
+// so the result does not depend on timing.
+__global__ __launch_bounds__(1024) void k_obj_reduce(const double* __restrict__ part, int64_t nblk,
+                                                     double* __restrict__ out, int64_t out_stride) {
+    __shared__ double red[1024];
     const int64_t b = blockIdx.x;
-    double acc = 0.0;
-    for (int64_t i = threadIdx.x; i < nblk; i += 256) acc += part[b * nblk + i];
-    red[threadIdx.x] = acc;
+    const double* pb = part + b * nblk;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t i = threadIdx.x;
+    for (; i + 7 * 1024 < nblk; i += 8 * 1024) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += pb[i + u * 1024];
+    }
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+        if (i + u * 1024 < nblk) acc[u] += pb[i + u * 1024];
+    red[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
+    for (int o = 512; o >= 1; o >>= 1) {
         if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
         __syncthreads();
     }
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ p
 hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double* out,
                              int64_t out_stride, hipStream_t s) {
     if (B == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_obj_reduce, dim3((unsigned)B), dim3(256), 0, s, part, nblk, out, out_stride);
+    hipLaunchKernelGGL(k_obj_reduce, dim3((unsigned)B), dim3(1024), 0, s, part, nblk, out, out_stride);
     return hipGetLastError();
 }
 

@@ -15,6 +15,12 @@
 //                   contiguous run per non-empty bin with a single global
 //                   atomic on that bin's cursor, then places its indices in
 //                   the run with LDS atomics.
+// Chunks are large (about one block per CU over the whole job): the global
+// atomics on the cursors of the most popular clusters are serialized by the
+// memory system, so their number, blocks x non-empty bins, is what limits
+// both passes on skewed label distributions.  The scattered 4-byte index
+// stores need no staging: successive stores into a run fill the same cache
+// lines, which are merged in L2 before they reach HBM.
 // Runs of different chunks land in a segment in arrival order, so the order
 // inside a segment is unspecified; the set of indices is exact.
 // Labels outside [0, K) are skipped by every pass.
@@ -22,12 +28,14 @@
 
 namespace km {
 
-constexpr int kSortThreads = 256;
+constexpr int kSortThreads = 512;
 
+// Labels per block: at least 4096 and K, doubled until the whole job takes
+// about 256 blocks.
 static int64_t sort_chunk(int64_t B, int64_t N, int64_t K) {
     int64_t ch = 4096;
     while (ch < K) ch *= 2;
-    while (ch < (1 << 20) && B * ((N + ch - 1) / ch) > 2048) ch *= 2;
+    while (ch < N && B * ((N + ch - 1) / ch) > 256) ch *= 2;
     return ch;
 }
 
@@ -66,9 +74,14 @@ __global__ __launch_bounds__(kSortThreads) void k_count(const int32_t* __restric
     }
 }
 
-// One block per batch: exclusive scan of K counts.
+// One block per batch: exclusive scan of K counts -> offsets and scatter
+// cursors.  When piece_seg is given it also records, for every reduction
+// piece of TW sorted rows, the segment its first row falls in (binary search
+// over the offsets, held in LDS).
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ counts, int K,
-                                               int32_t* __restrict__ offsets, int32_t* __restrict__ cursor) {
+                                               int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
+                                               int TW, int64_t npieces, int32_t* __restrict__ piece_seg) {
+    extern __shared__ int32_t s_off[];  // [K + 1] when piece_seg != nullptr
     __shared__ int32_t s_part[1024];
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
@@ -90,9 +103,25 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
     for (int j = j0; j < j1; ++j) {
         offsets[b * (K + 1) + j] = run;
         cursor[b * K + j] = run;
+        if (piece_seg) s_off[j] = run;
         run += counts[b * K + j];
     }
-    if (tid == 1023) offsets[b * (K + 1) + K] = s_part[1023];
+    const int32_t total = s_part[1023];
+    if (tid == 1023) offsets[b * (K + 1) + K] = total;
+    if (!piece_seg) return;
+    if (tid == 1023) s_off[K] = total;
+    __syncthreads();
+    // first segment of each piece that holds rows: the last j with offsets[j] <= p * TW
+    for (int64_t p = tid; p < npieces && p * TW < total; p += 1024) {
+        const int32_t q = (int32_t)(p * TW);
+        int lo = 0, hi = K;  // invariant: s_off[lo] <= q < s_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= q) lo = mid;
+            else hi = mid;
+        }
+        piece_seg[b * npieces + p] = lo;
+    }
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_scatter(const int32_t* __restrict__ labels, int64_t N,
@@ -115,36 +144,47 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(const int32_t* __restr
     }
     __syncthreads();
     int32_t* P = perm + b * N;
-    for (int64_t i = i0 + tid; i < i1; i += kSortThreads) {
-        const int32_t l = L[i];
-        if ((uint32_t)l < (uint32_t)K) {
-            const int32_t pos = atomicAdd(&s_h[l], 1);
-            P[pos] = (int32_t)i;
-        }
+    auto place = [&](int64_t i, int32_t l) {
+        if ((uint32_t)l < (uint32_t)K) P[atomicAdd(&s_h[l], 1)] = (int32_t)i;
+    };
+    int64_t i = i0 + tid;
+    for (; i + 3 * kSortThreads < i1; i += 4 * kSortThreads) {  // 4 labels in flight
+        const int32_t l0 = L[i], l1 = L[i + kSortThreads], l2 = L[i + 2 * kSortThreads],
+                      l3 = L[i + 3 * kSortThreads];
+        place(i, l0);
+        place(i + kSortThreads, l1);
+        place(i + 2 * kSortThreads, l2);
+        place(i + 3 * kSortThreads, l3);
     }
+    for (; i < i1; i += kSortThreads) place(i, L[i]);
+}
+
+static hipError_t set_lds(const void* f, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts,
-                       int32_t* offsets, int32_t* cursor, int32_t* perm, hipStream_t s) {
+                       int32_t* offsets, int32_t* cursor, int32_t* perm, int TW, int64_t npieces,
+                       int32_t* piece_seg, hipStream_t s) {
     // counts must be zero on entry (the caller clears it with the other accumulators)
     if (B == 0) return hipSuccess;
     const size_t lds = (size_t)K * sizeof(int32_t);
     hipError_t e;
-    if (lds > 64 * 1024) {
-        if ((e = hipFuncSetAttribute((const void*)k_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-            return e;
-        if ((e = hipFuncSetAttribute((const void*)k_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-            return e;
-    }
     if (N > 0) {
+        if ((e = set_lds((const void*)k_count, lds)) != hipSuccess) return e;
         const int64_t CH = sort_chunk(B, N, K);
         dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
         hipLaunchKernelGGL(k_count, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), 0, s, counts, (int)K, offsets, cursor);
+    const size_t scan_lds = piece_seg ? (size_t)(K + 1) * sizeof(int32_t) : 0;
+    if ((e = set_lds((const void*)k_scan, scan_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), scan_lds, s, counts, (int)K, offsets, cursor, TW,
+                       npieces, piece_seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (N > 0) {
+        if ((e = set_lds((const void*)k_scatter, lds)) != hipSuccess) return e;
         const int64_t CH = sort_chunk(B, N, K);
         dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
         hipLaunchKernelGGL(k_scatter, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, cursor, perm);

@@ -32,22 +32,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16 bytes of a row -> EPL floats.
 template <typename T>
-__device__ __forceinline__ void ld_vec(const T* p, float* out) {
-    const u32x4 u = *(const u32x4*)p;
+__device__ __forceinline__ void unpack(const u32x4 u, float* out) {
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(u[e]);
+    } else if constexpr (__is_same(T, _Float16)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[e] & 0xffffu));
+            out[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[e] >> 16));
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint16_t lo = (uint16_t)(u[e] & 0xffffu), hi = (uint16_t)(u[e] >> 16);
-            if constexpr (__is_same(T, _Float16)) {
-                out[2 * e] = (float)__builtin_bit_cast(_Float16, lo);
-                out[2 * e + 1] = (float)__builtin_bit_cast(_Float16, hi);
-            } else {
-                out[2 * e] = bf16_to_f32(lo);
-                out[2 * e + 1] = bf16_to_f32(hi);
-            }
+            out[2 * e] = __uint_as_float(u[e] << 16);
+            out[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
         }
     }
 }
@@ -153,23 +152,24 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                     const int32_t rr = r + u * RPW;
                     idx[u] = rr < e ? sidx[rr - c0] : -1;
                 }
-                float v[U][EPL];
+                // raw 16-byte loads stay packed until they are accumulated,
+                // which keeps U row steps in flight at a low register cost;
+                // point rows are read once per update, so they bypass the caches
+                u32x4 raw[U];
+                float vs[U][VEC ? 1 : EPL];
                 float wi[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const bool ok = idx[u] >= 0;
                     const T* row = Xb + (int64_t)(ok ? idx[u] : 0) * d;
                     if constexpr (VEC) {
-                        if (ok && active) ld_vec<T>(row + li * EPL, v[u]);
-                        else {
-#pragma unroll
-                            for (int t = 0; t < EPL; ++t) v[u][t] = 0.f;
-                        }
+                        raw[u] = (ok && active) ? __builtin_nontemporal_load((const u32x4*)(row + li * EPL))
+                                                : u32x4{0u, 0u, 0u, 0u};
                     } else {
 #pragma unroll
                         for (int t = 0; t < EPL; ++t) {
                             const int k = li + LPR * t;
-                            v[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
+                            vs[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
                         }
                     }
                     if constexpr (WEIGHTED) wi[u] = ok ? wb[idx[u]] : 0.f;
@@ -177,10 +177,16 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
+                    float v[EPL];
+                    if constexpr (VEC) unpack<T>(raw[u], v);
+                    else {
+#pragma unroll
+                        for (int t = 0; t < EPL; ++t) v[t] = vs[u][t];
+                    }
 #pragma unroll
                     for (int t = 0; t < EPL; ++t) {
-                        if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[u][t], acc[t]);
-                        else acc[t] += v[u][t];
+                        if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[t], acc[t]);
+                        else acc[t] += v[t];
                     }
                     wacc += wi[u];
                 }
@@ -206,28 +212,13 @@ int segreduce_tw(int64_t B, int64_t N) {
     return (int)tw;
 }
 
-// Also used by the scan: first segment of every piece.
-__global__ __launch_bounds__(256) void k_piece_seg(const int32_t* __restrict__ offsets, int K, int TW,
-                                                   int64_t npieces, int32_t* __restrict__ piece_seg) {
-    const int64_t b = blockIdx.y;
-    const int32_t* offb = offsets + b * (K + 1);
-    for (int j = blockIdx.x * 256 + threadIdx.x; j < K; j += gridDim.x * 256) {
-        const int64_t lo = offb[j], hi = offb[j + 1];
-        // pieces whose first row lies in [lo, hi)
-        for (int64_t p = (lo + TW - 1) / TW; p * TW < hi && p < npieces; ++p) piece_seg[b * npieces + p] = j;
-    }
-}
-
+// piece_seg: the first segment of every piece, written by the scan of the sort.
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
-                            float* wsum, int32_t* piece_seg, hipStream_t s) {
+                            float* wsum, const int32_t* piece_seg, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
     const int TW = segreduce_tw(B, N);
     const int64_t npieces = (N + TW - 1) / TW;
-    hipLaunchKernelGGL(k_piece_seg, dim3((unsigned)((K + 255) / 256 < 1024 ? (K + 255) / 256 : 1024), (unsigned)B),
-                       dim3(256), 0, s, offsets, (int)K, TW, npieces, piece_seg);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int esz = dtype_bytes(xt);
     const int epl = 16 / esz;
     const bool vec = (d % epl == 0) && ((uintptr_t)x % 16 == 0) && (d / epl <= 64);
