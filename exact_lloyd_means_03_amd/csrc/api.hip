@@ -59,7 +59,10 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     w.offsets = take(Bz * (K + 1) * sizeof(int32_t));
     w.cursor = take(Bz * K * sizeof(int32_t));
     w.perm = take(Bz * N * sizeof(int32_t));
-    w.piece_seg = take(Bz * segreduce_pieces(B, N) * sizeof(int32_t));
+    const size_t np = (size_t)segreduce_pieces(B, N);
+    w.piece_seg = take(Bz * np * sizeof(int32_t));
+    w.slot = take(Bz * np * d * sizeof(float));
+    w.wslot = take(Bz * np * sizeof(float));
     w.total = off;
     return w;
 }
@@ -179,7 +182,8 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
     int32_t* perm = at<int32_t>(ws, W.perm);
     int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
     KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, W, ws, s));
-    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr, piece_seg, s),
+    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr, piece_seg,
+                            at<float>(ws, W.slot), at<float>(ws, W.wslot), s),
            "segreduce");
     KM_HIP(launch_divide(sums, w ? wsum : nullptr, cnt, B, K, (int)d, c_old, c_new, s), "divide");
     return KM_OK;

@@ -82,6 +82,8 @@ struct Workspace {
     size_t sums;       // [B][K][d] float: segment sums
     size_t wsum;       // [B][K] float: segment weight sums (weighted update)
     size_t piece_seg;  // [B][npieces] int32: first segment of each reduction piece
+    size_t slot;       // [B][npieces][d] float: each piece's sum over its first segment
+    size_t wslot;      // [B][npieces] float: its weight sum (weighted update)
     size_t total;
     int DP;
     int64_t Kp;
@@ -118,7 +120,8 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
 
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K,
-                            float* sums, float* wsum, const int32_t* piece_seg, hipStream_t s);
+                            float* sums, float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
+                            hipStream_t s);
 int64_t segreduce_pieces(int64_t B, int64_t N);
 int segreduce_tw(int64_t B, int64_t N);
 

@@ -8,11 +8,19 @@
 // gfx950 layout (ours): the sorted positions are cut into pieces of TW rows,
 // one piece per 64-lane wave.  A point row is read with 16-byte loads by LPR
 // lanes (d=128 bf16: 16 lanes), so one wave gathers 64/LPR rows per step and
-// keeps 4 steps of loads in flight.  At a segment boundary the wave reduces
-// its row groups with cross-lane shuffles and issues d float atomics.  The
-// first segment of every piece is precomputed by the scan, and the following
-// segment boundaries come from a 64-entry window of offsets held one per
-// lane, so a wave never searches device memory serially.
+// keeps U steps of loads in flight.  At a segment boundary the wave reduces
+// its row groups with cross-lane shuffles.  The first segment of every piece
+// is precomputed by the scan, and the following segment boundaries come from
+// a 64-entry window of offsets held one per lane, so a wave never searches
+// device memory serially.
+//
+// Where the partial sums go: a segment that starts inside a piece is flushed
+// by that piece with one atomic per coordinate, and no other piece flushes it
+// that way.  A piece's first segment (which may have begun in earlier pieces)
+// is written to the piece's own slot instead, and a second, small kernel
+// folds runs of slots into the sums.  Without that split, the pieces of a
+// very large cluster (the head of a Zipf size distribution spans thousands
+// of pieces) would all finish together and serialize on the same addresses.
 //
 // Scalar points (d == 1) with a row that fits in LDS take a whole-row kernel
 // instead: the row's (x, w) pairs are placed in cluster order in LDS and each
@@ -69,7 +77,8 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                                                    const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ piece_seg, int64_t npieces,
                                                    int K, int TW, float* __restrict__ sums,
-                                                   float* __restrict__ wsum) {
+                                                   float* __restrict__ wsum, float* __restrict__ slot,
+                                                   float* __restrict__ wslot) {
     constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 4;
     constexpr int U = 8;  // row steps in flight
     __shared__ int32_t s_idx[4][kSegChunk];
@@ -112,22 +121,38 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
 #pragma unroll
     for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
     float wacc = 0.f;
+    bool first = true;
     auto flush = [&]() {
         for (int o = LPR; o < 64; o <<= 1) {
 #pragma unroll
             for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
             if constexpr (WEIGHTED) wacc += __shfl_xor(wacc, o, 64);
         }
-        float* sj = sums + (b * K + j) * (int64_t)d;
-        if (gl == 0 && active) {
+        if (first) {  // the piece's first segment goes to its private slot
+            float* sp = slot + (b * npieces + piece) * (int64_t)d;
+            if (gl == 0 && active) {
 #pragma unroll
-            for (int t = 0; t < EPL; ++t) {
-                const int k = VEC ? li * EPL + t : li + LPR * t;
-                if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
+                for (int t = 0; t < EPL; ++t) {
+                    const int k = VEC ? li * EPL + t : li + LPR * t;
+                    if (k < d) sp[k] = acc[t];
+                }
             }
-        }
-        if constexpr (WEIGHTED) {
-            if (lane == 0) unsafeAtomicAdd(wsum + b * K + j, wacc);
+            if constexpr (WEIGHTED) {
+                if (lane == 0) wslot[b * npieces + piece] = wacc;
+            }
+            first = false;
+        } else {  // a segment that starts inside this piece: this is its only flush here
+            float* sj = sums + (b * K + j) * (int64_t)d;
+            if (gl == 0 && active) {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) {
+                    const int k = VEC ? li * EPL + t : li + LPR * t;
+                    if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
+                }
+            }
+            if constexpr (WEIGHTED) {
+                if (lane == 0) unsafeAtomicAdd(wsum + b * K + j, wacc);
+            }
         }
 #pragma unroll
         for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
@@ -204,6 +229,78 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
     if (pending) flush();
 }
 
+// Second pass: fold the per-piece slots into the segment sums.  Pieces are in
+// sorted order, so the pieces that share a first segment are consecutive;
+// each wave walks kFoldG of them and issues one atomic per coordinate per
+// segment change, so even a segment that spans thousands of pieces receives
+// only (its pieces / kFoldG) atomic flushes.
+constexpr int kFoldG = 16;
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ slot, const float* __restrict__ wslot,
+                                                    const int32_t* __restrict__ piece_seg,
+                                                    const int32_t* __restrict__ offsets, int64_t npieces, int K,
+                                                    int TW, int d, float* __restrict__ sums,
+                                                    float* __restrict__ wsum) {
+    constexpr int U = 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t b = blockIdx.y;
+    const int32_t total = offsets[b * (K + 1) + K];
+    const int64_t np = ((int64_t)total + TW - 1) / TW;  // pieces that hold rows
+    const int64_t p0 = g * kFoldG;
+    const int64_t p1 = (p0 + kFoldG < np) ? p0 + kFoldG : np;
+    if (p0 >= p1) return;
+    const int32_t* ps = piece_seg + b * npieces;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // columns lane + 64 t (d <= 256)
+    float wacc = 0.f;
+    int cur = ps[p0];
+    auto flush = [&]() {
+        float* sj = sums + (b * K + cur) * (int64_t)d;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = lane + 64 * t;
+            if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
+            acc[t] = 0.f;
+        }
+        if constexpr (WEIGHTED) {
+            if (lane == 0) unsafeAtomicAdd(wsum + b * K + cur, wacc);
+        }
+        wacc = 0.f;
+    };
+    for (int64_t pb = p0; pb < p1; pb += U) {
+        float v[U][4];
+        float wv[U];
+        int sg[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = pb + u;
+            const bool ok = p < p1;
+            sg[u] = ok ? ps[p] : -1;
+            const float* sp = slot + (b * npieces + (ok ? p : p0)) * (int64_t)d;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = lane + 64 * t;
+                v[u][t] = (ok && k < d) ? sp[k] : 0.f;
+            }
+            wv[u] = (WEIGHTED && ok) ? wslot[b * npieces + p] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (sg[u] >= 0) {
+                if (sg[u] != cur) {
+                    flush();
+                    cur = sg[u];
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[t] += v[u][t];
+                wacc += wv[u];
+            }
+        }
+    }
+    flush();
+}
+
 // Rows per wave piece: enough pieces to fill the chip, and long pieces when
 // there is plenty of work (fewer atomics on the largest clusters).
 int segreduce_tw(int64_t B, int64_t N) {
@@ -215,7 +312,7 @@ int segreduce_tw(int64_t B, int64_t N) {
 // piece_seg: the first segment of every piece, written by the scan of the sort.
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
-                            float* wsum, const int32_t* piece_seg, hipStream_t s) {
+                            float* wsum, const int32_t* piece_seg, float* slot, float* wslot, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
     const int TW = segreduce_tw(B, N);
     const int64_t npieces = (N + TW - 1) / TW;
@@ -228,7 +325,7 @@ hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, 
     dim3 grid((unsigned)((npieces + 3) / 4), (unsigned)B);
 #define KM_SEG(T, V, W)                                                                                   \
     hipLaunchKernelGGL((k_segreduce<T, V, W>), grid, dim3(256), 0, s, (const T*)x, w, N, d, shift, perm, \
-                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum)
+                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot)
 #define KM_SEG_T(T)                      \
     if (vec) {                           \
         if (w) KM_SEG(T, true, true);    \
@@ -242,6 +339,15 @@ hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, 
     else { KM_SEG_T(bf16_t) }
 #undef KM_SEG_T
 #undef KM_SEG
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 fgrid((unsigned)((npieces + 4 * kFoldG - 1) / (4 * kFoldG)), (unsigned)B);
+    if (w)
+        hipLaunchKernelGGL(k_fold_slots<true>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
+                           (int)K, TW, d, sums, wsum);
+    else
+        hipLaunchKernelGGL(k_fold_slots<false>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
+                           (int)K, TW, d, sums, wsum);
     return hipGetLastError();
 }
 

@@ -183,6 +183,25 @@ def test_update_parity(km, dtype, B, N, d, K, weighted):
     np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
 
 
+@pytest.mark.parametrize("dtype,d,weighted", [("bf16", 128, False), ("f16", 64, True), ("f32", 1, True)])
+def test_update_parity_zipf_sizes(km, dtype, d, weighted):
+    """Cluster sizes with a power-law tail: the largest segments span hundreds
+    of reduction pieces, the smallest are empty or hold one point."""
+    B, N, K = 1, 200000, 1000
+    x, C = _rand_problem(B, N, d, K, dtype, seed=d + 11)
+    rng = np.random.default_rng(d + 12)
+    pk = np.arange(1, K + 1, dtype=np.float64) ** -1.2
+    pk /= pk.sum()
+    lab = rng.permutation(K)[rng.choice(K, size=(B, N), p=pk)].astype(np.int32)
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, (B, N)).astype(np.float32)) if weighted else None
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(lab).cuda(), C.cuda(),
+                                     weights=None if w is None else w.cuda())
+    X = oracle.decode(workloads.raw_bits(x), dtype)
+    ref_c, ref_n, _, _ = oracle.update(X, None if w is None else w.numpy(), lab, C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    parity.check_centroids(c_new.cpu().numpy(), ref_c, f"zipf update {dtype} d{d} w{weighted}")
+
+
 def test_update_in_place_and_invalid_labels(km):
     x, C = _rand_problem(1, 3000, 64, 20, "f16", seed=5)
     rng = np.random.default_rng(5)
