@@ -75,42 +75,55 @@ __global__ __launch_bounds__(kSortThreads) void k_count(const int32_t* __restric
 }
 
 // One block per batch: exclusive scan of K counts -> offsets and scatter
-// cursors.  When piece_seg is given it also records, for every reduction
-// piece of TW sorted rows, the segment its first row falls in (binary search
-// over the offsets, held in LDS).
+// cursors.  The counts are staged in LDS with coalesced loads; each thread
+// scans a contiguous run of bins, and the 1024 run totals are scanned with
+// wave shuffles.  When piece_seg is given it also records, for every
+// reduction piece of TW sorted rows, the segment its first row falls in
+// (binary search over the offsets in LDS).
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ counts, int K,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
                                                int TW, int64_t npieces, int32_t* __restrict__ piece_seg) {
-    extern __shared__ int32_t s_off[];  // [K + 1] when piece_seg != nullptr
-    __shared__ int32_t s_part[1024];
-    const int tid = threadIdx.x;
+    extern __shared__ int32_t s_off[];  // [K + 1]
+    __shared__ int32_t s_wave[16];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t b = blockIdx.x;
+    for (int j = tid; j < K; j += 1024) s_off[j] = counts[b * K + j];
+    __syncthreads();
     const int per = (K + 1023) / 1024;
     const int j0 = tid * per;
     const int j1 = (j0 + per < K) ? j0 + per : K;
     int32_t s = 0;
-    for (int j = j0; j < j1; ++j) s += counts[b * K + j];
-    s_part[tid] = s;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 partial sums
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int32_t v = tid >= o ? s_part[tid - o] : 0;
-        __syncthreads();
-        s_part[tid] += v;
-        __syncthreads();
+    for (int j = j0; j < j1; ++j) s += s_off[j];
+    int32_t v = s;  // inclusive scan of the run totals within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
     }
-    int32_t run = s_part[tid] - s;  // exclusive prefix of this thread's range
+    if (lane == 63) s_wave[wid] = v;
+    __syncthreads();
+    if (wid == 0) {
+        int32_t t = lane < 16 ? s_wave[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int32_t u = __shfl_up(t, o, 64);
+            if (lane >= o) t += u;
+        }
+        if (lane < 16) s_wave[lane] = t;
+    }
+    __syncthreads();
+    int32_t run = v - s + (wid > 0 ? s_wave[wid - 1] : 0);
+    const int32_t total = s_wave[15];
     for (int j = j0; j < j1; ++j) {
-        offsets[b * (K + 1) + j] = run;
-        cursor[b * K + j] = run;
-        if (piece_seg) s_off[j] = run;
-        run += counts[b * K + j];
+        const int32_t c = s_off[j];
+        s_off[j] = run;
+        run += c;
     }
-    const int32_t total = s_part[1023];
-    if (tid == 1023) offsets[b * (K + 1) + K] = total;
-    if (!piece_seg) return;
-    if (tid == 1023) s_off[K] = total;
+    if (tid == 0) s_off[K] = total;
     __syncthreads();
+    for (int j = tid; j <= K; j += 1024) offsets[b * (K + 1) + j] = s_off[j];
+    for (int j = tid; j < K; j += 1024) cursor[b * K + j] = s_off[j];
+    if (!piece_seg) return;
     // first segment of each piece that holds rows: the last j with offsets[j] <= p * TW
     for (int64_t p = tid; p < npieces && p * TW < total; p += 1024) {
         const int32_t q = (int32_t)(p * TW);
@@ -178,7 +191,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, i
         hipLaunchKernelGGL(k_count, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const size_t scan_lds = piece_seg ? (size_t)(K + 1) * sizeof(int32_t) : 0;
+    const size_t scan_lds = (size_t)(K + 1) * sizeof(int32_t);
     if ((e = set_lds((const void*)k_scan, scan_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), scan_lds, s, counts, (int)K, offsets, cursor, TW,
                        npieces, piece_seg);
