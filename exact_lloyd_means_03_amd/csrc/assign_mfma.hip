@@ -11,11 +11,11 @@
 //   * one 64-lane wave owns NCB column blocks of 32 points; their coordinates
 //     stay in VGPRs for the whole kernel as the B operand of
 //     v_mfma_f32_32x32x16_{f16,bf16} (v_mfma_f32_32x32x2_f32 for float32);
-//   * centroid tiles of 64 or 128 rows (with their -|c|^2/2 values appended) move
-//     from device memory to LDS by direct DMA (global_load_lds_dwordx4), up to
-//     three buffers deep, and are shared by the 4 waves of the block; rows are
-//     XOR-swizzled in 16-byte chunks so the 32 A-operand rows read by one
-//     instruction fall in distinct banks;
+//   * centroid tiles of up to 256 rows (64 KB, followed by their -|c|^2/2
+//     values) move from device memory to LDS by direct DMA
+//     (global_load_lds_dwordx4), double-buffered, and are shared by the 8 (or
+//     4) waves of the block; rows are XOR-swizzled in 16-byte chunks so the
+//     32 A-operand rows read by one instruction fall in distinct banks;
 //   * software pipeline over 32-row blocks: the MFMAs of block s are issued
 //     next to the epilogue of block s-1, so the matrix core and the vector
 //     ALU work at the same time;
@@ -121,26 +121,23 @@ __device__ __forceinline__ typename Mf<T>::frag load_point_frag(const T* row, in
 
 template <typename T, int DP>
 struct AssignCfg {
-#ifdef KM_NCB
-    static constexpr int NCB = (DP * (int)sizeof(T) <= 256) ? KM_NCB : ((DP * (int)sizeof(T) <= 512) ? 2 : 1);
-#else
     static constexpr int NCB = (DP * (int)sizeof(T) <= 512) ? 2 : 1;   // 32-point blocks per wave
-#endif
     static constexpr int WAVES = assign_waves(DP, sizeof(T));
     static constexpr int PTS = WAVES * NCB * 32;                         // points per block
     static constexpr int TK = tile_rows(DP, sizeof(T));                   // centroid rows per tile
     static_assert(TK % 64 == 0, "tiles hold an even number of 32-row blocks");
+    static constexpr int NRB = TK / 32;                                  // 32-row blocks per tile
     static constexpr int RB = DP * (int)sizeof(T);                       // bytes per centroid row
     static constexpr int CPR = RB / 16;                                   // 16-byte chunks per row
     static constexpr int SW = CPR < 32 ? CPR : 32;                        // XOR swizzle period (rows)
-    static constexpr int TILE = tile_bytes(DP, sizeof(T));                // rows + the -|c|^2/2 segment
-    static constexpr int NI = TILE / 1024;                                // 1 KB DMA instructions per tile
-    static constexpr int NIW = NI / WAVES;                                // ... per wave
-#ifndef KM_NBUF
-#define KM_NBUF 2
-#endif
-    static constexpr int NBUF = KM_NBUF * TILE <= 150 * 1024 ? KM_NBUF : 2;  // LDS tile buffers
+    static constexpr int TILE = tile_bytes(DP, sizeof(T));                // rows + the -|c|^2/2 floats
+    static constexpr int NR = TK * RB / 1024;                             // 1 KB DMA instructions of rows
+    static constexpr int HN_LANES = TK * 4 / 16;                          // lanes of the -|c|^2/2 instruction
+    static constexpr int NI = NR + 1;                                     // DMA instructions per tile
+    static constexpr int NIW = (NI + WAVES - 1) / WAVES;                  // ... at most per wave
     static constexpr int KSTEPS = DP / Mf<T>::KS;
+    static_assert(TK * RB % 1024 == 0 && HN_LANES <= 64, "tile rows split into whole 1 KB DMA instructions");
+    static_assert(2 * TILE <= 150 * 1024, "two tile buffers fit in LDS");
 };
 
 constexpr uint32_t vmcnt_imm(int n) {  // s_waitcnt with only vmcnt <= n
@@ -177,13 +174,19 @@ __device__ __forceinline__ uint32_t dma_src(int i, int lane) {
 }
 
 // Copy one tile (global bytes tile_g) into LDS buffer dst: wave w issues the
-// 1 KB instructions i = n * WAVES + w, with precomputed source offsets.
+// instructions i = n * WAVES + w < NI with precomputed source offsets; the
+// last instruction (i = NR) carries the -|c|^2/2 floats on its first
+// HN_LANES lanes only.  Waves may issue different numbers of instructions;
+// each waits for all of its own before the barrier that publishes the tile.
 template <typename T, int DP>
-__device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave, const uint32_t* voff) {
+__device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave, int lane, const uint32_t* voff) {
     typedef AssignCfg<T, DP> Cfg;
-    static_assert(Cfg::NI % Cfg::WAVES == 0, "tile must split evenly over the waves");
 #pragma unroll
-    for (int n = 0; n < Cfg::NIW; ++n) dma16(tile_g, voff[n], dst + (n * Cfg::WAVES + wave) * 1024);
+    for (int n = 0; n < Cfg::NIW; ++n) {
+        const int i = n * Cfg::WAVES + wave;
+        if (i < Cfg::NR) dma16(tile_g, voff[n], dst + i * 1024);
+        else if (i == Cfg::NR && lane < Cfg::HN_LANES) dma16(tile_g, voff[n], dst + i * 1024);
+    }
 }
 
 template <typename T, int DP, bool VEC>
@@ -194,9 +197,9 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
     typedef AssignCfg<T, DP> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
-    constexpr int NCB = Cfg::NCB, TK = Cfg::TK, RB = Cfg::RB, KSTEPS = Cfg::KSTEPS, NBUF = Cfg::NBUF;
+    constexpr int NCB = Cfg::NCB, TK = Cfg::TK, RB = Cfg::RB, KSTEPS = Cfg::KSTEPS, NRB = Cfg::NRB;
 
-    __shared__ __attribute__((aligned(1024))) char s_tile[NBUF][Cfg::TILE];
+    __shared__ __attribute__((aligned(1024))) char s_tile[2][Cfg::TILE];
     __shared__ double s_obj[Cfg::WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -209,10 +212,8 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
     uint32_t voff[Cfg::NIW];
 #pragma unroll
     for (int n = 0; n < Cfg::NIW; ++n) voff[n] = dma_src<T, DP>(n * Cfg::WAVES + wave, lane);
-    // start the first tiles' DMA before the point loads
-#pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t)
-        if (t < ntiles) dma_tile<T, DP>(Bb + (int64_t)t * Cfg::TILE, s_tile[t], wave, voff);
+    // start the first tile's DMA before the point loads
+    dma_tile<T, DP>(Bb, s_tile[0], wave, lane, voff);
 
     // ---- points of this wave: B operand fragments + squared norms -------
     F bx[NCB][KSTEPS];
@@ -295,13 +296,14 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
         }
     };
 
-    // One 32-row block: the first MFMA of each column block takes -|c|^2/2 of
-    // the lane's 16 rows as its C operand (one LDS read shared by the column
-    // blocks); A operands are loaded two k-steps ahead.  After the MFMAs of
-    // each k-step comes one piece of the previous block's epilogue, and a
-    // scheduling fence keeps that order, so the matrix core and the vector
-    // ALU are busy at the same time.
-    auto mma_block = [&](const char* tile, int rb, f32x16* acc, const f32x16* prev, int32_t pblk) {
+    // LDS operand reads: the A fragment of k-step ks of 32-row block rb, and
+    // the -|c|^2/2 values of the lane's 16 rows of block rb.
+    auto lda_at = [&](const char* tile, int rb, int ks) -> F {
+        const char* arow = tile + rb * 32 * RB;
+        if constexpr (sizeof(T) == 4) return *(const float*)(arow + aoff[ks]);
+        else return __builtin_bit_cast(F, *(const u32x4*)(arow + aoff[ks]));
+    };
+    auto ldh_at = [&](const char* tile, int rb) -> f32x16 {
         const float* hn = (const float*)(tile + TK * RB);
         f32x16 h;
 #pragma unroll
@@ -312,19 +314,28 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
             h[4 * g + 2] = v[2];
             h[4 * g + 3] = v[3];
         }
-        const char* arow = tile + rb * 32 * RB;
-        auto lda = [&](int ks) -> F {
-            if constexpr (sizeof(T) == 4) return *(const float*)(arow + aoff[ks]);
-            else return __builtin_bit_cast(F, *(const u32x4*)(arow + aoff[ks]));
-        };
-        F a0 = lda(0);
-        F a1 = KSTEPS > 1 ? lda(1) : a0;
+        return h;
+    };
+
+    // One 32-row block.  On entry a0, a1 hold the A fragments of its first two
+    // k-steps and h the -|c|^2/2 values of its rows, which the first MFMA of
+    // each column block takes as its C operand.  The A stream runs two
+    // k-steps ahead across block boundaries within the tile and the next
+    // block's h is read early, so LDS latency is exposed only at the start of
+    // a tile.  After the MFMAs of each k-step comes one piece of the previous
+    // block's epilogue, and a scheduling fence keeps that order, so the
+    // matrix core and the vector ALU are busy at the same time.
+    auto mma_block = [&](const char* tile, int rb, f32x16* acc, const f32x16* prev, int32_t pblk, F& a0, F& a1,
+                         f32x16& h) {
+        f32x16 hnext;
         constexpr int PER = (KSTEPS + 7) / 8;  // k-steps per epilogue piece
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             const F a = a0;
             a0 = a1;
-            if (ks + 2 < KSTEPS) a1 = lda(ks + 2);
+            const int g = rb * KSTEPS + ks + 2;  // the fragment two k-steps ahead
+            if (g < NRB * KSTEPS) a1 = lda_at(tile, g / KSTEPS, g % KSTEPS);
+            if (ks == (KSTEPS > 1 ? 1 : 0) && rb + 1 < NRB) hnext = ldh_at(tile, rb + 1);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) acc[cb] = M::mma(a, bx[cb][ks], ks == 0 ? h : acc[cb]);
             if (ks % PER == PER - 1 || ks == KSTEPS - 1) {
@@ -339,21 +350,21 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (rb + 1 < NRB) h = hnext;
     };
     auto epilogue = [&](const f32x16* v, int32_t blk) {
 #pragma unroll
         for (int pc = 0; pc < 8; ++pc) epi_piece(pc, v, blk);
     };
 
-    // wait for tile 0 (tile 1 may still be in flight), then make it visible
-    if (NBUF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(Cfg::NIW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // wait for tile 0, then make it visible
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
     // Software pipeline over 32-row blocks (acc0 / acc1 alternate).  The loop
-    // body is one basic block: every iteration issues the DMA of tile
-    // t + NBUF - 1 (past the end it re-reads the last tile into the buffer no
-    // one reads), so the vmcnt bookkeeping is the same on every iteration.
+    // body is one basic block: every iteration issues the DMA of tile t + 1
+    // (past the end it re-reads the last tile into the buffer no one reads),
+    // so the vmcnt bookkeeping is the same on every iteration.
     f32x16 acc0[NCB], acc1[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -361,19 +372,21 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
         for (int r = 0; r < 16; ++r) acc1[cb][r] = -INFINITY;
     int32_t blk1 = 0;
     for (int64_t t = 0; t < ntiles; ++t) {
-        const char* tile = s_tile[t % NBUF];
-        const int64_t tn = (t + NBUF - 1 < ntiles) ? t + NBUF - 1 : ntiles - 1;
-        dma_tile<T, DP>(Bb + tn * (int64_t)Cfg::TILE, s_tile[(t + NBUF - 1) % NBUF], wave, voff);
+        const char* tile = s_tile[t & 1];
+        F a0 = lda_at(tile, 0, 0);
+        F a1 = KSTEPS > 1 ? lda_at(tile, 0, 1) : lda_at(tile, 1, 0);
+        f32x16 h = ldh_at(tile, 0);
+        const int64_t tn = (t + 1 < ntiles) ? t + 1 : ntiles - 1;
+        dma_tile<T, DP>(Bb + tn * (int64_t)Cfg::TILE, s_tile[(t + 1) & 1], wave, lane, voff);
 #pragma unroll
-        for (int rb = 0; rb < TK / 32; rb += 2) {
-            const int32_t blk0 = (int32_t)(t * (TK / 32)) + rb;
-            mma_block(tile, rb, acc0, acc1, blk1);
-            mma_block(tile, rb + 1, acc1, acc0, blk0);
+        for (int rb = 0; rb < NRB; rb += 2) {
+            const int32_t blk0 = (int32_t)(t * NRB) + rb;
+            mma_block(tile, rb, acc0, acc1, blk1, a0, a1, h);
+            mma_block(tile, rb + 1, acc1, acc0, blk0, a0, a1, h);
             blk1 = blk0 + 1;
         }
         // tile t+1 must have landed before the barrier that publishes it
-        if (NBUF > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * Cfg::NIW));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
     }
     // no DMA may still be writing this block's LDS when it exits

@@ -30,27 +30,19 @@ inline int padded_dim(int64_t d) {
 }
 
 // Centroid tiles of the matrix-core assignment: tile_rows() rows in the point
-// dtype, followed by a 1 KB segment holding -|c|^2/2 of those rows (first
-// tile_rows() floats), padded so that every wave of an assignment block
-// copies an equal number of 1 KB pieces.  Large rows get 64-row tiles so two tile
-// buffers fit in LDS.
-#ifndef KM_TILE_ROWS
-#define KM_TILE_ROWS 128
-#endif
-constexpr int kTileRowsMax = 128;
+// dtype (the largest of 256, 128, 64 rows that fits in 64 KB), followed by
+// -|c|^2/2 of those rows as float32.  Two tiles are double-buffered in LDS.
+constexpr int kTileBytesMax = 64 * 1024;
+constexpr int kTileRowsMax = 256;
 constexpr int tile_rows(int DP, int elem_bytes) {
-    return (KM_TILE_ROWS * DP * elem_bytes <= 32 * 1024) ? KM_TILE_ROWS : 64;
+    return 256 * DP * elem_bytes <= kTileBytesMax ? 256 : (128 * DP * elem_bytes <= kTileBytesMax ? 128 : 64);
 }
-#ifndef KM_WAVES
-#define KM_WAVES 8
-#endif
 // Waves per assignment block: rows of up to 256 bytes keep their points in
 // few enough registers for 8 waves (two per SIMD); larger rows use 4 waves so
 // each wave may use the whole register file.
-constexpr int assign_waves(int DP, int elem_bytes) { return DP * elem_bytes <= 256 ? KM_WAVES : 4; }
+constexpr int assign_waves(int DP, int elem_bytes) { return DP * elem_bytes <= 256 ? 8 : 4; }
 constexpr int tile_bytes(int DP, int elem_bytes) {
-    return (tile_rows(DP, elem_bytes) * DP * elem_bytes + 1024 + assign_waves(DP, elem_bytes) * 1024 - 1) /
-           (assign_waves(DP, elem_bytes) * 1024) * (assign_waves(DP, elem_bytes) * 1024);
+    return tile_rows(DP, elem_bytes) * (DP * elem_bytes + 4);
 }
 
 // Rows of the padded centroid matrix: K rounded up to the largest tile.
