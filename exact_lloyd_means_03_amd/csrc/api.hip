@@ -260,6 +260,13 @@ km_status kmeans_fit(const void* x, km_dtype xt, const float* weights, int64_t B
     const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
     KM_TRY(check_ws(W, workspace, workspace_bytes));
     hipStream_t s = (hipStream_t)stream;
+    if (d == 1 && n_iter > 0 && fit_1d_rows_fits(N, K)) {
+        // scalar rows that fit on chip: every iteration in one launch
+        KM_HIP(launch_fit_1d_rows((DType)xt, x, weights, B, N, init, K, n_iter, centroids, labels, counts,
+                                  objective, s),
+               "fit_1d_rows");
+        return KM_OK;
+    }
     if (init != centroids && B > 0)
         KM_HIP(hipMemcpyAsync(centroids, init, (size_t)B * K * d * sizeof(float), hipMemcpyDeviceToDevice, s),
                "copy init");

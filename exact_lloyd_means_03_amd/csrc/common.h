@@ -122,6 +122,11 @@ hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* co
                          hipStream_t s);
 
 // Scalar points: whole-row on-chip update (sort-inverse in LDS).
+// Whole fits of scalar rows kept on chip (one block per row, all iterations).
+bool fit_1d_rows_fits(int64_t N, int64_t K);
+hipError_t launch_fit_1d_rows(DType xt, const void* x, const float* w, int64_t B, int64_t N, const float* init,
+                              int64_t K, int n_iter, float* centroids, int32_t* labels, int32_t* counts,
+                              double* objective, hipStream_t s);
 bool update_1d_row_fits(int64_t N, int64_t K);
 hipError_t launch_update_1d_row(DType xt, const void* x, const float* w, int64_t B, int64_t N,
                                 const int32_t* labels, int64_t K, const float* c_old,
