@@ -25,6 +25,13 @@ sys.path.insert(0, ROOT)
 METRIC = "Lloyd iter/s at N=1M K=8192 d=128 fp16; assign TFLOP/s, update GB/s"
 PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense MI355X matrix-core peaks
 PEAK_HBM_GBS = 8000.0
+# One float32 vector operation per lane per clock, unpacked: 256 CUs x 4 SIMDs
+# x 16 lanes x 2.4 GHz (the library is built without packed fp32).
+PEAK_VALU_GOPS = 256 * 4 * 16 * 2.4
+# Algorithmic float32 operations per point per scalar Lloyd iteration: the two
+# bracketing distances (2 sub, 2 mul) and their comparison, the weighted sum
+# and weight sum (fma, add), and the objective term (fma).
+OPS_1D_PER_POINT = 8
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_traffic.json")
 ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_03_amd", "csrc", "assign_mfma.hip")
@@ -62,46 +69,112 @@ def _traffic(wl):
 
 
 def cpu_baseline(p, target_s: float):
-    """Time the CPU oracle on a bounded sample: n_s points against all K
-    centroids (assignment) and their update, extrapolated linearly in N."""
+    """Time the CPU oracle on a bounded sample and extrapolate to one Lloyd
+    iteration over the whole workload: with one batch, n points against all
+    K centroids (assignment) plus their update, scaled linearly in N; with
+    several batches, whole batches (all their points), scaled linearly in B."""
     import numpy as np
 
     import oracle
     import workloads
 
     wl = p.wl
-    X_bits = workloads.raw_bits(p.x[0])
-    C = p.init[0:1].numpy()
-    Chat = oracle.decode(oracle.round_to(C, wl.dtype), wl.dtype)
+    bits = workloads.raw_bits(p.x)
+    C = p.init.numpy()
     rng = np.random.default_rng(12345)
 
-    def run(n):
+    def run_points(n):
         idx = np.sort(rng.choice(wl.N, size=n, replace=False))
-        X = oracle.decode(X_bits[idx][None], wl.dtype)
+        X = oracle.decode(bits[0:1, idx], wl.dtype)
+        Chat = oracle.decode(oracle.round_to(C[0:1], wl.dtype), wl.dtype)
         w = None if p.w is None else p.w[0:1, idx].numpy()
         t0 = time.perf_counter()
         lab, d1, d2 = oracle.assign(X, Chat)
-        oracle.update(X, w, lab, C)
+        oracle.update(X, w, lab, C[0:1])
         return time.perf_counter() - t0
 
-    n = min(wl.N, 256)
+    def run_batches(nb):
+        rows = np.sort(rng.choice(wl.B, size=nb, replace=False))
+        X = oracle.decode(bits[rows], wl.dtype)
+        Chat = oracle.decode(oracle.round_to(C[rows], wl.dtype), wl.dtype)
+        w = None if p.w is None else p.w[rows].numpy()
+        t0 = time.perf_counter()
+        lab, d1, d2 = oracle.assign(X, Chat)
+        oracle.update(X, w, lab, C[rows])
+        return time.perf_counter() - t0
+
+    if wl.B == 1:
+        total, run = wl.N, run_points
+    else:
+        total, run = wl.B, run_batches
+    n = min(total, 1 if wl.B > 1 else 256)
     t = run(n)
-    while t < 0.5 and n < wl.N:
-        n = min(wl.N, n * 4)
+    while t < 0.5 and n < total:
+        n = min(total, n * 4)
         t = run(n)
-    if n < wl.N:
-        n = int(min(wl.N, max(n, n * target_s / max(t, 1e-9))))
+    if n < total:
+        n = int(min(total, max(n, n * target_s / max(t, 1e-9))))
         t = run(n)
-    per_iter = t * (wl.N / n) * wl.B
+    per_iter = t * (total / n)
+    what = (f"{n} of {wl.N} points" if wl.B == 1 else f"{n} of {wl.B} batches ({wl.N} points each)")
     return {
         "value": 1.0 / per_iter,
         "unit": "iter/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"{n} of {wl.N} points of batch 0 (of {wl.B}): one oracle assignment against all "
-                   f"K={wl.K} centroids plus the update of those points, {t:.2f} s, extrapolated "
-                   f"linearly to all {wl.B * wl.N} points"),
+        "sample": (f"{what}: one oracle assignment against all K={wl.K} centroids plus the update, "
+                   f"{t:.2f} s, extrapolated linearly to one iteration over all {wl.B * wl.N} points"),
     }
+
+
+def bench_fit_1d(args, km, wl, p, x, w, C):
+    """Scalar rows: kmeans_fit runs every iteration of rows of up to 8192
+    points with K <= 16 in one launch, so a step is one iteration inside
+    that launch.  The warmup is a
+    fit of W iterations; the timed region is one fit of exactly K iterations
+    from the same initial centroids (HIP events on the launch stream, plus
+    the wall clock between synchronizations)."""
+    import torch
+
+    B, N, d, K = wl.B, wl.N, wl.d, wl.K
+    init = C.clone()
+    if args.warmup > 0:
+        km.kmeans_fit(x, init, args.warmup, weights=w)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    km.kmeans_fit(x, init, args.steps, weights=w)
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fit_ms = e0.elapsed_time(e1)
+    ops = OPS_1D_PER_POINT * B * N * args.steps
+    achieved = ops / (fit_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": args.steps / elapsed,
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "N": N, "d": d, "K": K, "point_dtype": wl.dtype,
+                   "weighted": wl.weighted, "init": wl.init, "path": "whole fit in one launch"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_GOPS, "unit": "Gop/s",
+                     "frac": achieved / PEAK_VALU_GOPS, "traffic": None,
+                     "kernel": "k_fit_1d_rows" if N <= 8192 and K <= 16 else "kmeans_fit",
+                     "algorithmic_per_launch": ops, "avg_launch_ms": fit_ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -148,6 +221,9 @@ def main():
     labels = torch.empty((B, N), dtype=torch.int32, device=dev)
     counts = torch.empty((B, K), dtype=torch.int32, device=dev)
     obj = torch.empty((max(args.steps, args.warmup, 1), B), dtype=torch.float64, device=dev)
+
+    if d == 1:
+        return bench_fit_1d(args, km, wl, p, x, w, C)
 
     def step(k):
         km.kmeans_assign(x, C, weights=w, labels=labels, objective=obj[k], ws=ws)
