@@ -73,7 +73,8 @@ using namespace km;
 
 namespace {
 
-constexpr int64_t kMaxD = 256;
+constexpr int64_t kMaxD = 512;     // 16-bit points
+constexpr int64_t kMaxDF32 = 256;  // float32 points
 constexpr int64_t kMaxK = 32768;
 constexpr int64_t kMaxB = 65535;
 constexpr int64_t kMaxN = 0x7fffffff;
@@ -83,6 +84,9 @@ km_status check_shape(int64_t B, int64_t N, int64_t d, int64_t K, int xt) {
     if (d < 1 || K < 1) return fail(KM_EINVAL, "d and K must be >= 1 (d=%lld K=%lld)", (long long)d, (long long)K);
     if (xt != KM_F32 && xt != KM_F16 && xt != KM_BF16) return fail(KM_EUNSUPPORTED, "unknown dtype %d", xt);
     if (d > kMaxD) return fail(KM_EUNSUPPORTED, "d=%lld > %lld is not supported", (long long)d, (long long)kMaxD);
+    if (xt == KM_F32 && d > kMaxDF32)
+        return fail(KM_EUNSUPPORTED, "d=%lld > %lld is not supported for float32 points", (long long)d,
+                    (long long)kMaxDF32);
     if (K > kMaxK) return fail(KM_EUNSUPPORTED, "K=%lld > %lld is not supported", (long long)K, (long long)kMaxK);
     if (B > kMaxB) return fail(KM_EUNSUPPORTED, "B=%lld > %lld is not supported", (long long)B, (long long)kMaxB);
     if (N > kMaxN) return fail(KM_EUNSUPPORTED, "N=%lld >= 2^31 is not supported", (long long)N);

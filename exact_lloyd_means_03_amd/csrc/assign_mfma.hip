@@ -437,7 +437,11 @@ static int64_t blocks_for(int64_t N, int DP) {
         case 32: pts = AssignCfg<T, 32>::PTS; break;
         case 64: pts = AssignCfg<T, 64>::PTS; break;
         case 128: pts = AssignCfg<T, 128>::PTS; break;
-        default: pts = AssignCfg<T, 256>::PTS; break;
+        case 256: pts = AssignCfg<T, 256>::PTS; break;
+        default:
+            if constexpr (sizeof(T) == 2) pts = AssignCfg<T, 512>::PTS;
+            else pts = AssignCfg<T, 256>::PTS;  // float32 rows stop at 256 (checked by the caller)
+            break;
     }
     return (N + pts - 1) / pts;
 }
@@ -473,6 +477,11 @@ static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, 
         case 64: return launch_t<T, 64>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         case 128: return launch_t<T, 128>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         case 256: return launch_t<T, 256>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 512:
+            if constexpr (sizeof(T) == 2)
+                return launch_t<T, 512>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+            else
+                return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

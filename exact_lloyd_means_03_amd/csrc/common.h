@@ -26,7 +26,8 @@ inline int padded_dim(int64_t d) {
     if (d <= 32) return 32;
     if (d <= 64) return 64;
     if (d <= 128) return 128;
-    return 256;
+    if (d <= 256) return 256;
+    return 512;
 }
 
 // Centroid tiles of the matrix-core assignment: tile_rows() rows in the point

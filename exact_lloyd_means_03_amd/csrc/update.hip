@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                                                    int K, int TW, float* __restrict__ sums,
                                                    float* __restrict__ wsum, float* __restrict__ slot,
                                                    float* __restrict__ wslot) {
-    constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 4;
+    constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 8;  // non-vector rows: 64 lanes x 8 = 512 elements
     constexpr int U = 8;  // row steps in flight
     __shared__ int32_t s_idx[4][kSegChunk];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -252,13 +252,13 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
     const int64_t p1 = (p0 + kFoldG < np) ? p0 + kFoldG : np;
     if (p0 >= p1) return;
     const int32_t* ps = piece_seg + b * npieces;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // columns lane + 64 t (d <= 256)
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // columns lane + 64 t (d <= 512)
     float wacc = 0.f;
     int cur = ps[p0];
     auto flush = [&]() {
         float* sj = sums + (b * K + cur) * (int64_t)d;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 8; ++t) {
             const int k = lane + 64 * t;
             if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
             acc[t] = 0.f;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
         wacc = 0.f;
     };
     for (int64_t pb = p0; pb < p1; pb += U) {
-        float v[U][4];
+        float v[U][8];
         float wv[U];
         int sg[U];
 #pragma unroll
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
             sg[u] = ok ? ps[p] : -1;
             const float* sp = slot + (b * npieces + (ok ? p : p0)) * (int64_t)d;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < 8; ++t) {
                 const int k = lane + 64 * t;
                 v[u][t] = (ok && k < d) ? sp[k] : 0.f;
             }
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
                     cur = sg[u];
                 }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[t] += v[u][t];
+                for (int t = 0; t < 8; ++t) acc[t] += v[u][t];
                 wacc += wv[u];
             }
         }

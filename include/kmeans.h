@@ -38,9 +38,10 @@
  *     checked on the host before anything is enqueued; on an error nothing is
  *     enqueued and the status says why (kmeans_last_error() has the detail).
  *     Faults inside kernels surface at the caller's next synchronization.
- *   - Supported shapes: d == 1 (scalar path), or 2 <= d <= 256 (matrix-core
- *     path; d is zero-padded internally to 16, 32, 64, 128 or 256, which does
- *     not change any distance).  1 <= K <= 32768 (K <= 16384 when d == 1).
+ *   - Supported shapes: d == 1 (scalar path), or 2 <= d <= 512 for 16-bit
+ *     points and 2 <= d <= 256 for float32 points (matrix-core path; d is
+ *     zero-padded internally to 16, 32, 64, 128, 256 or 512, which does not
+ *     change any distance).  1 <= K <= 32768 (K <= 16384 when d == 1).
  *     N < 2^31, B <= 65535; B and N may be 0.
  *   - Centroids are float32 state.  Distances use the centroids rounded
  *     (IEEE round-to-nearest-even) to the point dtype, because that is the

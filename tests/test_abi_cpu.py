@@ -42,7 +42,9 @@ def test_workspace_bytes(lib):
     assert n >= (1 << 20) * 8 + 8192 * 128 * 4 + 8192 * 128 * 2
     assert n % 256 == 0
     assert lib.kmeans_workspace_bytes(1, 100, 0, 4, 1) == 0       # d < 1
-    assert lib.kmeans_workspace_bytes(1, 100, 300, 4, 1) == 0     # d > 256
+    assert lib.kmeans_workspace_bytes(1, 100, 513, 4, 1) == 0     # d > 512
+    assert lib.kmeans_workspace_bytes(1, 100, 300, 4, 0) == 0     # float32 rows above 256
+    assert lib.kmeans_workspace_bytes(1, 100, 512, 4, 2) > 0
     assert lib.kmeans_workspace_bytes(1, 100, 8, 40000, 1) == 0   # K > 32768
     assert lib.kmeans_workspace_bytes(-1, 100, 8, 4, 1) == 0
     assert lib.kmeans_workspace_bytes(1, 100, 8, 4, 7) == 0       # dtype
@@ -56,8 +58,9 @@ FAKE = C.c_void_p(0x1000)  # never dereferenced: every case fails before any HIP
     (dict(x=None), 1),
     # K = 0
     (dict(K=0), 1),
-    # d = 300
-    (dict(d=300), 2),
+    # d above the limits: 512 for 16-bit points, 256 for float32 points
+    (dict(d=513), 2),
+    (dict(d=300, xt=0), 2),
     # unsupported dtype
     (dict(xt=5), 2),
     # workspace too small

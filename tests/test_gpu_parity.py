@@ -202,6 +202,34 @@ def test_update_parity_zipf_sizes(km, dtype, d, weighted):
     parity.check_centroids(c_new.cpu().numpy(), ref_c, f"zipf update {dtype} d{d} w{weighted}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N,d,K", [(700, 300, 90), (530, 512, 300), (400, 257, 33)])
+def test_wide_rows_parity(km, dtype, N, d, K):
+    """Rows wider than 256 elements (16-bit points only): assignment, update
+    and a short fit."""
+    x, C = _rand_problem(1, N, d, K, dtype, seed=N + d + K)
+    gl = _assign_case(km, x, C, what=f"wide assign {dtype} d{d}")
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(gl).cuda(), C.cuda())
+    X = oracle.decode(workloads.raw_bits(x), dtype)
+    ref_c, ref_n, _, _ = oracle.update(X, None, gl, C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    parity.check_centroids(c_new.cpu().numpy(), ref_c, f"wide update {dtype} d{d}")
+    g = torch.Generator().manual_seed(d)
+    init = x[:, torch.randperm(N, generator=g)[:K]].float().contiguous()
+    cen, lab, cnt, J = km.kmeans_fit(x.cuda(), init.cuda(), 3)
+    torch.cuda.synchronize()
+    ref = oracle.fit(workloads.raw_bits(x), dtype, None, init.numpy(), 3)
+    parity.check_objective(J.cpu().numpy(), ref["J"], f"wide fit {dtype} d{d}")
+    parity.check_labels(lab.cpu().numpy(), ref["labels"], ref["d1"], ref["d2"], f"wide fit {dtype} d{d}")
+    parity.check_centroids(cen.cpu().numpy(), ref["centroids"], f"wide fit {dtype} d{d}")
+
+
+def test_float32_rows_above_256_are_rejected(km):
+    x, C = _rand_problem(1, 100, 300, 10, "f32", seed=1)
+    with pytest.raises(Exception):
+        km.kmeans_assign(x.cuda(), C.cuda())
+
+
 def test_update_in_place_and_invalid_labels(km):
     x, C = _rand_problem(1, 3000, 64, 20, "f16", seed=5)
     rng = np.random.default_rng(5)
