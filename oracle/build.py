@@ -11,15 +11,20 @@ SRC = os.path.join(HERE, "lloyd_oracle.c")
 LIB = os.path.join(HERE, "liblloyd_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+def compile_source(src: str, out: str, verbose: bool = False) -> str:
+    """Compile an oracle C source into the shared library `out`."""
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
-           "-shared", "-fPIC", SRC, "-o", tmp, "-lm"]
+           "-shared", "-fPIC", src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    return compile_source(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -10,6 +10,7 @@ fp64 exactly inside the C code.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 
@@ -22,30 +23,49 @@ DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 _lib = None
 
 
+def load_library(path: str):
+    """A ctypes handle of an oracle library built from this file's C source
+    (the tests also load deliberately broken copies to check the pins)."""
+    L = C.CDLL(path)
+    p = C.c_void_p
+    i64 = C.c_int64
+    L.oracle_decode_one.argtypes = [C.c_uint32, C.c_int]
+    L.oracle_decode_one.restype = C.c_double
+    L.oracle_round_one.argtypes = [C.c_float, C.c_int]
+    L.oracle_round_one.restype = C.c_uint32
+    L.oracle_decode.argtypes = [p, C.c_int, i64, p]
+    L.oracle_round.argtypes = [p, i64, C.c_int, p]
+    L.oracle_assign.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
+    L.oracle_update.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p]
+    L.oracle_objective.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+    L.oracle_fit.argtypes = [p, C.c_int, p, i64, i64, i64, i64, p, C.c_int32,
+                             p, p, p, p, p, p]
+    L.oracle_fit.restype = C.c_int
+    L.oracle_num_threads.restype = C.c_int
+    return L
+
+
 def lib():
     """The loaded oracle library; compiled first if it has not been built."""
     global _lib
     if _lib is None:
         if not os.path.exists(_build.LIB):
             _build.build()
-        L = C.CDLL(_build.LIB)
-        p = C.c_void_p
-        i64 = C.c_int64
-        L.oracle_decode_one.argtypes = [C.c_uint32, C.c_int]
-        L.oracle_decode_one.restype = C.c_double
-        L.oracle_round_one.argtypes = [C.c_float, C.c_int]
-        L.oracle_round_one.restype = C.c_uint32
-        L.oracle_decode.argtypes = [p, C.c_int, i64, p]
-        L.oracle_round.argtypes = [p, i64, C.c_int, p]
-        L.oracle_assign.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
-        L.oracle_update.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p]
-        L.oracle_objective.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
-        L.oracle_fit.argtypes = [p, C.c_int, p, i64, i64, i64, i64, p, C.c_int32,
-                                 p, p, p, p, p, p]
-        L.oracle_fit.restype = C.c_int
-        L.oracle_num_threads.restype = C.c_int
-        _lib = L
+        _lib = load_library(_build.LIB)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every call of this module to another build of the oracle source
+    for the duration of the block."""
+    global _lib
+    saved = lib()
+    _lib = load_library(path)
+    try:
+        yield
+    finally:
+        _lib = saved
 
 
 def _ptr(a):

@@ -346,6 +346,36 @@ def test_lloyd_invariants_on_mixture(orc):
                 np.testing.assert_allclose(rn["centroids"][b, :, k], want, rtol=1e-6, atol=1e-7)
 
 
+def test_fit_assigns_with_centroids_rounded_to_the_point_dtype(orc):
+    """The first assignment of a fit uses the initial centroids rounded to
+    the point dtype: labels and J_0 from numpy's float16 / torch's bfloat16
+    rounding and scipy's cdist, with and without weights."""
+    rng = np.random.default_rng(21)
+    B, N, d, K = 2, 600, 5, 9
+    for dt in ("f16", "bf16"):
+        x32 = rng.standard_normal((B, N, d)).astype(np.float32)
+        init = (rng.standard_normal((B, K, d)) * 0.7).astype(np.float32)
+        w = rng.uniform(0.2, 1.0, (B, N)).astype(np.float32)
+        if dt == "f16":
+            bits = x32.astype(np.float16).view(np.uint16)
+            X = x32.astype(np.float16).astype(np.float64)
+            Chat = init.astype(np.float16).astype(np.float64)
+        else:
+            tb = torch.from_numpy(x32).to(torch.bfloat16)
+            bits = tb.view(torch.int16).numpy().view(np.uint16)
+            X = tb.double().numpy()
+            Chat = torch.from_numpy(init).to(torch.bfloat16).double().numpy()
+        for weights in (None, w):
+            r = orc.fit(bits, dt, weights, init, 1)
+            for b in range(B):
+                D = cdist(X[b], Chat[b], "sqeuclidean")
+                lab = np.argmin(D, axis=1)
+                np.testing.assert_array_equal(r["labels"][b], lab)
+                ww = np.ones(N) if weights is None else weights[b].astype(np.float64)
+                J0 = (ww * D[np.arange(N), lab]).sum()
+                assert abs(r["J"][b, 0] - J0) <= 1e-12 * J0, (dt, b)
+
+
 def test_objective_of_labels(orc):
     """J of the assignment's labels equals the fit's J; J of other labels is larger."""
     rng = np.random.default_rng(11)
