@@ -1,13 +1,16 @@
-// Whole Lloyd fits of scalar rows (d == 1) that fit on chip, one block per
-// row, every iteration in one launch.
+// Whole Lloyd fits of scalar rows (d == 1) that fit on chip, every
+// iteration in one launch.
 //
 // The per-row weighted 1D clustering of LLM weight rows (github
 // LeanModels/LeanQuant issue #1 "1D k-means", the kmeans_fit diff: K = 16 or
 // 8 clusters per row of a few thousand weights, sample weights, a fixed
 // number of iterations) is far too small per row for one kernel per step:
 // every iteration would re-read the row's points and weights from device
-// memory.  Here a block keeps its row's points and weights in registers for
-// all iterations and reads device memory once.
+// memory.  Here the row's points and weights stay in registers for all
+// iterations and device memory is read once.  Rows of up to 4096 points get
+// one wave each (k_fit_1d_wave: no barriers, so the serial part of one row
+// overlaps the point work of the other rows on the CU); longer rows, up to
+// 8192 points, get one 256-thread block (k_fit_1d_rows).
 //
 // Iteration t (same result as the assignment and update kernels):
 //   1. The row's centroids, rounded to the point dtype, are ordered by
@@ -18,18 +21,18 @@
 //      bracket it, because the float32 distance (x - v)^2 is monotone in
 //      |x - v|.  Between v_a and v_{a+1}, "x prefers v_a" (smaller float32
 //      distance, or equal distance and smaller index) holds up to some float
-//      and fails from it on; that float, the threshold t_a, is found by
-//      bisection over the ordered float bit patterns in (v_a, v_{a+1}].  The
-//      rank of x is then the number of thresholds <= x (a branch-free
-//      binary search over the A-1 thresholds in LDS).
+//      and fails from it on; that float, the threshold t_a, is found by a
+//      search over the ordered float bit patterns in (v_a, v_{a+1}].  The
+//      rank of x is then the number of thresholds <= x.
 //   3. Each thread adds w*x and w of its points, in float64, into its own
-//      per-rank bins in LDS (no atomics), and w * (x - v)^2 into its
-//      objective partial.
+//      per-rank bins in LDS (adds that return nothing, on addresses no other
+//      lane touches), and w * (x - v)^2 into its objective partial.
 //   4. The bins are reduced per rank in float64; the new centroid of the
 //      smallest index of each value is S / W (float64 divide, then float32),
 //      a value with no points keeps its centroid, and so does every centroid
 //      that duplicates a smaller index's value.
-// The last iteration also writes the labels and the counts.
+// After the last iteration the labels and counts of its assignment are
+// written.
 #include "common.h"
 
 namespace km {
@@ -37,6 +40,7 @@ namespace km {
 constexpr int kFit1DThreads = 256;
 constexpr int kFit1DMaxK = 16;
 constexpr int kFit1DMaxN = 8192;
+constexpr int kFit1DWaveMaxN = 64 * 64;  // rows a single wave keeps in registers
 
 bool fit_1d_rows_fits(int64_t N, int64_t K) { return N >= 1 && N <= kFit1DMaxN && K <= kFit1DMaxK; }
 
@@ -69,6 +73,79 @@ __device__ __forceinline__ bool f1_prefers(float x, float va, int ia, float vb, 
     const float ta = x - va, tb = vb - x;
     const float da = ta * ta, db = tb * tb;
     return da < db || (da == db && ia < ib);
+}
+
+// Steps 1-2 for one row, by one wave: from the centroids in s_c, the distinct
+// rounded values in ascending order (s_val), the smallest index holding each
+// (s_idx) and the thresholds between neighbours (s_thr, +inf past A - 1).
+// Returns A, the number of distinct values (the same in every lane).
+template <typename T>
+__device__ __forceinline__ int f1_thresholds(const float* s_c, int K, int lane, float* s_val, int* s_idx,
+                                             float* s_thr) {
+    float u[kFit1DMaxK];  // every centroid, rounded (the same in all lanes)
+#pragma unroll
+    for (int k = 0; k < kFit1DMaxK; ++k) u[k] = k < K ? f1_round<T>(s_c[k]) : INFINITY;
+    const float v = lane < K ? f1_round<T>(s_c[lane]) : INFINITY;
+    bool first = lane < K;  // no smaller index holds the same value
+#pragma unroll
+    for (int k = 0; k < kFit1DMaxK; ++k)
+        if (k < lane && u[k] == v) first = false;
+    const unsigned long long firsts = __ballot(first);
+    int a = 0;  // distinct values below v
+#pragma unroll
+    for (int k = 0; k < kFit1DMaxK; ++k)
+        if (((firsts >> k) & 1ull) && u[k] < v) ++a;
+    if (first) {
+        s_val[a] = v;
+        s_idx[a] = lane;
+    }
+    const int A = __popcll(firsts);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < kFit1DMaxK) {
+        float thr = INFINITY;
+        if (lane < A - 1) {
+            const float va = s_val[lane], vb = s_val[lane + 1];
+            const int ia = s_idx[lane], ib = s_idx[lane + 1];
+            // invariant: x = unord(lo) prefers va, x = unord(hi) does not
+            uint32_t lo = f1_ord(va), hi = f1_ord(vb);
+            // the switch is within a few floats of the midpoint: probe
+            // there, gallop outwards, then bisect the bracket found
+            uint32_t probe = f1_ord(va + 0.5f * (vb - va));
+            probe = probe <= lo ? lo + 1 : (probe > hi ? hi : probe);
+            if (probe < hi) {
+                if (f1_prefers(f1_unord(probe), va, ia, vb, ib)) {
+                    lo = probe;
+                    for (uint32_t step = 1; step < hi - lo; step <<= 1) {  // lo + step < hi
+                        if (f1_prefers(f1_unord(lo + step), va, ia, vb, ib)) {
+                            lo += step;
+                        } else {
+                            hi = lo + step;
+                            break;
+                        }
+                    }
+                } else {
+                    hi = probe;
+                    for (uint32_t step = 1; step < hi - lo; step <<= 1) {  // hi - step > lo
+                        if (!f1_prefers(f1_unord(hi - step), va, ia, vb, ib)) {
+                            hi -= step;
+                        } else {
+                            lo = hi - step;
+                            break;
+                        }
+                    }
+                }
+            }
+            while (hi - lo > 1) {
+                const uint32_t mid = lo + ((hi - lo) >> 1);
+                if (f1_prefers(f1_unord(mid), va, ia, vb, ib)) lo = mid;
+                else hi = mid;
+            }
+            thr = f1_unord(hi);
+        }
+        s_thr[lane] = thr;
+    }
+    return A;
 }
 
 // PPT: points per thread (N <= PPT * kFit1DThreads).
@@ -106,69 +183,7 @@ __global__ __launch_bounds__(kFit1DThreads) void k_fit_1d_rows(
         const bool last = t == n_iter - 1;
         // ---- 1-2: distinct sorted values and thresholds (one wave) ----
         if (wave == 0) {
-            float u[kFit1DMaxK];  // every centroid, rounded (the same in all lanes)
-#pragma unroll
-            for (int k = 0; k < kFit1DMaxK; ++k) u[k] = k < K ? f1_round<T>(s_c[k]) : INFINITY;
-            const float v = lane < K ? f1_round<T>(s_c[lane]) : INFINITY;
-            bool first = lane < K;  // no smaller index holds the same value
-#pragma unroll
-            for (int k = 0; k < kFit1DMaxK; ++k)
-                if (k < lane && u[k] == v) first = false;
-            const unsigned long long firsts = __ballot(first);
-            int a = 0;  // distinct values below v
-#pragma unroll
-            for (int k = 0; k < kFit1DMaxK; ++k)
-                if (((firsts >> k) & 1ull) && u[k] < v) ++a;
-            if (first) {
-                s_val[a] = v;
-                s_idx[a] = lane;
-            }
-            const int A = __popcll(firsts);
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            if (lane < kFit1DMaxK) {
-                float thr = INFINITY;
-                if (lane < A - 1) {
-                    const float va = s_val[lane], vb = s_val[lane + 1];
-                    const int ia = s_idx[lane], ib = s_idx[lane + 1];
-                    // invariant: x = unord(lo) prefers va, x = unord(hi) does not
-                    uint32_t lo = f1_ord(va), hi = f1_ord(vb);
-                    // the switch is within a few floats of the midpoint: probe
-                    // there, gallop outwards, then bisect the bracket found
-                    uint32_t u = f1_ord(va + 0.5f * (vb - va));
-                    u = u <= lo ? lo + 1 : (u > hi ? hi : u);
-                    if (u < hi) {
-                        if (f1_prefers(f1_unord(u), va, ia, vb, ib)) {
-                            lo = u;
-                            for (uint32_t step = 1; step < hi - lo; step <<= 1) {  // lo + step < hi
-                                if (f1_prefers(f1_unord(lo + step), va, ia, vb, ib)) {
-                                    lo += step;
-                                } else {
-                                    hi = lo + step;
-                                    break;
-                                }
-                            }
-                        } else {
-                            hi = u;
-                            for (uint32_t step = 1; step < hi - lo; step <<= 1) {  // hi - step > lo
-                                if (!f1_prefers(f1_unord(hi - step), va, ia, vb, ib)) {
-                                    hi -= step;
-                                } else {
-                                    lo = hi - step;
-                                    break;
-                                }
-                            }
-                        }
-                    }
-                    while (hi - lo > 1) {
-                        const uint32_t mid = lo + ((hi - lo) >> 1);
-                        if (f1_prefers(f1_unord(mid), va, ia, vb, ib)) lo = mid;
-                        else hi = mid;
-                    }
-                    thr = f1_unord(hi);
-                }
-                s_thr[lane] = thr;
-            }
+            const int A = f1_thresholds<T>(s_c, K, lane, s_val, s_idx, s_thr);
             if (lane == 0) s_A = A;
         }
         // ---- clear this thread's bins ----
@@ -267,6 +282,121 @@ __global__ __launch_bounds__(kFit1DThreads) void k_fit_1d_rows(
     }
 }
 
+// One wave per row (rows of up to 64 * PPT points): the same iteration with
+// no block barriers, so the serial step of one row (the thresholds) overlaps
+// the point work of the other rows on the CU, and about ten rows share a CU.
+template <typename T, int PPT>
+__global__ __launch_bounds__(64) void k_fit_1d_wave(
+    const T* __restrict__ X, const float* __restrict__ w, int N, const float* __restrict__ init, int K,
+    int n_iter, float* __restrict__ centroids, int32_t* __restrict__ labels, int32_t* __restrict__ counts,
+    double* __restrict__ objective) {
+    __shared__ float s_c[kFit1DMaxK];
+    __shared__ float s_val[kFit1DMaxK];
+    __shared__ int s_idx[kFit1DMaxK];
+    __shared__ float s_thr[kFit1DMaxK];
+    __shared__ double2 s_bin[kFit1DMaxK][64 + 1];  // per-lane (sum w*x, sum w) per rank (rows padded)
+    __shared__ int s_cnt[kFit1DMaxK];
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const T* Xb = X + b * (int64_t)N;
+    auto wave_sync = [] {
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+
+    float xs[PPT], ws[PPT];
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int i = p * 64 + lane;
+        xs[p] = i < N ? f1_load<T>(Xb + i) : 0.f;
+        ws[p] = i < N ? (w ? w[b * N + i] : 1.f) : 0.f;  // past the row end: weight 0, no effect
+    }
+    if (lane < K) s_c[lane] = init[b * K + lane];
+    if (lane < kFit1DMaxK) s_cnt[lane] = 0;
+    wave_sync();
+
+    int A = 0;
+    for (int t = 0; t < n_iter; ++t) {
+        A = f1_thresholds<T>(s_c, K, lane, s_val, s_idx, s_thr);
+#pragma unroll
+        for (int r = 0; r < kFit1DMaxK; ++r) s_bin[r][lane] = make_double2(0.0, 0.0);
+        wave_sync();
+        // the thresholds are the same in every lane: held in scalar registers,
+        // a point's rank is a branch-free count of compares
+        float tr[kFit1DMaxK - 1];
+#pragma unroll
+        for (int a = 0; a < kFit1DMaxK - 1; ++a)
+            tr[a] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_thr[a])));
+        float jpart = 0.f;
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            // the empty asm hides that x and w do not change between
+            // iterations, so their float64 forms are not kept live across them
+            float xv = xs[p], wv = ws[p];
+            asm volatile("" : "+v"(xv), "+v"(wv));
+            int m = 0;
+#pragma unroll
+            for (int a = 0; a < kFit1DMaxK - 1; ++a) m += (xv >= tr[a]) ? 1 : 0;
+            const float tv = xv - s_val[m];
+            jpart = fmaf(wv, tv * tv, jpart);
+            // this lane's own bins, adds that return nothing: no point waits on another
+            atomicAdd(&s_bin[m][lane].x, (double)wv * (double)xv);
+            atomicAdd(&s_bin[m][lane].y, (double)wv);
+            if (p % 16 == 15) __builtin_amdgcn_sched_barrier(0);  // 16 points in flight at most
+        }
+        double jd = jpart;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) jd += __shfl_xor(jd, o, 64);
+        wave_sync();
+        // per-rank sums: lane (r, part) adds the bins of rank r of lanes
+        // part*16 .. +16; two exchanges combine the four parts
+        const int r = lane & (kFit1DMaxK - 1), part = lane >> 4;
+        double S = 0.0, W = 0.0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const double2 v = s_bin[r][part * 16 + q];
+            S += v.x;
+            W += v.y;
+        }
+        S += __shfl_xor(S, 16, 64);
+        W += __shfl_xor(W, 16, 64);
+        S += __shfl_xor(S, 32, 64);
+        W += __shfl_xor(W, 32, 64);
+        if (lane < A && W > 0.0) s_c[s_idx[lane]] = (float)(S / W);
+        if (lane == 0 && objective) objective[b * n_iter + t] = jd;
+        wave_sync();
+    }
+    // labels and counts of the last assignment: s_thr, s_val and s_idx still
+    // hold that iteration's values (only s_c has moved on)
+    if (n_iter > 0) {
+        float tr[kFit1DMaxK - 1];
+#pragma unroll
+        for (int a = 0; a < kFit1DMaxK - 1; ++a)
+            tr[a] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_thr[a])));
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int i = p * 64 + lane;
+            if (i < N) {
+                int m = 0;
+#pragma unroll
+                for (int a = 0; a < kFit1DMaxK - 1; ++a) m += (xs[p] >= tr[a]) ? 1 : 0;
+                if (labels) labels[b * N + i] = s_idx[m];
+                atomicAdd(&s_cnt[m], 1);
+            }
+        }
+        wave_sync();
+    }
+    if (lane < K) {
+        centroids[b * K + lane] = s_c[lane];
+        if (counts && n_iter > 0) {
+            int c = 0;  // ranks map to the smallest index of each value; other indices are empty
+            for (int q = 0; q < A; ++q)
+                if (s_idx[q] == lane) c = s_cnt[q];
+            counts[b * K + lane] = c;
+        }
+    }
+}
+
 hipError_t launch_fit_1d_rows(DType xt, const void* x, const float* w, int64_t B, int64_t N, const float* init,
                               int64_t K, int n_iter, float* centroids, int32_t* labels, int32_t* counts,
                               double* objective, hipStream_t s) {
@@ -282,9 +412,28 @@ hipError_t launch_fit_1d_rows(DType xt, const void* x, const float* w, int64_t B
     } else {                             \
         KM_F1(TT, 32);                   \
     }
-    if (xt == DType::F32) { KM_F1_T(float) }
-    else if (xt == DType::F16) { KM_F1_T(_Float16) }
-    else { KM_F1_T(bf16_t) }
+#define KM_FW(TT, PP)                                                                                 \
+    hipLaunchKernelGGL((k_fit_1d_wave<TT, PP>), grid, dim3(64), 0, s, (const TT*)x, w, (int)N, init,    \
+                       (int)K, n_iter, centroids, labels, counts, objective)
+#define KM_FW_T(TT)                      \
+    if (N <= 16 * 64) {                  \
+        KM_FW(TT, 16);                   \
+    } else if (N <= 32 * 64) {           \
+        KM_FW(TT, 32);                   \
+    } else {                             \
+        KM_FW(TT, 64);                   \
+    }
+    if (N <= kFit1DWaveMaxN) {
+        if (xt == DType::F32) { KM_FW_T(float) }
+        else if (xt == DType::F16) { KM_FW_T(_Float16) }
+        else { KM_FW_T(bf16_t) }
+    } else {
+        if (xt == DType::F32) { KM_F1_T(float) }
+        else if (xt == DType::F16) { KM_F1_T(_Float16) }
+        else { KM_F1_T(bf16_t) }
+    }
+#undef KM_FW_T
+#undef KM_FW
 #undef KM_F1_T
 #undef KM_F1
     return hipGetLastError();
