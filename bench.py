@@ -168,13 +168,65 @@ def bench_fit_1d(args, km, wl, p, x, w, C):
                    "weighted": wl.weighted, "init": wl.init, "path": "whole fit in one launch"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_GOPS, "unit": "Gop/s",
                      "frac": achieved / PEAK_VALU_GOPS, "traffic": None,
-                     "kernel": "k_fit_1d_rows" if N <= 8192 and K <= 16 else "kmeans_fit",
+                     "kernel": ("k_fit_1d_wave" if N <= 4096 else "k_fit_1d_rows") if N <= 8192 and K <= 16
+                     else "kmeans_fit",
                      "algorithmic_per_launch": ops, "avg_launch_ms": fit_ms},
         "cpu_baseline": None,
     }
+    out["steps_1d"] = bench_steps_1d(km, wl, x, w, C)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _device_ms(fn, reps: int) -> float:
+    """Device time per call of fn, with the calls queued back to back: a spin
+    kernel holds the stream while they are enqueued, so host-side launch
+    overhead does not open gaps between them."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e6))
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_steps_1d(km, wl, x, w, C, reps: int = 10) -> dict:
+    """The single assignment (with the weighted objective) and update calls on
+    the same rows, each against HBM: the bytes they must move are the points,
+    the weights and the labels once each, plus the centroids (the update needs
+    no argsort for K <= 16, so no permutation bytes are counted)."""
+    import torch
+
+    B, N, K, s = wl.B, wl.N, wl.K, ELEM_BYTES[wl.dtype]
+    labels = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    counts = torch.empty((B, K), dtype=torch.int32, device=x.device)
+    obj = torch.empty((B,), dtype=torch.float64, device=x.device)
+    c_new = torch.empty_like(C)
+    ws = km.workspace(B, N, 1, K, x.dtype, x.device)
+    wb = 4 * B * N if w is not None else 0
+
+    def assign():
+        km.kmeans_assign(x, C, weights=w, labels=labels, objective=obj, ws=ws)
+
+    def update():
+        km.kmeans_update(x, labels, C, weights=w, c_new=c_new, counts=counts, ws=ws)
+
+    assign()
+    update()
+    a_ms, u_ms = _device_ms(assign, reps), _device_ms(update, reps)
+    a_bytes = B * N * (s + 4) + wb + 4 * B * K
+    u_bytes = B * N * (s + 4) + wb + 8 * B * K + 4 * B * K
+    out = {}
+    for name, ms, nb in (("assign", a_ms, a_bytes), ("update", u_ms, u_bytes)):
+        gbs = nb / (ms * 1e-3) / 1e9
+        out[name] = {"avg_ms": ms, "algorithmic_bytes": nb, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    return out
 
 
 def main():

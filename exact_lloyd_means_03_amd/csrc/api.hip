@@ -33,7 +33,10 @@ static km_status hip_fail(hipError_t e, const char* where) {
 static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static bool use_assign_1d(int64_t d, int64_t K) { return d == 1 && assign_1d_supports(K); }
-static bool use_update_1d(int64_t d, int64_t N, int64_t K) { return d == 1 && update_1d_row_fits(N, K); }
+static bool use_update_1d(DType xt, const void* x, const float* w, const int32_t* labels, int64_t d, int64_t N,
+                          int64_t K) {
+    return d == 1 && (update_1d_row_fits(N, K) || update_1d_few_fits(xt, x, w, labels, N, K));
+}
 
 Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     Workspace w{};
@@ -143,7 +146,14 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
                      const Workspace& W, void* ws, hipStream_t s) {
     double* part = obj_out ? at<double>(ws, W.obj_part) : nullptr;
     if (use_assign_1d(d, K)) {
-        KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, part, W.nblk_assign, s), "assign_1d");
+        if (obj_out && N > 0 && W.nblk_assign == 1) {
+            // one partial per row: it is the row's objective, written in place
+            KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, obj_out, obj_stride, 1, s),
+                   "assign_1d");
+            return KM_OK;
+        }
+        KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, part, W.nblk_assign, W.nblk_assign, s),
+               "assign_1d");
     } else {
         void* blob = at<void>(ws, W.chat);
         KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, blob, s), "prep");
@@ -174,7 +184,7 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
                      const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
                      const Workspace& W, void* ws, hipStream_t s) {
     int32_t* cnt = counts ? counts : at<int32_t>(ws, W.counts);
-    if (use_update_1d(d, N, K)) {
+    if (use_update_1d(xt, x, w, labels, d, N, K)) {
         KM_HIP(launch_update_1d_row(xt, x, w, B, N, labels, K, c_old, c_new, cnt, s), "update_1d_row");
         return KM_OK;
     }

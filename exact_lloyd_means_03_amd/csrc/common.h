@@ -95,9 +95,11 @@ hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int
                               float* min_dist, double* obj_part, int64_t nblk, hipStream_t s);
 int64_t assign_mfma_blocks(int64_t N, int DP, DType xt);
 
+// obj_part (may be NULL): the objective partial of block j of row b goes to
+// obj_part[b * obj_stride + j].
 hipError_t launch_assign_1d(DType xt, const void* x, int64_t B, int64_t N, const float* C,
                             int64_t K, const float* w, int32_t* labels, float* min_dist,
-                            double* obj_part, int64_t nblk, hipStream_t s);
+                            double* obj_part, int64_t obj_stride, int64_t nblk, hipStream_t s);
 int64_t assign_1d_blocks(int64_t N);
 bool assign_1d_supports(int64_t K);
 
@@ -122,13 +124,15 @@ hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* co
                          int64_t B, int64_t K, int d, const float* c_old, float* c_new,
                          hipStream_t s);
 
-// Scalar points: whole-row on-chip update (sort-inverse in LDS).
 // Whole fits of scalar rows kept on chip (one block per row, all iterations).
 bool fit_1d_rows_fits(int64_t N, int64_t K);
 hipError_t launch_fit_1d_rows(DType xt, const void* x, const float* w, int64_t B, int64_t N, const float* init,
                               int64_t K, int n_iter, float* centroids, int32_t* labels, int32_t* counts,
                               double* objective, hipStream_t s);
+// Scalar points: whole-row on-chip update (sort-inverse in LDS).
 bool update_1d_row_fits(int64_t N, int64_t K);
+// Few clusters (K <= 16): one wave per row, N % 4 == 0, aligned rows.
+bool update_1d_few_fits(DType xt, const void* x, const float* w, const int32_t* labels, int64_t N, int64_t K);
 hipError_t launch_update_1d_row(DType xt, const void* x, const float* w, int64_t B, int64_t N,
                                 const int32_t* labels, int64_t K, const float* c_old,
                                 float* c_new, int32_t* counts, hipStream_t s);

@@ -33,120 +33,15 @@
 //      that duplicates a smaller index's value.
 // After the last iteration the labels and counts of its assignment are
 // written.
-#include "common.h"
+#include "scalar_rows.h"
 
 namespace km {
 
 constexpr int kFit1DThreads = 256;
-constexpr int kFit1DMaxK = 16;
 constexpr int kFit1DMaxN = 8192;
 constexpr int kFit1DWaveMaxN = 64 * 64;  // rows a single wave keeps in registers
 
 bool fit_1d_rows_fits(int64_t N, int64_t K) { return N >= 1 && N <= kFit1DMaxN && K <= kFit1DMaxK; }
-
-template <typename T>
-__device__ __forceinline__ float f1_round(float v) {
-    if constexpr (sizeof(T) == 4) return v;
-    else if constexpr (__is_same(T, _Float16)) return (float)(_Float16)v;
-    else return bf16_to_f32(f32_to_bf16_rne(v));
-}
-
-template <typename T>
-__device__ __forceinline__ float f1_load(const T* p) {
-    if constexpr (sizeof(T) == 4) return *p;
-    else if constexpr (__is_same(T, _Float16)) return (float)*p;
-    else return bf16_to_f32(*p);
-}
-
-// Order-preserving float <-> uint32 maps (-0 is canonicalized to +0 first).
-__device__ __forceinline__ uint32_t f1_ord(float f) {
-    const uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float f1_unord(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-
-// x prefers (va, ia) over (vb, ib): smaller float32 squared distance, or the
-// same distance and the smaller index.
-__device__ __forceinline__ bool f1_prefers(float x, float va, int ia, float vb, int ib) {
-    const float ta = x - va, tb = vb - x;
-    const float da = ta * ta, db = tb * tb;
-    return da < db || (da == db && ia < ib);
-}
-
-// Steps 1-2 for one row, by one wave: from the centroids in s_c, the distinct
-// rounded values in ascending order (s_val), the smallest index holding each
-// (s_idx) and the thresholds between neighbours (s_thr, +inf past A - 1).
-// Returns A, the number of distinct values (the same in every lane).
-template <typename T>
-__device__ __forceinline__ int f1_thresholds(const float* s_c, int K, int lane, float* s_val, int* s_idx,
-                                             float* s_thr) {
-    float u[kFit1DMaxK];  // every centroid, rounded (the same in all lanes)
-#pragma unroll
-    for (int k = 0; k < kFit1DMaxK; ++k) u[k] = k < K ? f1_round<T>(s_c[k]) : INFINITY;
-    const float v = lane < K ? f1_round<T>(s_c[lane]) : INFINITY;
-    bool first = lane < K;  // no smaller index holds the same value
-#pragma unroll
-    for (int k = 0; k < kFit1DMaxK; ++k)
-        if (k < lane && u[k] == v) first = false;
-    const unsigned long long firsts = __ballot(first);
-    int a = 0;  // distinct values below v
-#pragma unroll
-    for (int k = 0; k < kFit1DMaxK; ++k)
-        if (((firsts >> k) & 1ull) && u[k] < v) ++a;
-    if (first) {
-        s_val[a] = v;
-        s_idx[a] = lane;
-    }
-    const int A = __popcll(firsts);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    if (lane < kFit1DMaxK) {
-        float thr = INFINITY;
-        if (lane < A - 1) {
-            const float va = s_val[lane], vb = s_val[lane + 1];
-            const int ia = s_idx[lane], ib = s_idx[lane + 1];
-            // invariant: x = unord(lo) prefers va, x = unord(hi) does not
-            uint32_t lo = f1_ord(va), hi = f1_ord(vb);
-            // the switch is within a few floats of the midpoint: probe
-            // there, gallop outwards, then bisect the bracket found
-            uint32_t probe = f1_ord(va + 0.5f * (vb - va));
-            probe = probe <= lo ? lo + 1 : (probe > hi ? hi : probe);
-            if (probe < hi) {
-                if (f1_prefers(f1_unord(probe), va, ia, vb, ib)) {
-                    lo = probe;
-                    for (uint32_t step = 1; step < hi - lo; step <<= 1) {  // lo + step < hi
-                        if (f1_prefers(f1_unord(lo + step), va, ia, vb, ib)) {
-                            lo += step;
-                        } else {
-                            hi = lo + step;
-                            break;
-                        }
-                    }
-                } else {
-                    hi = probe;
-                    for (uint32_t step = 1; step < hi - lo; step <<= 1) {  // hi - step > lo
-                        if (!f1_prefers(f1_unord(hi - step), va, ia, vb, ib)) {
-                            hi -= step;
-                        } else {
-                            lo = hi - step;
-                            break;
-                        }
-                    }
-                }
-            }
-            while (hi - lo > 1) {
-                const uint32_t mid = lo + ((hi - lo) >> 1);
-                if (f1_prefers(f1_unord(mid), va, ia, vb, ib)) lo = mid;
-                else hi = mid;
-            }
-            thr = f1_unord(hi);
-        }
-        s_thr[lane] = thr;
-    }
-    return A;
-}
 
 // PPT: points per thread (N <= PPT * kFit1DThreads).
 template <typename T, int PPT>
@@ -322,11 +217,9 @@ __global__ __launch_bounds__(64) void k_fit_1d_wave(
         for (int r = 0; r < kFit1DMaxK; ++r) s_bin[r][lane] = make_double2(0.0, 0.0);
         wave_sync();
         // the thresholds are the same in every lane: held in scalar registers,
-        // a point's rank is a branch-free count of compares
+        // a point's rank is a branch-free count over them
         float tr[kFit1DMaxK - 1];
-#pragma unroll
-        for (int a = 0; a < kFit1DMaxK - 1; ++a)
-            tr[a] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_thr[a])));
+        f1_scalar_thresholds(s_thr, tr);
         float jpart = 0.f;
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
@@ -334,9 +227,7 @@ __global__ __launch_bounds__(64) void k_fit_1d_wave(
             // iterations, so their float64 forms are not kept live across them
             float xv = xs[p], wv = ws[p];
             asm volatile("" : "+v"(xv), "+v"(wv));
-            int m = 0;
-#pragma unroll
-            for (int a = 0; a < kFit1DMaxK - 1; ++a) m += (xv >= tr[a]) ? 1 : 0;
+            const int m = f1_rank_cmp(xv, tr);
             const float tv = xv - s_val[m];
             jpart = fmaf(wv, tv * tv, jpart);
             // this lane's own bins, adds that return nothing: no point waits on another
@@ -370,16 +261,12 @@ __global__ __launch_bounds__(64) void k_fit_1d_wave(
     // hold that iteration's values (only s_c has moved on)
     if (n_iter > 0) {
         float tr[kFit1DMaxK - 1];
-#pragma unroll
-        for (int a = 0; a < kFit1DMaxK - 1; ++a)
-            tr[a] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_thr[a])));
+        f1_scalar_thresholds(s_thr, tr);
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int i = p * 64 + lane;
             if (i < N) {
-                int m = 0;
-#pragma unroll
-                for (int a = 0; a < kFit1DMaxK - 1; ++a) m += (xs[p] >= tr[a]) ? 1 : 0;
+                const int m = f1_rank_cmp(xs[p], tr);
                 if (labels) labels[b * N + i] = s_idx[m];
                 atomicAdd(&s_cnt[m], 1);
             }

@@ -127,10 +127,29 @@ __global__ __launch_bounds__(1024) void k_obj_reduce(const double* __restrict__ 
     if (threadIdx.x == 0) out[b * out_stride] = red[0];
 }
 
+// Few partials per row (many short rows): one wave per row, four rows per block.
+__global__ __launch_bounds__(256) void k_obj_reduce_rows(const double* __restrict__ part, int64_t B,
+                                                         int64_t nblk, double* __restrict__ out,
+                                                         int64_t out_stride) {
+    const int lane = threadIdx.x & 63;
+    const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= B) return;
+    const double* pb = part + b * nblk;
+    double acc = 0.0;
+    for (int64_t i = lane; i < nblk; i += 64) acc += pb[i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) out[b * out_stride] = acc;
+}
+
 hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double* out,
                              int64_t out_stride, hipStream_t s) {
     if (B == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_obj_reduce, dim3((unsigned)B), dim3(1024), 0, s, part, nblk, out, out_stride);
+    if (nblk <= 256)
+        hipLaunchKernelGGL(k_obj_reduce_rows, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s, part, B, nblk, out,
+                           out_stride);
+    else
+        hipLaunchKernelGGL(k_obj_reduce, dim3((unsigned)B), dim3(1024), 0, s, part, nblk, out, out_stride);
     return hipGetLastError();
 }
 

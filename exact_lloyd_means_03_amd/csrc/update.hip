@@ -24,8 +24,11 @@
 //
 // Scalar points (d == 1) with a row that fits in LDS take a whole-row kernel
 // instead: the row's (x, w) pairs are placed in cluster order in LDS and each
-// segment is summed by one wave in float64.
-#include "common.h"
+// segment is summed by one wave in float64.  Rows with few clusters (K <= 16)
+// need no ordering at all: one wave streams the row and adds every point into
+// bins of its own lane (float64 sums, integer counts), then combines the
+// lanes' bins.
+#include "scalar_rows.h"
 
 namespace km {
 
@@ -426,10 +429,137 @@ __global__ __launch_bounds__(256) void k_update_1d_row(const T* __restrict__ X, 
     }
 }
 
+// d == 1, K <= KC <= 16, rows of up to kUpd1DFewMaxN points with N % 4 == 0
+// and four-element-aligned rows: one wave per row.  Each lane adds its points
+// into its own bins in LDS (bin j of lane l at [j][l]: the 64 lanes of one
+// add cover consecutive 8-byte words, so an add touches every bank the same
+// number of times whatever the labels), with adds that return nothing; no
+// other lane touches those words, so the adds of one point never wait on
+// another's.  Labels outside [0, K) add nothing.
+constexpr int kUpd1DFewMaxN = 16384;
+constexpr int kUpd1DGroups = 4;
+
+template <typename T, int KC, bool WEIGHTED>
+__global__ __launch_bounds__(64) void k_update_1d_few(const T* __restrict__ X, const float* __restrict__ w,
+                                                      int N, const int32_t* __restrict__ labels, int K,
+                                                      const float* c_old, float* c_new,
+                                                      int32_t* __restrict__ counts) {
+    constexpr int G = kUpd1DGroups, P = 4 * G;
+    __shared__ double s_S[KC][64];                 // sum of w * x
+    __shared__ double s_W[WEIGHTED ? KC : 1][64];  // sum of w (weighted rows)
+    __shared__ int32_t s_N[KC][64];                // number of points
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const T* Xb = X + b * N;
+    const int32_t* Lb = labels + b * N;
+    const float* wb = WEIGHTED ? w + b * N : nullptr;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+        s_S[j][lane] = 0.0;
+        if constexpr (WEIGHTED) s_W[j][lane] = 0.0;
+        s_N[j][lane] = 0;
+    }
+
+    auto load = [&](int g0, float (&xv)[P], float (&wv)[P], int (&lv)[P]) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int i = g0 + g * 256 + lane * 4;
+            float xq[4] = {0.f, 0.f, 0.f, 0.f}, wq[4] = {1.f, 1.f, 1.f, 1.f};
+            int lq[4] = {-1, -1, -1, -1};
+            if (i < N) {  // N and i are multiples of 4: the four points are in the row
+                typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+                const i32x4 l4 = __builtin_nontemporal_load((const i32x4*)(Lb + i));
+                lq[0] = l4[0], lq[1] = l4[1], lq[2] = l4[2], lq[3] = l4[3];
+                f1_load4<T>(Xb + i, xq);
+                if constexpr (WEIGHTED) f1_load4<float>(wb + i, wq);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[4 * g + e] = xq[e], wv[4 * g + e] = wq[e], lv[4 * g + e] = lq[e];
+        }
+    };
+
+    float xa[P], wa[P];
+    int la[P];
+    load(0, xa, wa, la);
+    f1_wave_sync();  // bins cleared
+    for (int g0 = 0; g0 < N; g0 += 256 * G) {
+        float xn[P], wn[P];
+        int ln[P];
+        if (g0 + 256 * G < N) load(g0 + 256 * G, xn, wn, ln);
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int l = la[j];
+            if ((uint32_t)l < (uint32_t)K) {
+                if constexpr (WEIGHTED) {
+                    atomicAdd(&s_S[l][lane], (double)wa[j] * (double)xa[j]);
+                    atomicAdd(&s_W[l][lane], (double)wa[j]);
+                } else {
+                    atomicAdd(&s_S[l][lane], (double)xa[j]);
+                }
+                atomicAdd(&s_N[l][lane], 1);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) xa[j] = xn[j], wa[j] = wn[j], la[j] = ln[j];
+    }
+    f1_wave_sync();
+    // lane (r, part) adds the bins of cluster r of lanes part*KC .. +KC (the
+    // walk starts at a different lane per r, so the reads spread over the
+    // banks), then exchanges combine the parts
+    const int r = lane % KC, part = lane / KC;
+    double S = 0.0, W = 0.0;
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+        const int l = part * KC + ((q + r) & (KC - 1));
+        S += s_S[r][l];
+        if constexpr (WEIGHTED) W += s_W[r][l];
+        n += s_N[r][l];
+    }
+#pragma unroll
+    for (int o = KC; o < 64; o <<= 1) {
+        S += __shfl_xor(S, o, 64);
+        if constexpr (WEIGHTED) W += __shfl_xor(W, o, 64);
+        n += __shfl_xor(n, o, 64);
+    }
+    if constexpr (!WEIGHTED) W = (double)n;
+    if (part == 0 && r < K) {
+        c_new[b * K + r] = n > 0 ? (float)(S / W) : c_old[b * K + r];
+        counts[b * K + r] = n;
+    }
+}
+
+bool update_1d_few_fits(DType xt, const void* x, const float* w, const int32_t* labels, int64_t N, int64_t K) {
+    const size_t eb = xt == DType::F32 ? 16 : 8;
+    return N <= kUpd1DFewMaxN && N % 4 == 0 && K <= kFit1DMaxK && (uintptr_t)x % eb == 0 &&
+           (uintptr_t)labels % 16 == 0 && (uintptr_t)w % 16 == 0;
+}
+
 hipError_t launch_update_1d_row(DType xt, const void* x, const float* w, int64_t B, int64_t N,
                                 const int32_t* labels, int64_t K, const float* c_old, float* c_new,
                                 int32_t* counts, hipStream_t s) {
     if (B == 0) return hipSuccess;
+    if (update_1d_few_fits(xt, x, w, labels, N, K)) {
+#define KM_U1F(TT, KK)                                                                                        \
+    do {                                                                                                      \
+        if (w)                                                                                                \
+            hipLaunchKernelGGL((k_update_1d_few<TT, KK, true>), dim3((unsigned)B), dim3(64), 0, s,            \
+                               (const TT*)x, w, (int)N, labels, (int)K, c_old, c_new, counts);                \
+        else                                                                                                  \
+            hipLaunchKernelGGL((k_update_1d_few<TT, KK, false>), dim3((unsigned)B), dim3(64), 0, s,           \
+                               (const TT*)x, w, (int)N, labels, (int)K, c_old, c_new, counts);                \
+    } while (0)
+#define KM_U1F_T(TT)              \
+    if (K <= 4) KM_U1F(TT, 4);     \
+    else if (K <= 8) KM_U1F(TT, 8); \
+    else KM_U1F(TT, 16);
+        if (xt == DType::F32) { KM_U1F_T(float) }
+        else if (xt == DType::F16) { KM_U1F_T(_Float16) }
+        else { KM_U1F_T(bf16_t) }
+#undef KM_U1F_T
+#undef KM_U1F
+        return hipGetLastError();
+    }
     if (!update_1d_row_fits(N, K)) return hipErrorInvalidValue;
     if (xt == DType::F32)
         hipLaunchKernelGGL(k_update_1d_row<float>, dim3((unsigned)B), dim3(256), 0, s, (const float*)x, w,
