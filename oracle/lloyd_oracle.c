@@ -304,6 +304,124 @@ int oracle_fit(const void *x, int dtype, const float *w,
     return ok ? 0 : -1;
 }
 
+/* ----------------------------------------------------------------------- *
+ * Globally optimal weighted 1D k-means of every row (github LeanModels/
+ * LeanQuant issue #1 "1D k-means": for scalar data the globally optimal
+ * centroids can be found, and the diff swaps Lloyd for such a 1D clustering
+ * with per-point sample weights that returns the centroids).
+ *
+ * Definition: among all partitions of a row's N points into K non-empty
+ * groups, one with the least J = sum_g sum_{i in g} w_i (x_i - mean_g)^2,
+ * mean_g = sum_g w_i x_i / sum_g w_i.  For scalars some optimal partition
+ * consists of runs of consecutive values in ascending order, so J* is the
+ * least cost over the ways to cut the sorted row into K non-empty runs.
+ * That minimum is taken by dynamic programming over prefixes of the sorted
+ * row:
+ *     D[1][j] = SSE(0, j),
+ *     D[k][j] = min over k-1 <= i < j of D[k-1][i] + SSE(i, j),
+ * where SSE(i, j) is the weighted sum of squared deviations of sorted points
+ * i .. j-1 from their weighted mean.  For fixed j, SSE(i, j) is accumulated
+ * point by point as i moves down (running weight, weighted mean and sum of
+ * squares, fp64).  The first minimizing i (smallest) is kept; points are
+ * sorted by (value, original index).
+ *
+ * X [B,N] fp64 values, w [B,N] fp64 weights or NULL (all 1), 1 <= K <= N.
+ * Outputs: J_out [B] = D[K][N]; means_out [B,K] the run means in ascending
+ * order (fp64, each a fresh weighted average of its run); labels_out [B,N]
+ * the run of every point (in the row's original order); counts_out [B,K] the
+ * run sizes.  Returns 0, or -1 when memory runs out or K is out of range.
+ * ----------------------------------------------------------------------- */
+typedef struct { double v; int64_t i; } orc_vi;
+
+static int orc_vi_cmp(const void *a, const void *b)
+{
+    const orc_vi *p = (const orc_vi *)a, *q = (const orc_vi *)b;
+    if (p->v < q->v) return -1;
+    if (p->v > q->v) return 1;
+    return (p->i > q->i) - (p->i < q->i);
+}
+
+int oracle_optimal_1d(const double *X, const double *w, int64_t B, int64_t N, int64_t K,
+                      double *J_out, double *means_out, int32_t *labels_out, int32_t *counts_out)
+{
+    if (K < 1 || K > N) return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t b = 0; b < B; ++b) {
+        orc_vi *s = (orc_vi *)malloc((size_t)N * sizeof(orc_vi));
+        double *xs = (double *)malloc((size_t)N * sizeof(double));
+        double *ws = (double *)malloc((size_t)N * sizeof(double));
+        double *D = (double *)malloc((size_t)((K + 1) * (N + 1)) * sizeof(double));
+        int64_t *cut = (int64_t *)malloc((size_t)((K + 1) * (N + 1)) * sizeof(int64_t));
+        int64_t *bound = (int64_t *)malloc((size_t)(K + 1) * sizeof(int64_t));
+        if (!s || !xs || !ws || !D || !cut || !bound) {
+            failed = 1;
+        } else {
+            for (int64_t i = 0; i < N; ++i) {
+                s[i].v = X[b * N + i];
+                s[i].i = i;
+            }
+            qsort(s, (size_t)N, sizeof(orc_vi), orc_vi_cmp);
+            for (int64_t p = 0; p < N; ++p) {
+                xs[p] = s[p].v;
+                ws[p] = w ? w[b * N + s[p].i] : 1.0;
+            }
+            for (int64_t k = 0; k <= K; ++k)
+                for (int64_t j = 0; j <= N; ++j) {
+                    D[k * (N + 1) + j] = INFINITY;
+                    cut[k * (N + 1) + j] = -1;
+                }
+            D[0] = 0.0; /* no points in no runs */
+            for (int64_t k = 1; k <= K; ++k) {
+                for (int64_t j = k; j <= N; ++j) {
+                    double best = INFINITY;
+                    int64_t arg = -1;
+                    /* the last run is sorted points i .. j-1; grow it downwards */
+                    double W = 0.0, mean = 0.0, sse = 0.0;
+                    for (int64_t i = j - 1; i >= k - 1; --i) {
+                        const double wi = ws[i], xi = xs[i];
+                        const double Wn = W + wi;
+                        const double delta = xi - mean;
+                        const double mean_n = mean + wi * delta / Wn;
+                        sse += wi * delta * (xi - mean_n);
+                        W = Wn;
+                        mean = mean_n;
+                        const double cand = D[(k - 1) * (N + 1) + i] + sse;
+                        /* i descends, so '<=' keeps the smallest i among equal costs */
+                        if (cand <= best) {
+                            best = cand;
+                            arg = i;
+                        }
+                    }
+                    D[k * (N + 1) + j] = best;
+                    cut[k * (N + 1) + j] = arg;
+                }
+            }
+            J_out[b] = D[K * (N + 1) + N];
+            /* runs from the cuts: run k-1 is sorted points bound[k-1] .. bound[k]-1 */
+            bound[K] = N;
+            for (int64_t k = K; k >= 1; --k) bound[k - 1] = cut[k * (N + 1) + bound[k]];
+            for (int64_t k = 0; k < K; ++k) {
+                double sw = 0.0, swx = 0.0;
+                for (int64_t p = bound[k]; p < bound[k + 1]; ++p) {
+                    sw += ws[p];
+                    swx += ws[p] * xs[p];
+                    labels_out[b * N + s[p].i] = (int32_t)k;
+                }
+                means_out[b * K + k] = swx / sw;
+                counts_out[b * K + k] = (int32_t)(bound[k + 1] - bound[k]);
+            }
+        }
+        free(s);
+        free(xs);
+        free(ws);
+        free(D);
+        free(cut);
+        free(bound);
+    }
+    return failed ? -1 : 0;
+}
+
 int oracle_num_threads(void)
 {
     int n = 1;

@@ -42,6 +42,8 @@ def load_library(path: str):
                              p, p, p, p, p, p]
     L.oracle_fit.restype = C.c_int
     L.oracle_num_threads.restype = C.c_int
+    L.oracle_optimal_1d.argtypes = [p, p, i64, i64, i64, p, p, p, p]
+    L.oracle_optimal_1d.restype = C.c_int
     return L
 
 
@@ -168,6 +170,29 @@ def fit(x_bits: np.ndarray, dtype: str, w, init: np.ndarray, n_iter: int) -> dic
     if rc != 0:
         raise MemoryError("oracle_fit ran out of host memory")
     return dict(centroids=C_out, labels=labels, counts=counts, J=J, d1=d1, d2=d2)
+
+
+def optimal_1d(X: np.ndarray, w, K: int) -> dict:
+    """Globally optimal weighted 1D k-means of every row.  X [B,N] fp64 (or
+    [B,N,1]), w [B,N] or None, 1 <= K <= N.  Returns J [B] (fp64), means
+    [B,K] (fp64, ascending), labels int32 [B,N] (run index of every point)
+    and counts int32 [B,K]."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    if X.ndim == 3:
+        assert X.shape[2] == 1
+        X = X[..., 0]
+    X = np.ascontiguousarray(X)
+    B, N = X.shape
+    wd = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
+    J = np.empty(B, np.float64)
+    means = np.empty((B, K), np.float64)
+    labels = np.empty((B, N), np.int32)
+    counts = np.empty((B, K), np.int32)
+    rc = lib().oracle_optimal_1d(_ptr(X), _ptr(wd), B, N, int(K), _ptr(J), _ptr(means), _ptr(labels),
+                                 _ptr(counts))
+    if rc != 0:
+        raise ValueError(f"oracle_optimal_1d failed (K={K}, N={N}, or out of memory)")
+    return dict(J=J, means=means, labels=labels, counts=counts)
 
 
 def near_tie(d1: np.ndarray, d2: np.ndarray, rel: float = 1e-4) -> np.ndarray:

@@ -50,6 +50,18 @@ MUTANTS = [
      "                    J += d1_out[b * N + i];"),
     ("objective of the previous centroids", "                J_out[b * n_iter + t] = J;",
      "                J_out[b * n_iter + t] = t > 0 ? J_out[b * n_iter + t - 1] : J;"),
+    ("optimum: running scatter ignores the weights", "                        sse += wi * delta * (xi - mean_n);",
+     "                        sse += delta * (xi - mean_n);"),
+    ("optimum: running mean update unweighted", "                        const double mean_n = mean + wi * delta / Wn;",
+     "                        const double mean_n = mean + delta / Wn;"),
+    ("optimum: previous prefix one point too long", "                        const double cand = D[(k - 1) * (N + 1) + i] + sse;",
+     "                        const double cand = D[(k - 1) * (N + 1) + i + 1] + sse;"),
+    ("optimum: ties go to the latest cut", "                        if (cand <= best) {", "                        if (cand < best) {"),
+    ("optimum: last run starts one point late", "        bound[K] = N;\n            for (int64_t k = K; k >= 1; --k) bound[k - 1] = cut[k * (N + 1) + bound[k]];",
+     "        bound[K] = N;\n            for (int64_t k = K; k >= 1; --k) bound[k - 1] = cut[k * (N + 1) + bound[k]] + (k == K);"),
+    ("optimum: means not weighted", "                    swx += ws[p] * xs[p];", "                    swx += xs[p];"),
+    ("optimum: runs numbered from the top", "                    labels_out[b * N + s[p].i] = (int32_t)k;",
+     "                    labels_out[b * N + s[p].i] = (int32_t)(K - 1 - k);"),
 ]
 
 

@@ -392,3 +392,110 @@ def test_objective_of_labels(orc):
     assert abs(J[1] - want) <= 1e-10 * want
     worse = orc.objective(Xd, w, (r["labels"] + 1) % 7, init.astype(np.float64))
     assert np.all(worse > J)
+
+
+# ------------------------------------------- globally optimal 1D k-means
+
+def _groups(labels):
+    """The partition of labels as a set of frozensets of point indices."""
+    out = {}
+    for i, l in enumerate(labels):
+        out.setdefault(int(l), set()).add(i)
+    return {frozenset(g) for g in out.values()}
+
+
+def test_optimal_1d_matches_every_labelling(orc):
+    """Exhaustive search over all K^N labellings (no contiguity assumed)."""
+    rng = np.random.default_rng(21)
+    for trial in range(6):
+        n, K = (8, 3) if trial % 2 else (7, 2)
+        v = (0.02 * rng.standard_t(4, n))
+        w = rng.uniform(0.1, 1.0, n) if trial % 3 else None
+        Jstar, lab = brute.best_partition([(float(t),) for t in v], K, None if w is None else list(w))
+        r = orc.optimal_1d(v[None], None if w is None else w[None], K)
+        assert abs(r["J"][0] - Jstar) <= 1e-12 * Jstar
+        assert _groups(r["labels"][0]) == _groups(lab)
+        assert r["counts"][0].sum() == n and np.all(r["counts"][0] >= 1)
+        # labels are runs of the sorted values, numbered in ascending order
+        assert np.all(np.diff(r["labels"][0][np.argsort(v, kind="stable")]) >= 0)
+
+
+def test_optimal_1d_matches_split_enumeration(orc):
+    """The C(N-1, K-1) ways to cut the sorted values into K runs."""
+    rng = np.random.default_rng(22)
+    for trial in range(3):
+        n, K = 11, 4
+        v = rng.normal(0, 1, n)
+        w = rng.uniform(0.1, 1.0, n)
+        Jstar, means = brute.best_1d_split(list(v), K, list(w))
+        r = orc.optimal_1d(v[None], w[None], K)
+        assert abs(r["J"][0] - Jstar) <= 1e-12 * Jstar
+        np.testing.assert_allclose(r["means"][0], means, rtol=1e-12, atol=1e-15)
+
+
+def test_optimal_1d_worked_example(orc):
+    """The pages' thirteen weights: the optimum is the three printed groups
+    with the printed shared values."""
+    g = json.load(open(os.path.join(HERE, "golden", "cache_aware_clustering_example.json")))
+    v = np.array(g["weights13"], dtype=np.float32).astype(np.float64)
+    r = orc.optimal_1d(v[None], None, 3)
+    assert _groups(r["labels"][0]) == {frozenset(x) for x in g["groups13"]}
+    printed = sorted(g["centroids13_printed"].values())
+    np.testing.assert_array_equal(np.round(r["means"][0], g["decimals"]), printed)
+    Jstar, _ = brute.best_1d_split([float(t) for t in v], 3)
+    assert abs(r["J"][0] - Jstar) <= 1e-12 * Jstar
+
+
+def test_optimal_1d_closed_forms(orc):
+    rng = np.random.default_rng(23)
+    v = rng.normal(0.3, 0.1, 300)
+    w = rng.uniform(0.1, 1.0, 300)
+    # one run: the weighted mean and the total weighted scatter
+    r = orc.optimal_1d(v[None], w[None], 1)
+    m = (w * v).sum() / w.sum()
+    assert abs(r["means"][0, 0] - m) <= 1e-14
+    assert abs(r["J"][0] - (w * (v - m) ** 2).sum()) <= 1e-12 * r["J"][0]
+    # as many runs as distinct points: every point alone, J = 0
+    u = rng.permutation(np.arange(40) * 0.25 - 3.0)
+    r = orc.optimal_1d(u[None], None, 40)
+    assert r["J"][0] == 0.0
+    np.testing.assert_array_equal(r["means"][0], np.sort(u))
+    np.testing.assert_array_equal(r["labels"][0], np.argsort(np.argsort(u)))
+    # a weight of 2 is the same as the point twice
+    K = 5
+    r1 = orc.optimal_1d(v[None], np.where(np.arange(300) == 17, 2.0, 1.0)[None], K)
+    r2 = orc.optimal_1d(np.append(v, v[17])[None], None, K)
+    assert abs(r1["J"][0] - r2["J"][0]) <= 1e-12 * r2["J"][0]
+    np.testing.assert_allclose(r1["means"][0], r2["means"][0], rtol=1e-12)
+    # translation moves the means and keeps J; scaling by 2 multiplies J by 4
+    r0 = orc.optimal_1d(v[None], w[None], K)
+    rt = orc.optimal_1d((v + 0.5)[None], w[None], K)
+    rs = orc.optimal_1d((2.0 * v)[None], w[None], K)
+    assert abs(rt["J"][0] - r0["J"][0]) <= 1e-9 * r0["J"][0]
+    np.testing.assert_allclose(rt["means"][0], r0["means"][0] + 0.5, rtol=1e-12)
+    assert abs(rs["J"][0] - 4 * r0["J"][0]) <= 1e-12 * r0["J"][0]
+
+
+def test_optimal_1d_earliest_cut_on_ties(orc):
+    """Values 2, 1, 1, 1 in three runs: J = 0 either way the equal values are
+    cut; the earliest cut in sorted (value, index) order is kept."""
+    r = orc.optimal_1d(np.array([[2.0, 1.0, 1.0, 1.0]]), None, 3)
+    assert r["J"][0] == 0.0
+    np.testing.assert_array_equal(r["labels"][0], [2, 0, 1, 1])
+    np.testing.assert_array_equal(r["counts"][0], [1, 2, 1])
+
+
+def test_optimal_1d_bounds_lloyd(orc):
+    """Lloyd from a grid init never goes below the optimum, and the
+    optimum's labels and means reproduce its J."""
+    rng = np.random.default_rng(24)
+    X = (0.02 * rng.standard_t(4, (3, 150))).astype(np.float32)
+    w = rng.uniform(0.1, 1.0, (3, 150)).astype(np.float32)
+    K = 6
+    r = orc.optimal_1d(X.astype(np.float64), w.astype(np.float64), K)
+    init = np.stack([np.linspace(x.min(), x.max(), K) for x in X]).astype(np.float32)[..., None]
+    lloyd = orc.fit(X[..., None], "f32", w, init, 30)
+    assert np.all(lloyd["J"][:, -1] >= r["J"] * (1 - 1e-12))
+    Jl = orc.objective(X[..., None].astype(np.float64), w.astype(np.float64), r["labels"],
+                       r["means"][..., None])
+    np.testing.assert_allclose(Jl, r["J"], rtol=1e-12)
