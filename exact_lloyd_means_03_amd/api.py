@@ -158,3 +158,38 @@ def kmeans_fit(x, init, n_iter: int, weights=None, centroids=None, labels=None, 
                                 ws.numel(), _stream(dev))
     _lib.check(st, "kmeans_fit")
     return centroids, labels, counts, objective
+
+
+def kmeans_optimal_1d(x, K: int, weights=None, centroids=None, labels=None, counts=None, objective=None, ws=None):
+    """Globally optimal weighted 1D k-means of every row of x [B, N] (or
+    [B, N, 1]).  Returns (centroids [B, K] float32 ascending, labels [B, N]
+    int32, counts [B, K] int32, objective [B] float64)."""
+    _dev_tensor(x, "x")
+    if x.dim() == 3 and x.shape[2] == 1:
+        B, N = x.shape[0], x.shape[1]
+    elif x.dim() == 2:
+        B, N = x.shape
+    else:
+        raise ValueError("x must be [B, N] or [B, N, 1]")
+    if x.dtype not in _DT:
+        raise TypeError(f"x dtype {x.dtype} is not float32 / float16 / bfloat16")
+    dev = x.device
+    if weights is not None:
+        _dev_tensor(weights, "weights", torch.float32, (B, N))
+    centroids = torch.empty((B, K), dtype=torch.float32, device=dev) if centroids is None else \
+        _dev_tensor(centroids, "centroids", torch.float32, (B, K))
+    labels = torch.empty((B, N), dtype=torch.int32, device=dev) if labels is None else \
+        _dev_tensor(labels, "labels", torch.int32, (B, N))
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev) if counts is None else \
+        _dev_tensor(counts, "counts", torch.int32, (B, K))
+    objective = torch.empty((B,), dtype=torch.float64, device=dev) if objective is None else \
+        _dev_tensor(objective, "objective", torch.float64, (B,))
+    L = _lib.load()
+    if ws is None:
+        n = L.kmeans_optimal_1d_workspace_bytes(B, N, K)
+        ws = torch.empty(max(int(n), 256), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "workspace", torch.uint8)
+    st = L.kmeans_optimal_1d(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, K, _ptr(centroids), _ptr(labels),
+                             _ptr(counts), _ptr(objective), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_optimal_1d")
+    return centroids, labels, counts, objective

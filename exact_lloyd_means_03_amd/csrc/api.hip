@@ -293,6 +293,39 @@ km_status kmeans_fit(const void* x, km_dtype xt, const float* weights, int64_t B
     return KM_OK;
 }
 
+size_t kmeans_optimal_1d_workspace_bytes(int64_t B, int64_t N, int64_t K) {
+    if (B < 0 || !optimal_1d_supports(N, K)) return 0;
+    size_t d_off, cut_off, perm_off, total;
+    optimal_1d_workspace(B, N, K, &d_off, &cut_off, &perm_off, &total);
+    return total;
+}
+
+km_status kmeans_optimal_1d(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t K,
+                            float* centroids, int32_t* labels, int32_t* counts, double* objective,
+                            void* workspace, size_t workspace_bytes, km_stream stream) {
+    if (B < 0 || N < 0) return fail(KM_EINVAL, "negative size: B=%lld N=%lld", (long long)B, (long long)N);
+    if (xt != KM_F32 && xt != KM_F16 && xt != KM_BF16) return fail(KM_EUNSUPPORTED, "unknown dtype %d", xt);
+    if (K < 1 || K > N)
+        return fail(KM_EINVAL, "the optimum needs 1 <= K <= N (K=%lld, N=%lld)", (long long)K, (long long)N);
+    if (N > kOpt1DMaxN)
+        return fail(KM_EUNSUPPORTED, "the optimum supports rows of N <= %d points (N=%lld)", kOpt1DMaxN,
+                    (long long)N);
+    if (K > kOpt1DMaxK)
+        return fail(KM_EUNSUPPORTED, "the optimum supports K <= %d (K=%lld)", kOpt1DMaxK, (long long)K);
+    if (B > kMaxB) return fail(KM_EUNSUPPORTED, "B=%lld > %lld is not supported", (long long)B, (long long)kMaxB);
+    KM_TRY(need(x, B * N, "x"));
+    KM_TRY(need(centroids, B, "centroids"));
+    size_t d_off, cut_off, perm_off, total;
+    optimal_1d_workspace(B, N, K, &d_off, &cut_off, &perm_off, &total);
+    Workspace W{};
+    W.total = total;
+    KM_TRY(check_ws(W, workspace, workspace_bytes));
+    KM_HIP(launch_optimal_1d((DType)xt, x, weights, B, N, K, centroids, labels, counts, objective, workspace,
+                             (hipStream_t)stream),
+           "optimal_1d");
+    return KM_OK;
+}
+
 const char* kmeans_status_str(km_status st) {
     switch (st) {
         case KM_OK: return "ok";

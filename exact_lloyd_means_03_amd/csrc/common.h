@@ -137,4 +137,14 @@ hipError_t launch_update_1d_row(DType xt, const void* x, const float* w, int64_t
                                 const int32_t* labels, int64_t K, const float* c_old,
                                 float* c_new, int32_t* counts, hipStream_t s);
 
+// Globally optimal 1D k-means (one block per row).
+constexpr int kOpt1DMaxN = 4096;  // points per row
+constexpr int kOpt1DMaxK = 256;   // runs per row
+bool optimal_1d_supports(int64_t N, int64_t K);
+void optimal_1d_workspace(int64_t B, int64_t N, int64_t K, size_t* d_off, size_t* cut_off, size_t* perm_off,
+                          size_t* total);
+hipError_t launch_optimal_1d(DType xt, const void* x, const float* w, int64_t B, int64_t N, int64_t K,
+                             float* centroids, int32_t* labels, int32_t* counts, double* objective, void* ws,
+                             hipStream_t s);
+
 }  // namespace km

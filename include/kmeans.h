@@ -136,6 +136,30 @@ KM_API km_status kmeans_fit(const void *x, km_dtype xt, const float *weights,
                      float *centroids, int32_t *labels, int32_t *counts, double *objective,
                      void *workspace, size_t workspace_bytes, km_stream stream);
 
+/* Globally optimal weighted 1D k-means of every row (github LeanModels/
+ * LeanQuant issue #1 "1D k-means": for scalar data the globally optimal
+ * centroids can be found; the issue's diff calls such a weighted 1D
+ * clustering in place of Lloyd).  Among all partitions of a row's points
+ * into K non-empty groups, one with the least sum_i w_i (x_i - mean_g(i))^2,
+ * found exactly (up to float64 rounding) over the cuts of the sorted row
+ * into K runs.
+ *   x          [B,N] (or [B,N,1]) points of dtype xt.
+ *   weights    [B,N] float32 or NULL (all 1); must be positive.
+ *   centroids  out [B,K] float32: the runs' weighted means, ascending.
+ *   labels     out [B,N] int32 or NULL: the run of every point (0 .. K-1).
+ *   counts     out [B,K] int32 or NULL: points per run.
+ *   objective  out [B] float64 or NULL: the least cost J*.
+ * Needs 1 <= K <= N (KM_EINVAL otherwise); supports N <= 4096 and K <= 256
+ * (KM_EUNSUPPORTED beyond).  Equal values may be split between runs only
+ * where that does not change J*; ties between cuts go to the earliest cut
+ * in (value, index) order, up to float64 rounding.  The workspace must hold
+ * kmeans_optimal_1d_workspace_bytes(B, N, K) bytes, 256-byte aligned. */
+KM_API size_t kmeans_optimal_1d_workspace_bytes(int64_t B, int64_t N, int64_t K);
+KM_API km_status kmeans_optimal_1d(const void *x, km_dtype xt, const float *weights,
+                            int64_t B, int64_t N, int64_t K,
+                            float *centroids, int32_t *labels, int32_t *counts, double *objective,
+                            void *workspace, size_t workspace_bytes, km_stream stream);
+
 /* Static description of a status code. */
 KM_API const char *kmeans_status_str(km_status status);
 

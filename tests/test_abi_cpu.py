@@ -19,7 +19,7 @@ def lib():
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "kmeans.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kmeans_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kmeans_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -99,3 +99,30 @@ def test_python_binding_requires_gpu_tensors():
     x = torch.zeros(1, 10, 8)
     with pytest.raises(ValueError, match="GPU"):
         km.kmeans_assign(x, torch.zeros(1, 4, 8))
+
+
+def test_optimal_1d_rejects(lib):
+    ws = C.c_void_p(0x100000)
+    n = lib.kmeans_optimal_1d_workspace_bytes(4096, 4096, 16)
+    # D per row, the cuts of every layer (uint16) and the sort permutation
+    assert n >= 4096 * (4097 * 8 + 16 * 4097 * 2 + 4096 * 4) and n % 256 == 0
+    assert lib.kmeans_optimal_1d_workspace_bytes(1, 4097, 16) == 0   # N above the limit
+    assert lib.kmeans_optimal_1d_workspace_bytes(1, 10, 11) == 0     # K > N
+    assert lib.kmeans_optimal_1d_workspace_bytes(1, 4000, 257) == 0  # K above the limit
+
+    def call(**kw):
+        a = dict(x=FAKE, xt=0, w=None, B=2, N=100, K=4, C=FAKE, ws=ws, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.kmeans_optimal_1d(a["x"], a["xt"], a["w"], a["B"], a["N"], a["K"], a["C"], None, None, None,
+                                     a["ws"], a["ws_bytes"], None)
+
+    assert call(K=0) == 1
+    assert call(K=101) == 1 and b"K <= N" in lib.kmeans_last_error()
+    assert call(N=5000, K=4) == 2
+    assert call(N=1000, K=300) == 2
+    assert call(xt=9) == 2
+    assert call(x=None) == 1
+    assert call(C=None) == 1
+    assert call(ws_bytes=100) == 3
+    assert call(ws=C.c_void_p(0x100010)) == 1
+    assert call(N=-1) == 1
