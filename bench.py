@@ -144,7 +144,7 @@ def bench_fit_1d(args, km, wl, p, x, w, C):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    km.kmeans_fit(x, init, args.steps, weights=w)
+    _, _, _, J_lloyd = km.kmeans_fit(x, init, args.steps, weights=w)
     e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -174,6 +174,8 @@ def bench_fit_1d(args, km, wl, p, x, w, C):
         "cpu_baseline": None,
     }
     out["steps_1d"] = bench_steps_1d(km, wl, x, w, C)
+    if N <= 4096:
+        out["optimal_1d"] = bench_optimal_1d(km, wl, x, w, J_lloyd[:, -1])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -227,6 +229,31 @@ def bench_steps_1d(km, wl, x, w, C, reps: int = 10) -> dict:
         gbs = nb / (ms * 1e-3) / 1e9
         out[name] = {"avg_ms": ms, "algorithmic_bytes": nb, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
     return out
+
+
+def bench_optimal_1d(km, wl, x, w, J_lloyd, reps: int = 3) -> dict:
+    """The globally optimal 1D clustering of the same rows (kmeans_optimal_1d,
+    one launch): device time per call, and its objective next to the Lloyd
+    fit's last objective from the same rows."""
+    import torch
+
+    B, N, K = wl.B, wl.N, wl.K
+    L = km.load()
+    ws = torch.empty(max(int(L.kmeans_optimal_1d_workspace_bytes(B, N, K)), 256), dtype=torch.uint8,
+                     device=x.device)
+    cen = torch.empty((B, K), dtype=torch.float32, device=x.device)
+    lab = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    cnt = torch.empty((B, K), dtype=torch.int32, device=x.device)
+    J = torch.empty((B,), dtype=torch.float64, device=x.device)
+
+    def run():
+        km.kmeans_optimal_1d(x, K, weights=w, centroids=cen, labels=lab, counts=cnt, objective=J, ws=ws)
+
+    run()
+    ms = _device_ms(run, reps)
+    Jm, Jl = float(J.mean()), float(J_lloyd.mean())
+    return {"kernel": "k_optimal_1d", "avg_ms": ms, "rows_per_s": B / (ms * 1e-3), "J_mean": Jm,
+            "lloyd_J_mean": Jl, "J_over_lloyd": Jm / Jl}
 
 
 def main():
