@@ -31,7 +31,12 @@
 //     each;
 //   * the two half-waves that share a point merge at the end by (value, then
 //     smaller index);
-//   * padding centroids (K..Kp-1) start at -inf and never win.
+//   * padding centroids (K..Kp-1) start at -inf and never win;
+//   * persistent blocks: the grid holds as many blocks as the device runs at
+//     once, and each walks groups of points i, i + grid, ...; the tile
+//     pipeline runs on from one group into the next (the next group's first
+//     tile loads during the current group's last tile), which matters when
+//     K is small and a group walks few tiles.
 #include "common.h"
 
 namespace km {
@@ -193,7 +198,7 @@ template <typename T, int DP, bool VEC>
 __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfma(
     const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int64_t ntiles,
     const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
-    double* __restrict__ obj_part) {
+    double* __restrict__ obj_part, int64_t gpb, int64_t ngroups) {
     typedef AssignCfg<T, DP> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
@@ -204,8 +209,10 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
-    const int64_t b = blockIdx.y;
-    const T* Xb = X + b * N * (int64_t)d;
+    // groups of PTS points, g = b * gpb + pg; block i takes groups i, i + gridDim.x, ...
+    int64_t g = blockIdx.x;
+    if (g >= ngroups) return;
+    int64_t b = g / gpb, pg = g % gpb;
     const char* Bb = blob + b * ntiles * (int64_t)Cfg::TILE;
 
     // per-lane DMA source offsets (the same for every tile)
@@ -214,38 +221,40 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
     for (int n = 0; n < Cfg::NIW; ++n) voff[n] = dma_src<T, DP>(n * Cfg::WAVES + wave, lane);
     // start the first tile's DMA before the point loads
     dma_tile<T, DP>(Bb, s_tile[0], wave, lane, voff);
+    int par = 0;  // the buffer that holds a group's first tile
 
     // ---- points of this wave: B operand fragments + squared norms -------
     F bx[NCB][KSTEPS];
     float xx[NCB];
-    int64_t pidx[NCB];
+    auto load_points = [&](int64_t bb, int64_t pgg) {
+        const T* Xb = X + bb * N * (int64_t)d;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int64_t p = (int64_t)blockIdx.x * Cfg::PTS + (wave * NCB + cb) * 32 + col;
-        pidx[cb] = p;
-        const bool valid = p < N;
-        const T* row = Xb + (valid ? p : 0) * (int64_t)d;
-        float s = 0.f;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int64_t p = pgg * Cfg::PTS + (wave * NCB + cb) * 32 + col;
+            const bool valid = p < N;
+            const T* row = Xb + (valid ? p : 0) * (int64_t)d;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            bx[cb][ks] = load_point_frag<T, VEC>(row, ks * M::KS + half * M::EPL, d, valid);
-            s += frag_sq<T>(bx[cb][ks]);
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                bx[cb][ks] = load_point_frag<T, VEC>(row, ks * M::KS + half * M::EPL, d, valid);
         }
-        xx[cb] = s + __shfl_xor(s, 32, 64);
-    }
+    };
+    auto point_norms = [&]() {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            float s = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) s += frag_sq<T>(bx[cb][ks]);
+            xx[cb] = s + __shfl_xor(s, 32, 64);
+        }
+    };
+    load_points(b, pg);
+    point_norms();
 
     // running best per point: value, 32-row block that holds it, and that
     // block's 16 values of this lane (to recover the row at the end)
     float best[NCB];
     int32_t bblk[NCB];
     f32x16 saved[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        best[cb] = -INFINITY;
-        bblk[cb] = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) saved[cb][r] = -INFINITY;
-    }
 
     // per-lane byte offsets of the A operand in a tile (row col of block 0)
     int aoff[KSTEPS];
@@ -357,76 +366,109 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
         for (int pc = 0; pc < 8; ++pc) epi_piece(pc, v, blk);
     };
 
-    // wait for tile 0, then make it visible
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-
-    // Software pipeline over 32-row blocks (acc0 / acc1 alternate).  The loop
-    // body is one basic block: every iteration issues the DMA of tile t + 1
-    // (past the end it re-reads the last tile into the buffer no one reads),
-    // so the vmcnt bookkeeping is the same on every iteration.
-    f32x16 acc0[NCB], acc1[NCB];
+    for (;;) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb) {
+            best[cb] = -INFINITY;
+            bblk[cb] = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc1[cb][r] = -INFINITY;
-    int32_t blk1 = 0;
-    for (int64_t t = 0; t < ntiles; ++t) {
-        const char* tile = s_tile[t & 1];
-        F a0 = lda_at(tile, 0, 0);
-        F a1 = KSTEPS > 1 ? lda_at(tile, 0, 1) : lda_at(tile, 1, 0);
-        f32x16 h = ldh_at(tile, 0);
-        const int64_t tn = (t + 1 < ntiles) ? t + 1 : ntiles - 1;
-        dma_tile<T, DP>(Bb + tn * (int64_t)Cfg::TILE, s_tile[(t + 1) & 1], wave, lane, voff);
-#pragma unroll
-        for (int rb = 0; rb < NRB; rb += 2) {
-            const int32_t blk0 = (int32_t)(t * NRB) + rb;
-            mma_block(tile, rb, acc0, acc1, blk1, a0, a1, h);
-            mma_block(tile, rb + 1, acc1, acc0, blk0, a0, a1, h);
-            blk1 = blk0 + 1;
+            for (int r = 0; r < 16; ++r) saved[cb][r] = -INFINITY;
         }
-        // tile t+1 must have landed before the barrier that publishes it
+        // wait for the group's first tile, then make it visible
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
+
+        // the next group of this block: its first tile is loaded during this
+        // group's last tile, its points while this group's outputs are written
+        const int64_t gn = g + gridDim.x;
+        const bool has_next = gn < ngroups;
+        const int64_t bn = has_next ? gn / gpb : b;
+        const char* Bn = blob + bn * ntiles * (int64_t)Cfg::TILE;
+
+        // Software pipeline over 32-row blocks (acc0 / acc1 alternate).  The loop
+        // body is one basic block: every iteration issues one tile DMA (the next
+        // tile, the next group's first tile, or past the end a re-read of the
+        // last tile into the buffer no one reads), so the vmcnt bookkeeping is
+        // the same on every iteration.
+        f32x16 acc0[NCB], acc1[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc1[cb][r] = -INFINITY;
+        int32_t blk1 = 0;
+        for (int64_t t = 0; t < ntiles; ++t) {
+            const char* tile = s_tile[(par + t) & 1];
+            F a0 = lda_at(tile, 0, 0);
+            F a1 = KSTEPS > 1 ? lda_at(tile, 0, 1) : lda_at(tile, 1, 0);
+            f32x16 h = ldh_at(tile, 0);
+            const char* src = t + 1 < ntiles ? Bb + (t + 1) * (int64_t)Cfg::TILE
+                              : has_next     ? Bn
+                                             : Bb + t * (int64_t)Cfg::TILE;
+            dma_tile<T, DP>(src, s_tile[(par + t + 1) & 1], wave, lane, voff);
+#pragma unroll
+            for (int rb = 0; rb < NRB; rb += 2) {
+                const int32_t blk0 = (int32_t)(t * NRB) + rb;
+                mma_block(tile, rb, acc0, acc1, blk1, a0, a1, h);
+                mma_block(tile, rb + 1, acc1, acc0, blk0, a0, a1, h);
+                blk1 = blk0 + 1;
+            }
+            // tile t+1 must have landed before the barrier that publishes it
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();
+        }
+        par = (int)((par + ntiles) & 1);
+        epilogue(acc1, blk1);
+
+        // ---- recover the row, merge the two half-waves that share a point ----
+        int32_t bidx[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            int rs = 15;
+#pragma unroll
+            for (int r = 15; r >= 0; --r) rs = (saved[cb][r] == best[cb]) ? r : rs;  // first (smallest) row
+            bidx[cb] = bblk[cb] * 32 + 8 * (rs >> 2) + 4 * half + (rs & 3);
+            const float ob = __shfl_xor(best[cb], 32, 64);
+            const int32_t oi = __shfl_xor(bidx[cb], 32, 64);
+            if (ob > best[cb] || (ob == best[cb] && oi < bidx[cb])) {
+                best[cb] = ob;
+                bidx[cb] = oi;
+            }
+        }
+        // the next group's points load while this group's outputs are written
+        // (xx keeps this group's norms until then)
+        if (has_next) load_points(bn, gn % gpb);
+        double obj = 0.0;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int64_t p = pg * Cfg::PTS + (wave * NCB + cb) * 32 + col;
+            if (half == 0 && p < N) {
+                const float dist = fmaxf(xx[cb] - 2.f * best[cb], 0.f);
+                labels[b * N + p] = bidx[cb];
+                if (min_dist) min_dist[b * N + p] = dist;
+                obj += (double)(w ? w[b * N + p] : 1.f) * (double)dist;
+            }
+        }
+        if (obj_part) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) obj += __shfl_xor(obj, o, 64);
+            if (lane == 0) s_obj[wave] = obj;
+            __syncthreads();
+            if (tid == 0) {
+                double s = 0.0;
+#pragma unroll
+                for (int i = 0; i < Cfg::WAVES; ++i) s += s_obj[i];
+                obj_part[b * gpb + pg] = s;
+            }
+        }
+        if (!has_next) break;
+        g = gn;
+        b = bn;
+        pg = gn % gpb;
+        Bb = Bn;
+        point_norms();
     }
     // no DMA may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    epilogue(acc1, blk1);
-
-    // ---- recover the row, merge the two half-waves that share a point ----
-    double obj = 0.0;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        int rs = 15;
-#pragma unroll
-        for (int r = 15; r >= 0; --r) rs = (saved[cb][r] == best[cb]) ? r : rs;  // first (smallest) row
-        int32_t bidx = bblk[cb] * 32 + 8 * (rs >> 2) + 4 * half + (rs & 3);
-        const float ob = __shfl_xor(best[cb], 32, 64);
-        const int32_t oi = __shfl_xor(bidx, 32, 64);
-        if (ob > best[cb] || (ob == best[cb] && oi < bidx)) {
-            best[cb] = ob;
-            bidx = oi;
-        }
-        const int64_t p = pidx[cb];
-        if (half == 0 && p < N) {
-            const float dist = fmaxf(xx[cb] - 2.f * best[cb], 0.f);
-            labels[b * N + p] = bidx;
-            if (min_dist) min_dist[b * N + p] = dist;
-            obj += (double)(w ? w[b * N + p] : 1.f) * (double)dist;
-        }
-    }
-    if (obj_part) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) obj += __shfl_xor(obj, o, 64);
-        if (lane == 0) s_obj[wave] = obj;
-        __syncthreads();
-        if (tid == 0) {
-            double s = 0.0;
-#pragma unroll
-            for (int i = 0; i < Cfg::WAVES; ++i) s += s_obj[i];
-            obj_part[b * gridDim.x + blockIdx.x] = s;
-        }
-    }
 }
 
 template <typename T>
@@ -452,18 +494,38 @@ int64_t assign_mfma_blocks(int64_t N, int DP, DType xt) {
     return blocks_for<bf16_t>(N, DP);
 }
 
+// Persistent blocks: as many as the device holds at once (compute units x
+// resident blocks per unit), each walking groups i, i + grid, ...
+template <typename T, int DP, bool VEC>
+static int64_t resident_blocks() {
+    static int64_t n = 0;
+    if (n == 0) {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC>,
+                                                         64 * AssignCfg<T, DP>::WAVES, 0) != hipSuccess ||
+            cus <= 0 || per <= 0)
+            return 256;
+        n = (int64_t)cus * per;
+    }
+    return n;
+}
+
 template <typename T, int DP>
 static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
                            double* obj_part, int64_t nblk, hipStream_t s) {
-    dim3 grid((unsigned)nblk, (unsigned)B);
+    const int64_t ngroups = B * nblk;
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
+    const int64_t P = vec ? resident_blocks<T, DP, true>() : resident_blocks<T, DP, false>();
+    dim3 grid((unsigned)(ngroups < P ? ngroups : P));
     if (vec)
         hipLaunchKernelGGL((k_assign_mfma<T, DP, true>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s, (const T*)x, N, d,
-                           (const char*)blob, ntiles, w, labels, min_dist, obj_part);
+                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
     else
         hipLaunchKernelGGL((k_assign_mfma<T, DP, false>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s, (const T*)x, N, d,
-                           (const char*)blob, ntiles, w, labels, min_dist, obj_part);
+                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
     return hipGetLastError();
 }
 
