@@ -23,6 +23,9 @@ SIGNATURES = {
     "kmeans_sort_labels": (C.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "kmeans_update": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _sz, _p]),
     "kmeans_fit": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "kmeans_stream_workspace_bytes": (_sz, [_i64, _i64, _i64, C.c_int, _i64]),
+    "kmeans_fit_stream": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p, _sz,
+                                    _p]),
     "kmeans_optimal_1d_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "kmeans_optimal_1d": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p]),
     "kmeans_status_str": (C.c_char_p, [C.c_int]),

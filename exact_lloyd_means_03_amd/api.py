@@ -193,3 +193,55 @@ def kmeans_optimal_1d(x, K: int, weights=None, centroids=None, labels=None, coun
                              _ptr(counts), _ptr(objective), _ptr(ws), ws.numel(), _stream(dev))
     _lib.check(st, "kmeans_optimal_1d")
     return centroids, labels, counts, objective
+
+
+def kmeans_fit_stream(x_host, init, n_iter: int, weights=None, chunk: int = 1 << 22, centroids=None, labels=None,
+                      counts=None, objective=None, ws=None):
+    """n_iter Lloyd iterations of one problem whose points x_host [N, d] (or
+    [1, N, d]) stay in host memory (a CPU tensor, ideally pinned), streamed
+    to the GPU in chunks of `chunk` points.  init [K, d] (or [1, K, d])
+    float32 on the GPU.  Returns (centroids [K, d], labels [N] (None unless
+    True or a tensor is passed), counts [K], objective [n_iter] float64)."""
+    if not isinstance(x_host, torch.Tensor) or x_host.is_cuda:
+        raise ValueError("x_host must be a CPU tensor")
+    if not x_host.is_contiguous():
+        raise ValueError("x_host must be contiguous")
+    if x_host.dim() == 3 and x_host.shape[0] == 1:
+        x_host = x_host[0]
+    if x_host.dim() != 2:
+        raise ValueError("x_host must be [N, d]")
+    if x_host.dtype not in _DT:
+        raise TypeError(f"x dtype {x_host.dtype} is not float32 / float16 / bfloat16")
+    N, d = x_host.shape
+    _dev_tensor(init, "init", torch.float32)
+    if init.dim() == 3 and init.shape[0] == 1:
+        init = init[0]
+    if init.dim() != 2 or init.shape[1] != d:
+        raise ValueError("init must be [K, d] float32")
+    K = init.shape[0]
+    dev = init.device
+    if weights is not None:
+        if not isinstance(weights, torch.Tensor) or weights.is_cuda or weights.dtype != torch.float32 \
+                or tuple(weights.shape) != (N,) or not weights.is_contiguous():
+            raise ValueError("weights must be a contiguous float32 CPU tensor [N]")
+    centroids = torch.empty_like(init) if centroids is None else \
+        _dev_tensor(centroids, "centroids", torch.float32, init.shape)
+    if labels is True:
+        labels = torch.empty((N,), dtype=torch.int32, device=dev)
+    elif labels is not None:
+        _dev_tensor(labels, "labels", torch.int32, (N,))
+    counts = torch.empty((K,), dtype=torch.int32, device=dev) if counts is None else \
+        _dev_tensor(counts, "counts", torch.int32, (K,))
+    objective = torch.empty((max(n_iter, 0),), dtype=torch.float64, device=dev) if objective is None else \
+        _dev_tensor(objective, "objective", torch.float64, (n_iter,))
+    L = _lib.load()
+    if ws is None:
+        # 0 for arguments the entry point rejects: it then reports why
+        n = L.kmeans_stream_workspace_bytes(N, d, K, _DT[x_host.dtype], chunk)
+        ws = torch.empty(max(int(n), 256), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "workspace", torch.uint8)
+    st = L.kmeans_fit_stream(_ptr(x_host), _DT[x_host.dtype], _ptr(weights), N, d, K, _ptr(init), int(n_iter),
+                             _ptr(centroids), _ptr(labels), _ptr(counts), _ptr(objective), int(chunk), _ptr(ws),
+                             ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_fit_stream")
+    return centroids, labels, counts, objective

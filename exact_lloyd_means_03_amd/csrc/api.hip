@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "../../include/kmeans.h"
@@ -203,6 +205,76 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
     return KM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Fits of one problem whose points stay in host memory (technologypulse.uk
+// "Flash-KMeans" article, performance section: out-of-core runs in which a
+// chunked stream overlap hides the PCIe transfers; wispaper.ai blog,
+// performance: up to a billion points by overlapping CPU-to-GPU copies with
+// computation).  Every iteration streams the points through two device
+// buffers: chunk g is copied on a copy stream while chunk g - 1 is assigned
+// and reduced on the caller's stream; sums, weight sums and counts
+// accumulate over the chunks and the divide closes the iteration.
+
+constexpr int64_t kStreamAlign = 4096;  // chunk sizes: a multiple of every assignment group size
+
+struct StreamPlan {
+    Workspace chunk;  // the per-chunk plan (B = 1, N = chunk points)
+    int64_t chunk_n = 0, nchunks = 0, nblk_chunk = 0, nblk_total = 0;
+    size_t xbuf[2] = {0, 0}, wbuf[2] = {0, 0}, obj_all = 0, counts_total = 0, total = 0;
+};
+
+StreamPlan plan_stream(int64_t N, int64_t d, int64_t K, DType xt, int64_t chunk) {
+    StreamPlan p;
+    int64_t c = (chunk + kStreamAlign - 1) / kStreamAlign * kStreamAlign;
+    if (c > N) c = N;
+    if (c < 1) c = 1;
+    p.chunk_n = c;
+    p.nchunks = N > 0 ? (N + c - 1) / c : 0;
+    p.chunk = plan_workspace(1, c, d, K, xt);
+    p.nblk_chunk = p.chunk.nblk_assign;
+    const int64_t last = N - (p.nchunks > 0 ? (p.nchunks - 1) * c : 0);
+    const int64_t nblk_last = p.nchunks > 0 ? assign_mfma_blocks(last, p.chunk.DP, xt) : 0;
+    p.nblk_total = p.nchunks > 0 ? (p.nchunks - 1) * p.nblk_chunk + nblk_last : 1;
+    size_t off = p.chunk.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    for (int i = 0; i < 2; ++i) p.xbuf[i] = take((size_t)c * d * dtype_bytes(xt));
+    for (int i = 0; i < 2; ++i) p.wbuf[i] = take((size_t)c * sizeof(float));
+    p.obj_all = take((size_t)p.nblk_total * sizeof(double));
+    p.counts_total = take((size_t)K * sizeof(int32_t));
+    p.total = off;
+    return p;
+}
+
+// The copy stream of a device and the events that order its copies against
+// the caller's stream (created once per device, default priority).  Calls on
+// one device take the lock for as long as they enqueue work.
+struct StreamRes {
+    hipStream_t copy = nullptr;
+    hipEvent_t copied[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr}, start = nullptr;
+};
+std::mutex g_stream_mu;
+std::map<int, StreamRes> g_stream_res;
+
+hipError_t stream_res(int dev, StreamRes** out) {
+    auto it = g_stream_res.find(dev);
+    if (it != g_stream_res.end()) {
+        *out = &it->second;
+        return hipSuccess;
+    }
+    StreamRes r;
+    hipError_t e = hipStreamCreateWithFlags(&r.copy, hipStreamNonBlocking);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&r.consumed[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r.start, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    *out = &(g_stream_res[dev] = r);
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,6 +395,102 @@ km_status kmeans_optimal_1d(const void* x, km_dtype xt, const float* weights, in
     KM_HIP(launch_optimal_1d((DType)xt, x, weights, B, N, K, centroids, labels, counts, objective, workspace,
                              (hipStream_t)stream),
            "optimal_1d");
+    return KM_OK;
+}
+
+size_t kmeans_stream_workspace_bytes(int64_t N, int64_t d, int64_t K, km_dtype xt, int64_t chunk) {
+    if (check_shape(1, N, d, K, (int)xt) != KM_OK || d < 2 || chunk < 1) return 0;
+    return plan_stream(N, d, K, (DType)xt, chunk).total;
+}
+
+km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host, int64_t N, int64_t d, int64_t K,
+                            const float* init, int32_t n_iter, float* centroids, int32_t* labels, int32_t* counts,
+                            double* objective, int64_t chunk, void* workspace, size_t workspace_bytes,
+                            km_stream stream) {
+    KM_TRY(check_shape(1, N, d, K, (int)xt));
+    if (d < 2) return fail(KM_EUNSUPPORTED, "streamed fits need d >= 2 (d=%lld)", (long long)d);
+    if (n_iter < 0) return fail(KM_EINVAL, "n_iter=%d < 0", n_iter);
+    if (chunk < 1) return fail(KM_EINVAL, "chunk=%lld < 1", (long long)chunk);
+    KM_TRY(need(x_host, N, "x_host"));
+    KM_TRY(need(init, 1, "init"));
+    KM_TRY(need(centroids, 1, "centroids"));
+    const DType t = (DType)xt;
+    const StreamPlan P = plan_stream(N, d, K, t, chunk);
+    {
+        Workspace W{};
+        W.total = P.total;
+        KM_TRY(check_ws(W, workspace, workspace_bytes));
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const size_t cbytes = (size_t)K * d * sizeof(float);
+    if (init != centroids) KM_HIP(hipMemcpyAsync(centroids, init, cbytes, hipMemcpyDeviceToDevice, s), "copy init");
+    if (n_iter == 0) return KM_OK;
+    if (N == 0) {
+        if (objective) KM_HIP(launch_zero(objective, (size_t)n_iter * sizeof(double), s), "zero");
+        if (counts) KM_HIP(launch_zero(counts, (size_t)K * sizeof(int32_t), s), "zero");
+        return KM_OK;
+    }
+    int dev = 0;
+    KM_HIP(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_stream_mu);
+    StreamRes* R = nullptr;
+    KM_HIP(stream_res(dev, &R), "copy stream");
+    const Workspace& W = P.chunk;
+    char* ws = (char*)workspace;
+    const int64_t c = P.chunk_n, es = dtype_bytes(t);
+    float* sums = at<float>(ws, W.sums);
+    float* wsum = w_host ? at<float>(ws, W.wsum) : nullptr;
+    int32_t* ctot = at<int32_t>(ws, P.counts_total);
+    double* obj_all = at<double>(ws, P.obj_all);
+    // the first copies must not overwrite buffers that earlier work on the
+    // caller's stream may still read
+    KM_HIP(hipEventRecord(R->start, s), "event");
+    KM_HIP(hipStreamWaitEvent(R->copy, R->start, 0), "event wait");
+    int64_t g = 0;  // chunk counter over all iterations: buffer g % 2
+    for (int32_t it = 0; it < n_iter; ++it) {
+        KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, at<void>(ws, W.chat), s), "prep");
+        // sums and wsum are adjacent in the plan: clear both with one fill
+        KM_HIP(launch_zero(sums, W.offsets - W.sums, s), "zero");
+        KM_HIP(launch_zero(ctot, (size_t)K * sizeof(int32_t), s), "zero");
+        for (int64_t ci = 0; ci < P.nchunks; ++ci, ++g) {
+            const int buf = (int)(g & 1);
+            const int64_t p0 = ci * c, nc = (p0 + c <= N) ? c : N - p0;
+            void* xb = at<void>(ws, P.xbuf[buf]);
+            float* wb = w_host ? at<float>(ws, P.wbuf[buf]) : nullptr;
+            if (g >= 2) KM_HIP(hipStreamWaitEvent(R->copy, R->consumed[buf], 0), "event wait");
+            KM_HIP(hipMemcpyAsync(xb, (const char*)x_host + p0 * d * es, (size_t)(nc * d * es),
+                                  hipMemcpyHostToDevice, R->copy),
+                   "copy points");
+            if (w_host)
+                KM_HIP(hipMemcpyAsync(wb, w_host + p0, (size_t)nc * sizeof(float), hipMemcpyHostToDevice, R->copy),
+                       "copy weights");
+            KM_HIP(hipEventRecord(R->copied[buf], R->copy), "event");
+            KM_HIP(hipStreamWaitEvent(s, R->copied[buf], 0), "event wait");
+            int32_t* lab = labels ? labels + p0 : at<int32_t>(ws, W.labels);
+            KM_HIP(launch_assign_mfma(t, xb, 1, nc, (int)d, W.DP, at<void>(ws, W.chat), W.Kp, wb, lab, nullptr,
+                                      obj_all + ci * P.nblk_chunk, assign_mfma_blocks(nc, W.DP, t), s),
+                   "assign_mfma");
+            int32_t* cnt = at<int32_t>(ws, W.counts);
+            int32_t* offsets = at<int32_t>(ws, W.offsets);
+            int32_t* perm = at<int32_t>(ws, W.perm);
+            int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
+            KM_HIP(launch_zero(cnt, (size_t)K * sizeof(int32_t), s), "zero");
+            // every chunk uses the piece width of a full chunk, so a shorter
+            // last chunk never has more pieces than the plan holds
+            const int TW = segreduce_tw(1, c);
+            KM_HIP(launch_sort(lab, 1, nc, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (nc + TW - 1) / TW,
+                               piece_seg, s),
+                   "sort");
+            KM_HIP(launch_segreduce_tw(t, xb, wb, 1, nc, (int)d, perm, offsets, K, sums, wsum, piece_seg,
+                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, s),
+                   "segreduce");
+            KM_HIP(launch_add_i32(ctot, cnt, K, s), "add counts");
+            KM_HIP(hipEventRecord(R->consumed[buf], s), "event");
+        }
+        if (objective) KM_HIP(launch_obj_reduce(obj_all, 1, P.nblk_total, objective + it, 1, s), "obj_reduce");
+        KM_HIP(launch_divide(sums, wsum, ctot, 1, K, (int)d, centroids, centroids, s), "divide");
+    }
+    if (counts) KM_HIP(hipMemcpyAsync(counts, ctot, (size_t)K * sizeof(int32_t), hipMemcpyDeviceToDevice, s), "copy");
     return KM_OK;
 }
 

@@ -107,6 +107,8 @@ hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double
                              int64_t out_stride, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// dst[i] += src[i], i < n.
+hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 
 // piece_seg may be NULL (then TW and npieces are ignored).
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
@@ -117,6 +119,11 @@ hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, 
                             const int32_t* perm, const int32_t* offsets, int64_t K,
                             float* sums, float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
                             hipStream_t s);
+// The same with a given piece width TW (the sort must have used the same).
+hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
+                               const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
+                               float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
+                               hipStream_t s);
 int64_t segreduce_pieces(int64_t B, int64_t N);
 int segreduce_tw(int64_t B, int64_t N);
 

@@ -153,6 +153,18 @@ hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_add_i32(int32_t* __restrict__ dst, const int32_t* __restrict__ src,
+                                                 int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] += src[i];
+}
+
+hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_add_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ p, int64_t n_words) {
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * 256;

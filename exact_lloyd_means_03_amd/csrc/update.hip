@@ -316,8 +316,15 @@ int segreduce_tw(int64_t B, int64_t N) {
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                             float* wsum, const int32_t* piece_seg, float* slot, float* wslot, hipStream_t s) {
+    return launch_segreduce_tw(xt, x, w, B, N, d, perm, offsets, K, sums, wsum, piece_seg, slot, wslot,
+                               segreduce_tw(B, N), s);
+}
+
+hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
+                               const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
+                               float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
+                               hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
-    const int TW = segreduce_tw(B, N);
     const int64_t npieces = (N + TW - 1) / TW;
     const int esz = dtype_bytes(xt);
     const int epl = 16 / esz;

@@ -136,6 +136,36 @@ KM_API km_status kmeans_fit(const void *x, km_dtype xt, const float *weights,
                      float *centroids, int32_t *labels, int32_t *counts, double *objective,
                      void *workspace, size_t workspace_bytes, km_stream stream);
 
+/* Lloyd fit of one problem whose points stay in host memory
+ * (technologypulse.uk "Flash-KMeans" article, performance section:
+ * out-of-core runs in which a chunked stream overlap hides the PCIe
+ * transfers; wispaper.ai blog, performance: CPU-to-GPU copies overlapped
+ * with computation).  Every iteration copies the points chunk by chunk into
+ * two device buffers on a copy stream the library keeps per device, while
+ * the previous chunk is assigned and reduced on `stream`; sums, weight sums
+ * and counts accumulate over the chunks, then the divide.  The result is
+ * that of kmeans_fit on the same points up to fp32 summation order.
+ *   x_host     [N,d] points of dtype xt in host memory.  Pinned memory (e.g.
+ *              hipHostMalloc) lets the copies overlap the kernels; pageable
+ *              memory works, staged by the runtime.  It must stay valid and
+ *              unchanged until the work on `stream` completes.
+ *   w_host     [N] float32 in host memory, or NULL (same lifetime).
+ *   init       [K,d] float32 device (may alias centroids).
+ *   centroids  out [K,d] float32 device.
+ *   labels     out [N] int32 device or NULL: the last assignment.
+ *   counts     out [K] int32 device or NULL: the last update.
+ *   objective  out [n_iter] float64 device or NULL.
+ *   chunk      points per copy, rounded up to a multiple of 4096 (at most N).
+ * One problem (B = 1) with d >= 2 (KM_EUNSUPPORTED for d = 1).  The
+ * workspace must hold kmeans_stream_workspace_bytes(N, d, K, xt, chunk)
+ * bytes, 256-byte aligned.  Calls on one device enqueue their work one at a
+ * time (they share the device's copy stream). */
+KM_API size_t kmeans_stream_workspace_bytes(int64_t N, int64_t d, int64_t K, km_dtype xt, int64_t chunk);
+KM_API km_status kmeans_fit_stream(const void *x_host, km_dtype xt, const float *w_host,
+                            int64_t N, int64_t d, int64_t K, const float *init, int32_t n_iter,
+                            float *centroids, int32_t *labels, int32_t *counts, double *objective,
+                            int64_t chunk, void *workspace, size_t workspace_bytes, km_stream stream);
+
 /* Globally optimal weighted 1D k-means of every row (github LeanModels/
  * LeanQuant issue #1 "1D k-means": for scalar data the globally optimal
  * centroids can be found; the issue's diff calls such a weighted 1D

@@ -126,3 +126,26 @@ def test_optimal_1d_rejects(lib):
     assert call(ws_bytes=100) == 3
     assert call(ws=C.c_void_p(0x100010)) == 1
     assert call(N=-1) == 1
+
+
+def test_fit_stream_rejects(lib):
+    ws = C.c_void_p(0x100000)
+    assert lib.kmeans_stream_workspace_bytes(1 << 20, 128, 4096, 1, 1 << 18) > 0
+    assert lib.kmeans_stream_workspace_bytes(1000, 1, 4, 1, 4096) == 0      # d = 1
+    assert lib.kmeans_stream_workspace_bytes(1000, 16, 4, 1, 0) == 0        # chunk < 1
+
+    def call(**kw):
+        a = dict(x=FAKE, xt=1, w=None, N=1000, d=16, K=4, init=FAKE, n_iter=2, C=FAKE, chunk=4096, ws=ws,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.kmeans_fit_stream(a["x"], a["xt"], a["w"], a["N"], a["d"], a["K"], a["init"], a["n_iter"],
+                                     a["C"], None, None, None, a["chunk"], a["ws"], a["ws_bytes"], None)
+
+    assert call(d=1) == 2 and b"d >= 2" in lib.kmeans_last_error()
+    assert call(chunk=0) == 1
+    assert call(n_iter=-1) == 1
+    assert call(x=None) == 1
+    assert call(init=None) == 1
+    assert call(ws_bytes=64) == 3
+    assert call(K=0) == 1
+    assert call(xt=4) == 2
