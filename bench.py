@@ -256,6 +256,91 @@ def bench_optimal_1d(km, wl, x, w, J_lloyd, reps: int = 3) -> dict:
             "lloyd_J_mean": Jl, "J_over_lloyd": Jm / Jl}
 
 
+def bench_stream(args, km, wl):
+    """A workload whose points stay in pinned host memory (kmeans_fit_stream):
+    a step is one Lloyd iteration including the host-to-device copy of every
+    point.  The line also gives the bare copy rate, the same fit with the
+    points in device memory, and how much of the shorter of the two the
+    streamed iteration hides."""
+    import torch
+
+    import workloads
+
+    N, d, K = wl.N, wl.d, wl.K
+    chunk = args.chunk
+    x_host, init = workloads.generate_host(wl)
+    nbytes = x_host.numel() * x_host.element_size()
+    # the streamed fit first (a long run before it would leave the chip
+    # hotter): W warmup iterations, then exactly K timed ones
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L = km.load()
+    xt = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+    ws = torch.empty(max(int(L.kmeans_stream_workspace_bytes(N, d, K, xt, chunk)), 256), dtype=torch.uint8,
+                     device="cuda")
+    if args.warmup > 0:
+        km.kmeans_fit_stream(x_host, init, args.warmup, chunk=chunk, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    _, _, _, J = km.kmeans_fit_stream(x_host, init, args.steps, chunk=chunk, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    it_ms = e0.elapsed_time(e1) / args.steps
+    # then the bare copy, and the fit with the points already in device memory
+    x_dev = torch.empty((1, N, d), dtype=x_host.dtype, device="cuda")
+    x_dev[0].copy_(x_host, non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record()
+    x_dev[0].copy_(x_host, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1)
+    ws_dev = km.workspace(1, N, d, K, x_dev.dtype, x_dev.device)
+    km.kmeans_fit(x_dev, init[None], 1, ws=ws_dev)
+    torch.cuda.synchronize()
+    e0.record()
+    km.kmeans_fit(x_dev, init[None], args.steps, ws=ws_dev)
+    e1.record()
+    torch.cuda.synchronize()
+    dev_ms = e0.elapsed_time(e1) / args.steps
+    del x_dev, ws_dev
+    torch.cuda.empty_cache()
+    flops = 2.0 * N * K * d
+    achieved = flops / (it_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    out = {
+        "metric": "out-of-core Lloyd iter/s (points in pinned host memory, host-to-device copies included)",
+        "value": args.steps / elapsed,
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": 1, "N": N, "d": d, "K": K, "point_dtype": wl.dtype, "init": wl.init,
+                   "chunk": chunk, "host_bytes": nbytes},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None, "kernel": "k_assign_mfma (streamed)", "algorithmic_per_launch": flops,
+                     "avg_launch_ms": it_ms},
+        "transfer": {"bytes_per_iter": nbytes, "bare_copy_ms": copy_ms, "GB/s": nbytes / (copy_ms * 1e-3) / 1e9},
+        "device_memory_fit_ms_per_iter": dev_ms,
+        # 1: the streamed iteration takes max(copy, kernels); 0: their sum
+        "hidden": (copy_ms + dev_ms - it_ms) / min(copy_ms, dev_ms),
+        "objective_last": float(J[-1]),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import types
+        p = types.SimpleNamespace(wl=wl, x=x_host[None], w=None, init=init[None].cpu())
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +348,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--chunk", type=int, default=1 << 22, help="points per host-to-device copy (host workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
@@ -291,6 +377,8 @@ def main():
     wl = workloads.WORKLOADS[name]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if wl.host:
+        return bench_stream(args, km, wl)
     p = workloads.generate(wl)
     x = p.x.to(dev)
     w = None if p.w is None else p.w.to(dev)

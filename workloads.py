@@ -61,6 +61,7 @@ class Workload:
     t_scale: float = 0.02   # rows1d: scale of the t draws
     w_lo: float = 0.1       # rows1d: sample weights ~ U(w_lo, w_hi)
     w_hi: float = 1.0
+    host: bool = False      # the points stay in (pinned) host memory: generate_host()
 
     @property
     def components(self) -> int:
@@ -92,6 +93,8 @@ WORKLOADS = {
                  n_iter=30, seed=5, kind="rows1d", init="linspace"),
         Workload("rows1d-b4096-n4096-k8-f32", B=4096, N=4096, d=1, K=8, dtype="f32",
                  n_iter=30, seed=5, kind="rows1d", init="linspace"),
+        Workload("stream-n64m-k32768-d128-f16", B=1, N=1 << 26, d=128, K=32768, dtype="f16",
+                 n_iter=3, seed=6, sigma=0.15, init="random", host=True),
     ]
 }
 
@@ -260,3 +263,25 @@ def raw_bits(x: torch.Tensor) -> np.ndarray:
 
 def dtype_name(x: torch.Tensor) -> str:
     return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype]
+
+
+def generate_host(wl: Workload, chunk: int = 1 << 22):
+    """Points of a host-memory workload, made on the GPU from a seeded generator
+    (numpy would take minutes at this size) and copied into pinned host memory:
+    a Gaussian mixture of wl.components means ~ N(0, 1) with per-coordinate
+    std wl.sigma, components drawn uniformly, stored in wl.dtype.  Returns
+    (x_host [N, d] pinned CPU tensor, init [K, d] float32 on the GPU: K
+    distinct random points)."""
+    assert wl.host and wl.B == 1 and wl.kind == "gmm"
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    means = torch.randn((wl.components, wl.d), generator=g, device="cuda")
+    x = torch.empty((wl.N, wl.d), dtype=_TORCH_DTYPE[wl.dtype], pin_memory=True)
+    for p0 in range(0, wl.N, chunk):
+        n = min(chunk, wl.N - p0)
+        comp = torch.randint(0, wl.components, (n,), generator=g, device="cuda")
+        v = means[comp] + wl.sigma * torch.randn((n, wl.d), generator=g, device="cuda")
+        x[p0:p0 + n].copy_(v.to(_TORCH_DTYPE[wl.dtype]))
+    idx = torch.randperm(wl.N, generator=g, device="cuda")[:wl.K].cpu()
+    init = x[idx].float().cuda()
+    torch.cuda.synchronize()
+    return x, init
