@@ -422,6 +422,128 @@ int oracle_optimal_1d(const double *X, const double *w, int64_t B, int64_t N, in
     return failed ? -1 : 0;
 }
 
+/* ----------------------------------------------------------------------- *
+ * e-means (daily.steinslab.io "e-means" article): mini-batch k-means whose
+ * cluster statistics are exponential moving averages.
+ *   - "Breaking 70 Years of Full-Batch Inertia": each cluster keeps a sum
+ *     S_j and a count N_j, the centroid is their quotient, and every batch
+ *     updates S_j <- (1 - a) S_j + a s_j (s_j the batch's sum of cluster j;
+ *     the same for N_j with the batch count n_j).  After the last epoch the
+ *     centroids move to the plain mean of that epoch's assignments.
+ *   - "Mini-Batch Stochastic Noise...": the step a follows a cosine decay
+ *     from a0 down to 0.1 a0 (floor = 0.1 is the page's; it is a parameter).
+ *   - "Proportional Splitting Resurrects Thousands of Dead Centers": a dead
+ *     cluster takes over half of a live cluster drawn with probability
+ *     proportional to its size, and the two are split apart.
+ * Readings (listed with their reasons in the design notes): batches are
+ * consecutive slices of `batch` points in storage order (the caller fixes
+ * the order); S and N start at zero and a centroid moves only once its N
+ * is positive; a step t of T = epochs * ceil(N / batch) uses
+ * a_t = a0 floor + a0 (1 - floor) (1 + cos(pi t / (T - 1))) / 2 (a0 when
+ * T = 1); after a batch's update, cluster j is dead when N_j < dead_frac *
+ * min(batch, N) / K; dead clusters are handled in ascending order, each
+ * with the uniform u = uniforms[t * K + j], choosing the donor k as the
+ * first index whose prefix of N (taken after the update, before any split
+ * of this batch) exceeds u * sum(N), skipping k = j; the donor's S and N
+ * halve, the dead cluster gets the same S and N, and their centroids
+ * become c_k (1 + eps s_c) and c_k (1 - eps s_c), s_c = +1 for even and -1
+ * for odd coordinates (S rescaled to match).  Assignments use the
+ * centroids rounded to the point dtype, as in oracle_fit.
+ *
+ * x: stored bits [N, d]; init [K, d] fp32.  Outputs: C_out [K, d] fp32;
+ * J_out [T] (sum of each batch's nearest distances at assignment time);
+ * labels_out [N] (every point's assignment in the last epoch); counts_out
+ * [K] (points per cluster in the last epoch).  Returns 0, or -1 when memory
+ * runs out or an argument is out of range.
+ * ----------------------------------------------------------------------- */
+int oracle_emeans(const void *x, int dtype, int64_t N, int64_t d, int64_t K, const float *init,
+                  int64_t batch, int32_t epochs, double alpha0, double floor_frac, double dead_frac,
+                  double eps, const float *uniforms, float *C_out, double *J_out, int32_t *labels_out,
+                  int32_t *counts_out)
+{
+    if (N < 1 || d < 1 || K < 1 || batch < 1 || epochs < 1) return -1;
+    const int64_t nb = (N + batch - 1) / batch, T = (int64_t)epochs * nb;
+    const int64_t mfull = batch < N ? batch : N;
+    double *X = (double *)malloc((size_t)(N * d) * sizeof(double));
+    double *S = (double *)calloc((size_t)(K * d), sizeof(double));
+    double *Nc = (double *)calloc((size_t)K, sizeof(double));
+    double *s = (double *)malloc((size_t)(K * d) * sizeof(double));
+    double *n = (double *)malloc((size_t)K * sizeof(double));
+    double *F = (double *)calloc((size_t)(K * d), sizeof(double));
+    double *G = (double *)calloc((size_t)K, sizeof(double));
+    double *Ch = (double *)malloc((size_t)(K * d) * sizeof(double));
+    double *P = (double *)malloc((size_t)(K + 1) * sizeof(double));
+    int32_t *lab = (int32_t *)malloc((size_t)mfull * sizeof(int32_t));
+    double *d1 = (double *)malloc((size_t)mfull * sizeof(double));
+    double *d2 = (double *)malloc((size_t)mfull * sizeof(double));
+    int ok = X && S && Nc && s && n && F && G && Ch && P && lab && d1 && d2;
+    if (ok) {
+        oracle_decode(x, dtype, N * d, X);
+        memcpy(C_out, init, (size_t)(K * d) * sizeof(float));
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t e = t / nb, i0 = (t % nb) * batch;
+            const int64_t m = (i0 + batch <= N) ? batch : N - i0;
+            const double a = T > 1 ? alpha0 * floor_frac +
+                                         alpha0 * (1.0 - floor_frac) * 0.5 * (1.0 + cos(acos(-1.0) * (double)t / (double)(T - 1)))
+                                   : alpha0;
+            for (int64_t q = 0; q < K * d; ++q) Ch[q] = oracle_decode_one(oracle_round_one(C_out[q], dtype), dtype);
+            oracle_assign(X + i0 * d, 1, m, d, Ch, K, lab, d1, d2);
+            double J = 0.0;
+            for (int64_t i = 0; i < m; ++i) J += d1[i];
+            J_out[t] = J;
+            for (int64_t q = 0; q < K * d; ++q) s[q] = 0.0;
+            for (int64_t j = 0; j < K; ++j) n[j] = 0.0;
+            for (int64_t i = 0; i < m; ++i) {
+                const int64_t j = lab[i];
+                n[j] += 1.0;
+                for (int64_t c = 0; c < d; ++c) s[j * d + c] += X[(i0 + i) * d + c];
+            }
+            if (e == epochs - 1) {
+                for (int64_t q = 0; q < K * d; ++q) F[q] += s[q];
+                for (int64_t j = 0; j < K; ++j) G[j] += n[j];
+                for (int64_t i = 0; i < m; ++i) labels_out[i0 + i] = lab[i];
+            }
+            for (int64_t j = 0; j < K; ++j) {
+                Nc[j] = (1.0 - a) * Nc[j] + a * n[j];
+                for (int64_t c = 0; c < d; ++c) {
+                    S[j * d + c] = (1.0 - a) * S[j * d + c] + a * s[j * d + c];
+                    if (Nc[j] > 0.0) C_out[j * d + c] = (float)(S[j * d + c] / Nc[j]);
+                }
+            }
+            /* proportional splitting of dead clusters */
+            P[0] = 0.0;
+            for (int64_t j = 0; j < K; ++j) P[j + 1] = P[j] + Nc[j];
+            const double dead_below = dead_frac * (double)mfull / (double)K;
+            for (int64_t j = 0; j < K; ++j) {
+                if (!(Nc[j] < dead_below)) continue;
+                const double target = (double)uniforms[t * K + j] * P[K];
+                int64_t k = 0;
+                while (k < K - 1 && !(P[k + 1] > target)) ++k;
+                if (k == j || !(Nc[k] > 0.0)) continue;
+                Nc[k] *= 0.5;
+                Nc[j] = Nc[k];
+                for (int64_t c = 0; c < d; ++c) {
+                    const double ck = S[k * d + c] * 0.5 / Nc[k];
+                    const double sgn = (c % 2 == 0) ? 1.0 : -1.0;
+                    const float cj = (float)(ck * (1.0 + eps * sgn));
+                    const float ckn = (float)(ck * (1.0 - eps * sgn));
+                    C_out[j * d + c] = cj;
+                    C_out[k * d + c] = ckn;
+                    S[j * d + c] = (double)cj * Nc[j];
+                    S[k * d + c] = (double)ckn * Nc[k];
+                }
+            }
+        }
+        for (int64_t j = 0; j < K; ++j) {
+            counts_out[j] = (int32_t)G[j];
+            if (G[j] > 0.0)
+                for (int64_t c = 0; c < d; ++c) C_out[j * d + c] = (float)(F[j * d + c] / G[j]);
+        }
+    }
+    free(X); free(S); free(Nc); free(s); free(n); free(F); free(G); free(Ch); free(P); free(lab); free(d1); free(d2);
+    return ok ? 0 : -1;
+}
+
 int oracle_num_threads(void)
 {
     int n = 1;

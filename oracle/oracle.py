@@ -44,6 +44,9 @@ def load_library(path: str):
     L.oracle_num_threads.restype = C.c_int
     L.oracle_optimal_1d.argtypes = [p, p, i64, i64, i64, p, p, p, p]
     L.oracle_optimal_1d.restype = C.c_int
+    L.oracle_emeans.argtypes = [p, C.c_int, i64, i64, i64, p, i64, C.c_int32, C.c_double, C.c_double, C.c_double,
+                                C.c_double, p, p, p, p, p]
+    L.oracle_emeans.restype = C.c_int
     return L
 
 
@@ -193,6 +196,35 @@ def optimal_1d(X: np.ndarray, w, K: int) -> dict:
     if rc != 0:
         raise ValueError(f"oracle_optimal_1d failed (K={K}, N={N}, or out of memory)")
     return dict(J=J, means=means, labels=labels, counts=counts)
+
+
+def emeans(x_bits: np.ndarray, dtype: str, init: np.ndarray, batch: int, epochs: int, alpha0: float,
+           floor_frac: float, dead_frac: float, eps: float, uniforms: np.ndarray) -> dict:
+    """e-means on one problem.  x_bits [N, d] (or [1, N, d]) stored bits, init
+    [K, d] float32, uniforms [T * K] float32 in [0, 1) with T = epochs *
+    ceil(N / batch).  Returns centroids [K, d] float32, J [T] (each batch's
+    assignment cost), labels int32 [N] and counts int32 [K] of the last
+    epoch."""
+    want = np.float32 if dtype == "f32" else np.uint16
+    x_bits = np.ascontiguousarray(x_bits, dtype=want)
+    if x_bits.ndim == 3:
+        x_bits = x_bits[0]
+    N, d = x_bits.shape
+    init = np.ascontiguousarray(init, dtype=np.float32).reshape(-1, d)
+    K = init.shape[0]
+    T = epochs * ((N + batch - 1) // batch)
+    uniforms = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(-1)
+    assert uniforms.size == T * K
+    C_out = np.empty_like(init)
+    J = np.empty(T, np.float64)
+    labels = np.empty(N, np.int32)
+    counts = np.empty(K, np.int32)
+    rc = lib().oracle_emeans(_ptr(x_bits), DTYPES[dtype], N, d, K, _ptr(init), int(batch), int(epochs),
+                             float(alpha0), float(floor_frac), float(dead_frac), float(eps), _ptr(uniforms),
+                             _ptr(C_out), _ptr(J), _ptr(labels), _ptr(counts))
+    if rc != 0:
+        raise ValueError("oracle_emeans failed (arguments out of range, or out of memory)")
+    return dict(centroids=C_out, J=J, labels=labels, counts=counts)
 
 
 def near_tie(d1: np.ndarray, d2: np.ndarray, rel: float = 1e-4) -> np.ndarray:

@@ -62,6 +62,15 @@ MUTANTS = [
     ("optimum: means not weighted", "                    swx += ws[p] * xs[p];", "                    swx += xs[p];"),
     ("optimum: runs numbered from the top", "                    labels_out[b * N + s[p].i] = (int32_t)k;",
      "                    labels_out[b * N + s[p].i] = (int32_t)(K - 1 - k);"),
+    ("e-means: step weights swapped", "                    S[j * d + c] = (1.0 - a) * S[j * d + c] + a * s[j * d + c];",
+     "                    S[j * d + c] = a * S[j * d + c] + (1.0 - a) * s[j * d + c];"),
+    ("e-means: counts accumulate without decay", "                Nc[j] = (1.0 - a) * Nc[j] + a * n[j];",
+     "                Nc[j] = Nc[j] + n[j];"),
+    ("e-means: no final mean", "            if (G[j] > 0.0)\n", "            if (0)\n"),
+    ("e-means: donor not halved", "                Nc[k] *= 0.5;", "                Nc[k] *= 1.0;"),
+    ("e-means: donor drawn from the top", "                const double target = (double)uniforms[t * K + j] * P[K];",
+     "                const double target = (1.0 - (double)uniforms[t * K + j]) * P[K];"),
+    ("e-means: schedule floor ignored", "alpha0 * floor_frac +\n", "alpha0 * 0.0 +\n"),
 ]
 
 

@@ -499,3 +499,99 @@ def test_optimal_1d_bounds_lloyd(orc):
     Jl = orc.objective(X[..., None].astype(np.float64), w.astype(np.float64), r["labels"],
                        r["means"][..., None])
     np.testing.assert_allclose(Jl, r["J"], rtol=1e-12)
+
+
+# ------------------------------------------------------------------ e-means
+
+def _emeans(orc, X, init, batch, epochs, alpha0, floor_frac=0.1, dead_frac=0.0, eps=1e-3, u=None):
+    N = X.shape[0]
+    T = epochs * ((N + batch - 1) // batch)
+    u = np.zeros(T * init.shape[0], np.float32) if u is None else u
+    return orc.emeans(X.astype(np.float32), "f32", init.astype(np.float32), batch, epochs, alpha0, floor_frac,
+                      dead_frac, eps, u)
+
+
+def test_emeans_full_batch_unit_step_is_lloyd(orc):
+    """One batch of all points and a constant step of 1: every update is
+    S = s, N = n, i.e. Lloyd's; the last epoch's plain mean is Lloyd's last
+    update.  Includes a centroid that never gets a point (kept, as in Lloyd)."""
+    rng = np.random.default_rng(31)
+    X = rng.normal(0, 1, (600, 5)).astype(np.float32)
+    init = X[:7].copy()
+    init[6] = 50.0
+    for epochs in (1, 3):
+        r = _emeans(orc, X, init, batch=600, epochs=epochs, alpha0=1.0, floor_frac=1.0)
+        ref = orc.fit(X[None], "f32", None, init[None], epochs)
+        np.testing.assert_array_equal(r["centroids"], ref["centroids"][0])
+        np.testing.assert_array_equal(r["labels"], ref["labels"][0])
+        np.testing.assert_array_equal(r["counts"], ref["counts"][0])
+        np.testing.assert_allclose(r["J"], ref["J"][0], rtol=1e-15)
+
+
+def test_emeans_single_cluster_moving_average(orc):
+    """K = 1: a batch's cost is measured from the centroid before its
+    update, which is the weighted mean of the batch means with weights
+    a (1 - a)^age n_b (closed form, not the recursion); the cosine schedule's
+    middle step is the mean of a0 and 0.1 a0."""
+    rng = np.random.default_rng(32)
+    X = rng.normal(0, 1, (500, 3)) * np.array([1.0, 2.0, 0.5]) + np.array([3.0, -1.0, 0.0])
+    X = X.astype(np.float32)
+    Xd = X.astype(np.float64)
+    init = np.zeros((1, 3), np.float32)
+    batch, a0 = 100, 0.4
+    r = _emeans(orc, X, init, batch=batch, epochs=1, alpha0=a0, floor_frac=1.0)
+    sums = [Xd[i:i + batch].sum(0) for i in range(0, 500, batch)]
+    for t in range(1, 5):
+        wts = [a0 * (1 - a0) ** (t - 1 - k) for k in range(t)]
+        c = sum(w * s for w, s in zip(wts, sums)) / sum(w * batch for w in wts)
+        c = c.astype(np.float32).astype(np.float64)   # the centroid state is float32
+        J = ((Xd[t * batch:(t + 1) * batch] - c) ** 2).sum()
+        assert abs(r["J"][t] - J) <= 1e-9 * J
+    assert abs(r["J"][0] - (Xd[:batch] ** 2).sum()) <= 1e-9 * r["J"][0]   # from the init
+    np.testing.assert_allclose(r["centroids"][0], Xd.mean(0), rtol=1e-6)   # last-epoch mean
+    # cosine decay over T = 3 steps: a_1 = (a0 + 0.1 a0) / 2
+    r3 = _emeans(orc, X[:300], init, batch=batch, epochs=1, alpha0=a0)
+    a1 = (a0 + 0.1 * a0) / 2
+    S2 = (1 - a1) * a0 * sums[0] + a1 * sums[1]
+    c2 = (S2 / ((1 - a1) * a0 * batch + a1 * batch)).astype(np.float32).astype(np.float64)
+    J2 = ((Xd[200:300] - c2) ** 2).sum()
+    assert abs(r3["J"][2] - J2) <= 1e-9 * J2
+
+
+def test_emeans_dead_cluster_splits_the_drawn_donor(orc):
+    """Two tight groups and a centroid far from both: after the first batch
+    it is dead; the uniform picks the donor in proportion to size (u = 0.2 the
+    first group, u = 0.9 the second), the donor's points are then shared by
+    the two halves of the split, and the other group is untouched."""
+    rng = np.random.default_rng(33)
+    A = rng.normal(0, 0.05, (200, 4)) + np.array([1.0, 1.0, 0.0, 0.0])
+    Bg = rng.normal(0, 0.05, (200, 4)) + np.array([-1.0, 0.0, 2.0, 0.0])
+    X = np.concatenate([A, Bg]).astype(np.float32)
+    init = np.array([[1, 1, 0, 0], [-1, 0, 2, 0], [40, 40, 40, 40]], np.float32)
+    for u_dead, donor, other in ((0.2, 0, 1), (0.9, 1, 0)):
+        u = np.zeros(2 * 3, np.float32)
+        u[2] = u_dead                     # step 0, cluster 2
+        r = _emeans(orc, X, init, batch=400, epochs=2, alpha0=1.0, floor_frac=1.0, dead_frac=0.5, eps=0.05, u=u)
+        grp = np.arange(400) // 200       # 0: first group, 1: second
+        mine = grp == donor
+        assert set(r["labels"][mine]) == {donor, 2}, "the donor's points are shared by the split pair"
+        assert np.all(r["labels"][~mine] == other)
+        assert r["counts"][donor] > 0 and r["counts"][2] > 0 and r["counts"][other] == 200
+        np.testing.assert_allclose(r["centroids"][other], X[~mine].astype(np.float64).mean(0), rtol=1e-5)
+    # no splitting without dead clusters: the far centroid keeps its place
+    r = _emeans(orc, X, init, batch=400, epochs=2, alpha0=1.0, floor_frac=1.0, dead_frac=0.0)
+    np.testing.assert_array_equal(r["centroids"][2], init[2])
+
+
+def test_emeans_final_means_are_the_last_epochs_update(orc):
+    rng = np.random.default_rng(34)
+    X = rng.normal(0, 1, (3000, 6)).astype(np.float32)
+    init = X[rng.choice(3000, 40, replace=False)].copy()
+    T = 3 * 6
+    r = _emeans(orc, X, init, batch=512, epochs=3, alpha0=0.3, dead_frac=0.05,
+                u=rng.random(T * 40).astype(np.float32))
+    c_new, counts, _, _ = orc.update(X[None].astype(np.float64), None, r["labels"][None], r["centroids"][None])
+    np.testing.assert_array_equal(counts[0], r["counts"])
+    live = r["counts"] > 0
+    np.testing.assert_array_equal(c_new[0][live], r["centroids"][live])
+    assert np.isfinite(r["J"]).all() and r["J"][-1] < r["J"][0]
