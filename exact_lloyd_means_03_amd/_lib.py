@@ -28,6 +28,9 @@ SIGNATURES = {
                                     _p]),
     "kmeans_optimal_1d_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "kmeans_optimal_1d": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p]),
+    "kmeans_emeans_workspace_bytes": (_sz, [_i64, _i64, _i64, C.c_int, _i64]),
+    "kmeans_emeans": (C.c_int, [_p, C.c_int, _i64, _i64, _i64, _p, _i64, _i32, C.c_double, C.c_double, C.c_double,
+                                C.c_double, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "kmeans_status_str": (C.c_char_p, [C.c_int]),
     "kmeans_last_error": (C.c_char_p, []),
     "kmeans_version": (C.c_int, []),

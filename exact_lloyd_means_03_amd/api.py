@@ -245,3 +245,58 @@ def kmeans_fit_stream(x_host, init, n_iter: int, weights=None, chunk: int = 1 <<
                              ws.numel(), _stream(dev))
     _lib.check(st, "kmeans_fit_stream")
     return centroids, labels, counts, objective
+
+
+def emeans_steps(N: int, batch: int, epochs: int) -> int:
+    """Number of e-means steps: epochs times the batches of one pass."""
+    return epochs * ((N + batch - 1) // batch) if N > 0 else 0
+
+
+def kmeans_emeans(x, init, batch: int, epochs: int, alpha0: float, floor_frac: float = 0.1, dead_frac: float = 0.0,
+                  eps: float = 1e-3, uniforms=None, centroids=None, labels=None, counts=None, objective=None,
+                  ws=None):
+    """e-means (moving-average mini-batch k-means) of one problem x [N, d]
+    (or [1, N, d]) on the GPU from init [K, d] float32.  uniforms [T, K]
+    float32 on the GPU (T = emeans_steps(N, batch, epochs)) are the split
+    draws, needed when dead_frac > 0.  Returns (centroids [K, d], labels [N]
+    (None unless True or a tensor is passed), counts [K], objective [T]
+    float64)."""
+    _dev_tensor(x, "x")
+    if x.dim() == 3 and x.shape[0] == 1:
+        x = x[0]
+    if x.dim() != 2:
+        raise ValueError("x must be [N, d]")
+    if x.dtype not in _DT:
+        raise TypeError(f"x dtype {x.dtype} is not float32 / float16 / bfloat16")
+    N, d = x.shape
+    _dev_tensor(init, "init", torch.float32)
+    if init.dim() == 3 and init.shape[0] == 1:
+        init = init[0]
+    if init.dim() != 2 or init.shape[1] != d:
+        raise ValueError("init must be [K, d] float32")
+    K = init.shape[0]
+    dev = x.device
+    T = emeans_steps(N, batch, epochs) if batch >= 1 and epochs >= 1 else 0
+    if uniforms is not None:
+        _dev_tensor(uniforms, "uniforms", torch.float32, (T, K))
+    centroids = torch.empty_like(init) if centroids is None else \
+        _dev_tensor(centroids, "centroids", torch.float32, init.shape)
+    if labels is True:
+        labels = torch.empty((N,), dtype=torch.int32, device=dev)
+    elif labels is not None:
+        _dev_tensor(labels, "labels", torch.int32, (N,))
+    counts = torch.empty((K,), dtype=torch.int32, device=dev) if counts is None else \
+        _dev_tensor(counts, "counts", torch.int32, (K,))
+    objective = torch.empty((T,), dtype=torch.float64, device=dev) if objective is None else \
+        _dev_tensor(objective, "objective", torch.float64, (T,))
+    L = _lib.load()
+    if ws is None:
+        # 0 for arguments the entry point rejects: it then reports why
+        n = L.kmeans_emeans_workspace_bytes(N, d, K, _DT[x.dtype], int(batch))
+        ws = torch.empty(max(int(n), 256), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "workspace", torch.uint8)
+    st = L.kmeans_emeans(_ptr(x), _DT[x.dtype], N, d, K, _ptr(init), int(batch), int(epochs), float(alpha0),
+                         float(floor_frac), float(dead_frac), float(eps), _ptr(uniforms), _ptr(centroids),
+                         _ptr(labels), _ptr(counts), _ptr(objective), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_emeans")
+    return centroids, labels, counts, objective

@@ -16,8 +16,8 @@ LIB = os.path.join(HERE, "libkmeans_mi355x.so")
 ARCH = os.environ.get("KM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["small.hip", "assign_mfma.hip", "assign_1d.hip", "fit_1d.hip", "optimal_1d.hip", "sort.hip", "update.hip",
-           "api.hip"]
+SOURCES = ["small.hip", "assign_mfma.hip", "assign_1d.hip", "fit_1d.hip", "optimal_1d.hip", "emeans.hip",
+           "sort.hip", "update.hip", "api.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

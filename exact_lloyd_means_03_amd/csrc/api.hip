@@ -2,6 +2,7 @@
 // the workspace plan and the per-iteration kernel sequence.  Every check
 // happens before the first enqueue; nothing here allocates device memory or
 // synchronizes the stream.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -275,6 +276,50 @@ hipError_t stream_res(int dev, StreamRes** out) {
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// e-means (daily.steinslab.io "e-means" article): mini-batches of
+// consecutive points, each assigned against the current centroids by the
+// Lloyd assignment and reduced into per-cluster sums and counts by the
+// Lloyd sort and segmented reduction; a float64 moving average of those
+// statistics then moves the centroids, dead clusters are split from live
+// ones, and after the last epoch every centroid becomes that epoch's plain
+// mean.
+
+struct EmeansPlan {
+    Workspace batch;  // the per-batch plan (B = 1, N = batch points)
+    int64_t mfull = 0, nb = 0, steps = 0;
+    size_t S = 0, Nc = 0, F = 0, G = 0, P = 0, donor = 0, total = 0;
+};
+
+EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch, int32_t epochs) {
+    EmeansPlan p;
+    p.mfull = batch < N ? batch : N;
+    p.nb = N > 0 ? (N + batch - 1) / batch : 0;
+    p.steps = p.nb * epochs;
+    p.batch = plan_workspace(1, p.mfull > 0 ? p.mfull : 1, d, K, xt);
+    size_t off = p.batch.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    p.S = take((size_t)K * d * sizeof(double));
+    p.Nc = take((size_t)K * sizeof(double));
+    p.F = take((size_t)K * d * sizeof(double));
+    p.G = take((size_t)K * sizeof(double));
+    p.P = take((size_t)(K + 1) * sizeof(double));
+    p.donor = take((size_t)K * sizeof(int32_t));
+    p.total = off;
+    return p;
+}
+
+// The step size of step t of T: cosine decay from alpha0 to floor * alpha0.
+double emeans_step_size(double alpha0, double floor_frac, int64_t t, int64_t T) {
+    if (T <= 1) return alpha0;
+    return alpha0 * floor_frac +
+           alpha0 * (1.0 - floor_frac) * 0.5 * (1.0 + cos(acos(-1.0) * (double)t / (double)(T - 1)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -491,6 +536,104 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
         KM_HIP(launch_divide(sums, wsum, ctot, 1, K, (int)d, centroids, centroids, s), "divide");
     }
     if (counts) KM_HIP(hipMemcpyAsync(counts, ctot, (size_t)K * sizeof(int32_t), hipMemcpyDeviceToDevice, s), "copy");
+    return KM_OK;
+}
+
+size_t kmeans_emeans_workspace_bytes(int64_t N, int64_t d, int64_t K, km_dtype xt, int64_t batch) {
+    if (check_shape(1, N, d, K, (int)xt) != KM_OK || batch < 1 || !emeans_split_supports(K)) return 0;
+    if (d == 1 && !assign_1d_supports(K)) return 0;
+    return plan_emeans(N, d, K, (DType)xt, batch, 1).total;
+}
+
+km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_t K, const float* init,
+                        int64_t batch, int32_t epochs, double alpha0, double floor_frac, double dead_frac,
+                        double eps, const float* uniforms, float* centroids, int32_t* labels, int32_t* counts,
+                        double* objective, void* workspace, size_t workspace_bytes, km_stream stream) {
+    KM_TRY(check_shape(1, N, d, K, (int)xt));
+    KM_TRY(check_scalar_k(d, K));
+    if (!emeans_split_supports(K))
+        return fail(KM_EUNSUPPORTED, "e-means supports K <= %lld (K=%lld)", (long long)kEmeansMaxK, (long long)K);
+    if (batch < 1) return fail(KM_EINVAL, "batch=%lld < 1", (long long)batch);
+    if (epochs < 1) return fail(KM_EINVAL, "epochs=%d < 1", epochs);
+    if (!(alpha0 > 0.0 && alpha0 <= 1.0)) return fail(KM_EINVAL, "alpha0=%g is not in (0, 1]", alpha0);
+    if (!(floor_frac >= 0.0 && floor_frac <= 1.0))
+        return fail(KM_EINVAL, "floor_frac=%g is not in [0, 1]", floor_frac);
+    if (!(dead_frac >= 0.0)) return fail(KM_EINVAL, "dead_frac=%g < 0", dead_frac);
+    if (!(eps >= 0.0 && eps < 1.0)) return fail(KM_EINVAL, "eps=%g is not in [0, 1)", eps);
+    KM_TRY(need(x, N, "x"));
+    KM_TRY(need(init, 1, "init"));
+    KM_TRY(need(centroids, 1, "centroids"));
+    if (dead_frac > 0.0) KM_TRY(need(uniforms, N, "uniforms"));
+    const DType t = (DType)xt;
+    const EmeansPlan P = plan_emeans(N, d, K, t, batch, epochs);
+    {
+        Workspace W{};
+        W.total = P.total;
+        KM_TRY(check_ws(W, workspace, workspace_bytes));
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const size_t cbytes = (size_t)K * d * sizeof(float);
+    if (init != centroids) KM_HIP(hipMemcpyAsync(centroids, init, cbytes, hipMemcpyDeviceToDevice, s), "copy init");
+    if (N == 0) {
+        if (counts) KM_HIP(launch_zero(counts, (size_t)K * sizeof(int32_t), s), "zero");
+        return KM_OK;
+    }
+    const Workspace& W = P.batch;
+    char* ws = (char*)workspace;
+    double* S = at<double>(ws, P.S);
+    double* Nc = at<double>(ws, P.Nc);
+    double* F = at<double>(ws, P.F);
+    double* G = at<double>(ws, P.G);
+    // S, N, F, G are adjacent in the plan: clear them with one fill
+    KM_HIP(launch_zero(S, P.P - P.S, s), "zero");
+    const int64_t es = dtype_bytes(t);
+    float* sums = at<float>(ws, W.sums);
+    int32_t* cnt = at<int32_t>(ws, W.counts);
+    int32_t* offsets = at<int32_t>(ws, W.offsets);
+    int32_t* perm = at<int32_t>(ws, W.perm);
+    int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
+    double* part = at<double>(ws, W.obj_part);
+    // every batch uses the piece width of a full batch, so a shorter last
+    // batch never has more pieces than the plan holds
+    const int TW = segreduce_tw(1, P.mfull);
+    const double dead_below = dead_frac * (double)P.mfull / (double)K;
+    for (int64_t st = 0; st < P.steps; ++st) {
+        const int64_t e = st / P.nb, i0 = (st % P.nb) * batch;
+        const int64_t m = (i0 + batch <= N) ? batch : N - i0;
+        const bool last = e == epochs - 1;
+        const void* xb = (const char*)x + i0 * d * es;
+        int32_t* lab = (last && labels) ? labels + i0 : at<int32_t>(ws, W.labels);
+        int64_t nblk;
+        if (use_assign_1d(d, K)) {
+            nblk = assign_1d_blocks(m);
+            KM_HIP(launch_assign_1d(t, xb, 1, m, centroids, K, nullptr, lab, nullptr, part, nblk, nblk, s),
+                   "assign_1d");
+        } else {
+            nblk = assign_mfma_blocks(m, W.DP, t);
+            void* blob = at<void>(ws, W.chat);
+            KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, blob, s), "prep");
+            KM_HIP(launch_assign_mfma(t, xb, 1, m, (int)d, W.DP, blob, W.Kp, nullptr, lab, nullptr, part, nblk, s),
+                   "assign_mfma");
+        }
+        if (objective) KM_HIP(launch_obj_reduce(part, 1, nblk, objective + st, 1, s), "obj_reduce");
+        KM_HIP(launch_zero(sums, (size_t)K * d * sizeof(float), s), "zero");
+        KM_HIP(launch_zero(cnt, (size_t)K * sizeof(int32_t), s), "zero");
+        KM_HIP(launch_sort(lab, 1, m, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (m + TW - 1) / TW,
+                           piece_seg, s),
+               "sort");
+        KM_HIP(launch_segreduce_tw(t, xb, nullptr, 1, m, (int)d, perm, offsets, K, sums, nullptr, piece_seg,
+                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, s),
+               "segreduce");
+        const double a = emeans_step_size(alpha0, floor_frac, st, P.steps);
+        KM_HIP(launch_emeans_ema(S, Nc, sums, cnt, K, (int)d, a, centroids, last ? F : nullptr, last ? G : nullptr,
+                                 s),
+               "ema");
+        if (dead_frac > 0.0)
+            KM_HIP(launch_emeans_split(S, Nc, centroids, K, (int)d, dead_below, eps, uniforms + st * K,
+                                       at<double>(ws, P.P), at<int32_t>(ws, P.donor), s),
+                   "split");
+    }
+    KM_HIP(launch_emeans_final(F, G, K, (int)d, centroids, counts, s), "final mean");
     return KM_OK;
 }
 

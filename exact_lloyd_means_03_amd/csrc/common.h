@@ -154,4 +154,14 @@ hipError_t launch_optimal_1d(DType xt, const void* x, const float* w, int64_t B,
                              float* centroids, int32_t* labels, int32_t* counts, double* objective, void* ws,
                              hipStream_t s);
 
+// e-means state updates (float64 sums S [K][d] and counts N [K]).
+constexpr int64_t kEmeansMaxK = 32768;  // the split keeps one int per cluster in LDS
+hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_t* n, int64_t K, int d, double a,
+                             float* C, double* F, double* G, hipStream_t st);
+bool emeans_split_supports(int64_t K);
+hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d, double dead_below, double eps,
+                               const float* u, double* P, int32_t* donor, hipStream_t st);
+hipError_t launch_emeans_final(const double* F, const double* G, int64_t K, int d, float* C, int32_t* counts,
+                               hipStream_t st);
+
 }  // namespace km

@@ -190,6 +190,58 @@ KM_API km_status kmeans_optimal_1d(const void *x, km_dtype xt, const float *weig
                             float *centroids, int32_t *labels, int32_t *counts, double *objective,
                             void *workspace, size_t workspace_bytes, km_stream stream);
 
+/* e-means: mini-batch k-means with moving-average statistics
+ * (daily.steinslab.io "e-means" article: the update S_j <- (1 - a) S_j +
+ * a s_j of each cluster's sum and count in "Breaking 70 Years of Full-Batch
+ * Inertia"; the cosine step decay from alpha0 to a fraction of it, and the
+ * move to the last epoch's plain mean, in "Mini-Batch Stochastic Noise" and
+ * "Matching 25 Iterations"; proportional splitting of dead clusters in
+ * "Proportional Splitting Resurrects Thousands of Dead Centers").  Not
+ * Lloyd: a different, approximate algorithm that reuses its kernels.
+ *
+ * The points are cut into ceil(N / batch) batches of consecutive points
+ * (the last one shorter); there are T = epochs * ceil(N / batch) steps.
+ * Step t assigns its batch to the nearest current centroid (the Lloyd
+ * assignment, ties to the lower index), sums and counts the batch per
+ * cluster (s_j, n_j) and sets, in float64, S_j = (1 - a_t) S_j + a_t s_j,
+ * N_j = (1 - a_t) N_j + a_t n_j (both start at zero) and c_j = S_j / N_j
+ * where N_j > 0, with a_t = alpha0 (floor + (1 - floor) (1 + cos(pi t /
+ * (T - 1))) / 2) (a_0 = alpha0 when T = 1).  Then every cluster with
+ * N_j < dead_frac * min(batch, N) / K is dead; dead clusters are resolved
+ * in ascending order: the donor k is the first cluster whose prefix sum of
+ * N (taken before any split of the step) exceeds u_j * sum(N), with u_j =
+ * uniforms[t * K + j]; k == j or a donor with N_k == 0 does nothing;
+ * otherwise N_k and S_k halve, cluster j takes the same N, and the two
+ * centroids become c_k (1 + eps s_c) and c_k (1 - eps s_c) (s_c = +1 on even,
+ * -1 on odd coordinates), S rescaled to match.  After the last step every
+ * cluster that received points in the last epoch moves to the plain mean of
+ * those points.
+ *   x          [N,d] device points of dtype xt.
+ *   init       [K,d] float32 device (may alias centroids).
+ *   batch      points per step (>= 1; min(batch, N) is the full batch).
+ *   epochs     passes over the points (>= 1).
+ *   alpha0     first step size, in (0, 1]; floor_frac, in [0, 1], is the
+ *              last step's fraction of it.
+ *   dead_frac  0 turns splitting off.  eps in [0, 1).
+ *   uniforms   [T,K] float32 device in [0, 1), or NULL when dead_frac == 0:
+ *              the draws of the splits (the caller's random numbers).
+ *   centroids  out [K,d] float32 device.
+ *   labels     out [N] int32 device or NULL: the last epoch's assignments.
+ *   counts     out [K] int32 device or NULL: points per cluster in the last
+ *              epoch.
+ *   objective  out [T] float64 device or NULL: sum over the batch of step t
+ *              of the squared distance to the centroid it was assigned to.
+ * One problem (B = 1); d = 1 needs K <= 16384, and K <= 32768 always
+ * (KM_EUNSUPPORTED).  The workspace must hold
+ * kmeans_emeans_workspace_bytes(N, d, K, xt, batch) bytes, 256-byte
+ * aligned. */
+KM_API size_t kmeans_emeans_workspace_bytes(int64_t N, int64_t d, int64_t K, km_dtype xt, int64_t batch);
+KM_API km_status kmeans_emeans(const void *x, km_dtype xt, int64_t N, int64_t d, int64_t K,
+                        const float *init, int64_t batch, int32_t epochs, double alpha0,
+                        double floor_frac, double dead_frac, double eps, const float *uniforms,
+                        float *centroids, int32_t *labels, int32_t *counts, double *objective,
+                        void *workspace, size_t workspace_bytes, km_stream stream);
+
 /* Static description of a status code. */
 KM_API const char *kmeans_status_str(km_status status);
 

@@ -440,8 +440,9 @@ int oracle_optimal_1d(const double *X, const double *w, int64_t B, int64_t N, in
  * the order); S and N start at zero and a centroid moves only once its N
  * is positive; a step t of T = epochs * ceil(N / batch) uses
  * a_t = a0 floor + a0 (1 - floor) (1 + cos(pi t / (T - 1))) / 2 (a0 when
- * T = 1); after a batch's update, cluster j is dead when N_j < dead_frac *
- * min(batch, N) / K; dead clusters are handled in ascending order, each
+ * T = 1); after a batch's update (before any of its splits), cluster j is
+ * dead when N_j < dead_frac * min(batch, N) / K; dead clusters are handled
+ * in ascending order, each
  * with the uniform u = uniforms[t * K + j], choosing the donor k as the
  * first index whose prefix of N (taken after the update, before any split
  * of this batch) exceeds u * sum(N), skipping k = j; the donor's S and N
@@ -473,10 +474,11 @@ int oracle_emeans(const void *x, int dtype, int64_t N, int64_t d, int64_t K, con
     double *G = (double *)calloc((size_t)K, sizeof(double));
     double *Ch = (double *)malloc((size_t)(K * d) * sizeof(double));
     double *P = (double *)malloc((size_t)(K + 1) * sizeof(double));
+    char *dead = (char *)malloc((size_t)K);
     int32_t *lab = (int32_t *)malloc((size_t)mfull * sizeof(int32_t));
     double *d1 = (double *)malloc((size_t)mfull * sizeof(double));
     double *d2 = (double *)malloc((size_t)mfull * sizeof(double));
-    int ok = X && S && Nc && s && n && F && G && Ch && P && lab && d1 && d2;
+    int ok = X && S && Nc && s && n && F && G && Ch && P && dead && lab && d1 && d2;
     if (ok) {
         oracle_decode(x, dtype, N * d, X);
         memcpy(C_out, init, (size_t)(K * d) * sizeof(float));
@@ -514,8 +516,9 @@ int oracle_emeans(const void *x, int dtype, int64_t N, int64_t d, int64_t K, con
             P[0] = 0.0;
             for (int64_t j = 0; j < K; ++j) P[j + 1] = P[j] + Nc[j];
             const double dead_below = dead_frac * (double)mfull / (double)K;
+            for (int64_t j = 0; j < K; ++j) dead[j] = Nc[j] < dead_below;
             for (int64_t j = 0; j < K; ++j) {
-                if (!(Nc[j] < dead_below)) continue;
+                if (!dead[j]) continue;
                 const double target = (double)uniforms[t * K + j] * P[K];
                 int64_t k = 0;
                 while (k < K - 1 && !(P[k + 1] > target)) ++k;
@@ -540,7 +543,8 @@ int oracle_emeans(const void *x, int dtype, int64_t N, int64_t d, int64_t K, con
                 for (int64_t c = 0; c < d; ++c) C_out[j * d + c] = (float)(F[j * d + c] / G[j]);
         }
     }
-    free(X); free(S); free(Nc); free(s); free(n); free(F); free(G); free(Ch); free(P); free(lab); free(d1); free(d2);
+    free(X); free(S); free(Nc); free(s); free(n); free(F); free(G); free(Ch); free(P); free(dead); free(lab);
+    free(d1); free(d2);
     return ok ? 0 : -1;
 }
 

@@ -149,3 +149,40 @@ def test_fit_stream_rejects(lib):
     assert call(ws_bytes=64) == 3
     assert call(K=0) == 1
     assert call(xt=4) == 2
+
+
+def test_emeans_rejects(lib):
+    ws = C.c_void_p(0x100000)
+    n = lib.kmeans_emeans_workspace_bytes(1 << 20, 96, 16384, 2, 65536)
+    # the float64 sums S and last-epoch sums F, and the batch's labels and permutation
+    assert n >= 2 * 16384 * 96 * 8 + 2 * 65536 * 4 and n % 256 == 0
+    assert lib.kmeans_emeans_workspace_bytes(1000, 16, 4, 1, 0) == 0       # batch < 1
+    assert lib.kmeans_emeans_workspace_bytes(1000, 1, 20000, 0, 64) == 0   # d = 1 and K > 16384
+    assert lib.kmeans_emeans_workspace_bytes(1000, 16, 40000, 1, 64) == 0  # K > 32768
+
+    def call(**kw):
+        a = dict(x=FAKE, xt=1, N=1000, d=16, K=4, init=FAKE, batch=100, epochs=2, alpha0=0.5, floor=0.1,
+                 dead=0.0, eps=1e-3, u=None, C=FAKE, ws=ws, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.kmeans_emeans(a["x"], a["xt"], a["N"], a["d"], a["K"], a["init"], a["batch"], a["epochs"],
+                                 a["alpha0"], a["floor"], a["dead"], a["eps"], a["u"], a["C"], None, None, None,
+                                 a["ws"], a["ws_bytes"], None)
+
+    assert call(batch=0) == 1 and b"batch" in lib.kmeans_last_error()
+    assert call(epochs=0) == 1
+    assert call(alpha0=0.0) == 1 and b"alpha0" in lib.kmeans_last_error()
+    assert call(alpha0=1.5) == 1
+    assert call(floor=-0.1) == 1
+    assert call(floor=float("nan")) == 1
+    assert call(dead=-1.0) == 1
+    assert call(eps=1.0) == 1
+    assert call(dead=0.5) == 1 and b"uniforms" in lib.kmeans_last_error()  # splits need the draws
+    assert call(x=None) == 1
+    assert call(init=None) == 1
+    assert call(C=None) == 1
+    assert call(K=0) == 1
+    assert call(K=40000) == 2
+    assert call(d=1, K=20000, xt=0) == 2
+    assert call(xt=5) == 2
+    assert call(ws_bytes=64) == 3
+    assert call(ws=C.c_void_p(0x100010)) == 1

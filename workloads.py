@@ -62,6 +62,12 @@ class Workload:
     w_lo: float = 0.1       # rows1d: sample weights ~ U(w_lo, w_hi)
     w_hi: float = 1.0
     host: bool = False      # the points stay in (pinned) host memory: generate_host()
+    em_batch: int = 0       # e-means: points per step (0: not an e-means workload)
+    em_epochs: int = 0      # e-means: passes over the points
+    em_alpha0: float = 0.5  # e-means: first step size
+    em_floor: float = 0.1   # e-means: last step size as a fraction of the first
+    em_dead_frac: float = 0.1  # e-means: dead below this fraction of a batch's mean count per cluster
+    em_eps: float = 1e-3    # e-means: relative perturbation of a split
 
     @property
     def components(self) -> int:
@@ -95,6 +101,10 @@ WORKLOADS = {
                  n_iter=30, seed=5, kind="rows1d", init="linspace"),
         Workload("stream-n64m-k32768-d128-f16", B=1, N=1 << 26, d=128, K=32768, dtype="f16",
                  n_iter=3, seed=6, sigma=0.15, init="random", host=True),
+        # e-means against Lloyd: n_iter is the Lloyd comparison run
+        Workload("emeans-n1m-k16384-d96-bf16", B=1, N=1 << 20, d=96, K=16384, dtype="bf16",
+                 n_iter=25, seed=7, sigma=0.15, noise_frac=0.05, noise_range=3.0, init="random",
+                 em_batch=65536, em_epochs=5, em_alpha0=0.5, em_floor=0.1, em_dead_frac=0.1, em_eps=1e-3),
     ]
 }
 
@@ -285,3 +295,10 @@ def generate_host(wl: Workload, chunk: int = 1 << 22):
     init = x[idx].float().cuda()
     torch.cuda.synchronize()
     return x, init
+
+
+def emeans_uniforms(seed: int, steps: int, K: int) -> np.ndarray:
+    """The split draws of an e-means run: [steps, K] float32 uniform on
+    [0, 1), from their own seed sequence (entropy [seed, 7919])."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7919]))
+    return rng.random((steps, K), dtype=np.float32)
