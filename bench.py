@@ -341,6 +341,168 @@ def bench_stream(args, km, wl):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_emeans(p, target_s: float):
+    """Time the oracle's e-means on a bounded sample: n points as one batch
+    (one step against all K centroids, with the moving average and the
+    splits), scaled linearly to one epoch over all N points."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    wl = p.wl
+    bits = workloads.raw_bits(p.x)[0]
+    init = p.init[0].numpy()
+    u = workloads.emeans_uniforms(wl.seed, 1, wl.K)
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.emeans(bits[:n], wl.dtype, init, n, 1, wl.em_alpha0, wl.em_floor, wl.em_dead_frac, wl.em_eps, u)
+        return time.perf_counter() - t0
+
+    n = 256
+    t = run(n)
+    while t < 0.5 and n < wl.N:
+        n = min(wl.N, n * 4)
+        t = run(n)
+    if n < wl.N:
+        n = int(min(wl.N, max(n, n * target_s / max(t, 1e-9))))
+        t = run(n)
+    per_epoch = t * wl.N / n
+    return {
+        "value": 1.0 / per_epoch,
+        "unit": "epochs/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"the first {n} of {wl.N} points as one e-means step against all K={wl.K} centroids "
+                   f"(assignment, moving average, splits), {t:.2f} s, extrapolated linearly to one epoch"),
+    }
+
+
+def bench_emeans(args, km, wl):
+    """e-means (kmeans_emeans): a step is one whole e-means run of
+    wl.em_epochs epochs in batches of wl.em_batch points, points resident in
+    device memory.  `value` is epochs/s.  Outside the timed region the line
+    also gives the mean squared error of the final centroids after 1..E
+    epochs next to Lloyd's after wl.n_iter iterations from the same init,
+    both fits' times, and the assignment kernel on one batch against its
+    matrix-core roofline."""
+    import torch
+
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    p = workloads.generate(wl)
+    x = p.x[0].to(dev)
+    init = p.init[0].to(dev)
+    N, d, K, batch, E = wl.N, wl.d, wl.K, wl.em_batch, wl.em_epochs
+    T = km.emeans_steps(N, batch, E)
+    u = torch.from_numpy(workloads.emeans_uniforms(wl.seed, T, K)).to(dev)
+    L = km.load()
+    xt = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+    ws = torch.empty(max(int(L.kmeans_emeans_workspace_bytes(N, d, K, xt, batch)), 256), dtype=torch.uint8,
+                     device=dev)
+    cen = torch.empty_like(init)
+    counts = torch.empty((K,), dtype=torch.int32, device=dev)
+
+    def run(epochs):
+        t_ = km.emeans_steps(N, batch, epochs)
+        obj = torch.empty((t_,), dtype=torch.float64, device=dev)
+        km.kmeans_emeans(x, init, batch, epochs, wl.em_alpha0, wl.em_floor, wl.em_dead_frac, wl.em_eps,
+                         uniforms=u[:t_], centroids=cen, counts=counts, objective=obj, ws=ws)
+        return obj
+
+    for _ in range(args.warmup):
+        run(E)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run(E)
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    run_ms = e0.elapsed_time(e1) / args.steps
+
+    # quality: the mean squared error of the final centroids over all points
+    ws_a = km.workspace(1, N, d, K, x.dtype, dev)
+    xb = x[None]
+    o = torch.empty((1,), dtype=torch.float64, device=dev)
+
+    def mse(c):
+        km.kmeans_assign(xb, c[None], objective=o, ws=ws_a)
+        return float(o[0]) / N
+
+    em_mse, em_ms = [], []
+    for e in range(1, E + 1):
+        run(e)
+        torch.cuda.synchronize()
+        e0.record()
+        run(e)
+        e1.record()
+        torch.cuda.synchronize()
+        em_ms.append(e0.elapsed_time(e1))
+        em_mse.append(mse(cen))
+    ws_l = km.workspace(1, N, d, K, x.dtype, dev)
+    km.kmeans_fit(xb, init[None], 1, ws=ws_l)
+    torch.cuda.synchronize()
+    e0.record()
+    cl, _, _, Jl = km.kmeans_fit(xb, init[None], wl.n_iter, ws=ws_l)
+    e1.record()
+    torch.cuda.synchronize()
+    lloyd_ms = e0.elapsed_time(e1)
+    lloyd_mse = mse(cl[0])
+    match = next((e + 1 for e, m in enumerate(em_mse) if m <= lloyd_mse), None)
+
+    # the dominant kernel: the assignment of one full batch, timed on its own
+    xs = x[None, :batch]
+    lab = torch.empty((1, batch), dtype=torch.int32, device=dev)
+    ws_b = km.workspace(1, batch, d, K, x.dtype, dev)
+    reps = 20
+    km.kmeans_assign(xs, cen[None], labels=lab, ws=ws_b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        km.kmeans_assign(xs, cen[None], labels=lab, ws=ws_b)
+    e1.record()
+    torch.cuda.synchronize()
+    assign_ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * batch * K * d
+    achieved = flops / (assign_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    out = {
+        "metric": "e-means epochs/s (mini-batch moving-average k-means, all points resident in HBM)",
+        "value": args.steps * E / elapsed,
+        "unit": "epochs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "d": d, "K": K, "point_dtype": wl.dtype, "init": wl.init,
+                   "batch": batch, "epochs": E, "steps_per_run": T, "alpha0": wl.em_alpha0,
+                   "floor": wl.em_floor, "dead_frac": wl.em_dead_frac, "eps": wl.em_eps},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None, "kernel": "k_assign_mfma (one batch)", "algorithmic_per_launch": flops,
+                     "avg_launch_ms": assign_ms},
+        "run_ms_event": run_ms,
+        "quality": {"emeans_mse_by_epochs": em_mse, "emeans_ms_by_epochs": em_ms,
+                    "lloyd_iters": wl.n_iter, "lloyd_mse": lloyd_mse, "lloyd_ms": lloyd_ms,
+                    "lloyd_objective_last_iter": float(Jl[0, -1]) / N,
+                    "epochs_to_match_lloyd": match,
+                    "speedup_at_match": (lloyd_ms / em_ms[match - 1]) if match else None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_emeans(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -379,6 +541,8 @@ def main():
     dev = torch.device("cuda", 0)
     if wl.host:
         return bench_stream(args, km, wl)
+    if wl.em_batch:
+        return bench_emeans(args, km, wl)
     p = workloads.generate(wl)
     x = p.x.to(dev)
     w = None if p.w is None else p.w.to(dev)

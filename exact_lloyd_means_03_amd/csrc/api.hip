@@ -46,7 +46,7 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     w.DP = padded_dim(d);
     w.Kp = padded_k(K);
     const bool a1d = use_assign_1d(d, K);
-    w.nblk_assign = a1d ? assign_1d_blocks(N) : assign_mfma_blocks(N, w.DP, xt);
+    w.nblk_assign = a1d ? assign_1d_blocks(N) : assign_mfma_blocks(B, N, w.DP, xt);
     if (w.nblk_assign < 1) w.nblk_assign = 1;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -234,7 +234,7 @@ StreamPlan plan_stream(int64_t N, int64_t d, int64_t K, DType xt, int64_t chunk)
     p.chunk = plan_workspace(1, c, d, K, xt);
     p.nblk_chunk = p.chunk.nblk_assign;
     const int64_t last = N - (p.nchunks > 0 ? (p.nchunks - 1) * c : 0);
-    const int64_t nblk_last = p.nchunks > 0 ? assign_mfma_blocks(last, p.chunk.DP, xt) : 0;
+    const int64_t nblk_last = p.nchunks > 0 ? assign_mfma_blocks(1, last, p.chunk.DP, xt) : 0;
     p.nblk_total = p.nchunks > 0 ? (p.nchunks - 1) * p.nblk_chunk + nblk_last : 1;
     size_t off = p.chunk.total;
     auto take = [&](size_t bytes) {
@@ -288,7 +288,7 @@ hipError_t stream_res(int dev, StreamRes** out) {
 struct EmeansPlan {
     Workspace batch;  // the per-batch plan (B = 1, N = batch points)
     int64_t mfull = 0, nb = 0, steps = 0;
-    size_t S = 0, Nc = 0, F = 0, G = 0, P = 0, donor = 0, total = 0;
+    size_t S = 0, Nc = 0, F = 0, G = 0, list_j = 0, list_k = 0, total = 0;
 };
 
 EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch, int32_t epochs) {
@@ -307,8 +307,8 @@ EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch,
     p.Nc = take((size_t)K * sizeof(double));
     p.F = take((size_t)K * d * sizeof(double));
     p.G = take((size_t)K * sizeof(double));
-    p.P = take((size_t)(K + 1) * sizeof(double));
-    p.donor = take((size_t)K * sizeof(int32_t));
+    p.list_j = take((size_t)K * sizeof(int32_t));
+    p.list_k = take((size_t)K * sizeof(int32_t));
     p.total = off;
     return p;
 }
@@ -513,7 +513,7 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
             KM_HIP(hipStreamWaitEvent(s, R->copied[buf], 0), "event wait");
             int32_t* lab = labels ? labels + p0 : at<int32_t>(ws, W.labels);
             KM_HIP(launch_assign_mfma(t, xb, 1, nc, (int)d, W.DP, at<void>(ws, W.chat), W.Kp, wb, lab, nullptr,
-                                      obj_all + ci * P.nblk_chunk, assign_mfma_blocks(nc, W.DP, t), s),
+                                      obj_all + ci * P.nblk_chunk, assign_mfma_blocks(1, nc, W.DP, t), s),
                    "assign_mfma");
             int32_t* cnt = at<int32_t>(ws, W.counts);
             int32_t* offsets = at<int32_t>(ws, W.offsets);
@@ -585,7 +585,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
     double* F = at<double>(ws, P.F);
     double* G = at<double>(ws, P.G);
     // S, N, F, G are adjacent in the plan: clear them with one fill
-    KM_HIP(launch_zero(S, P.P - P.S, s), "zero");
+    KM_HIP(launch_zero(S, P.list_j - P.S, s), "zero");
     const int64_t es = dtype_bytes(t);
     float* sums = at<float>(ws, W.sums);
     int32_t* cnt = at<int32_t>(ws, W.counts);
@@ -609,7 +609,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
             KM_HIP(launch_assign_1d(t, xb, 1, m, centroids, K, nullptr, lab, nullptr, part, nblk, nblk, s),
                    "assign_1d");
         } else {
-            nblk = assign_mfma_blocks(m, W.DP, t);
+            nblk = assign_mfma_blocks(1, m, W.DP, t);
             void* blob = at<void>(ws, W.chat);
             KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, blob, s), "prep");
             KM_HIP(launch_assign_mfma(t, xb, 1, m, (int)d, W.DP, blob, W.Kp, nullptr, lab, nullptr, part, nblk, s),
@@ -630,7 +630,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
                "ema");
         if (dead_frac > 0.0)
             KM_HIP(launch_emeans_split(S, Nc, centroids, K, (int)d, dead_below, eps, uniforms + st * K,
-                                       at<double>(ws, P.P), at<int32_t>(ws, P.donor), s),
+                                       at<int32_t>(ws, P.list_j), at<int32_t>(ws, P.list_k), s),
                    "split");
     }
     KM_HIP(launch_emeans_final(F, G, K, (int)d, centroids, counts, s), "final mean");

@@ -124,9 +124,13 @@ __device__ __forceinline__ typename Mf<T>::frag load_point_frag(const T* row, in
     }
 }
 
-template <typename T, int DP>
+// 32-point column blocks per wave: two where rows are short (each A fragment
+// read from LDS feeds two MFMAs), one for long rows.
+constexpr int default_ncb(int DP, int elem_bytes) { return DP * elem_bytes <= 512 ? 2 : 1; }
+
+template <typename T, int DP, int NCBT = default_ncb(DP, sizeof(T))>
 struct AssignCfg {
-    static constexpr int NCB = (DP * (int)sizeof(T) <= 512) ? 2 : 1;   // 32-point blocks per wave
+    static constexpr int NCB = NCBT;                                      // 32-point blocks per wave
     static constexpr int WAVES = assign_waves(DP, sizeof(T));
     static constexpr int PTS = WAVES * NCB * 32;                         // points per block
     static constexpr int TK = tile_rows(DP, sizeof(T));                   // centroid rows per tile
@@ -194,12 +198,12 @@ __device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave
     }
 }
 
-template <typename T, int DP, bool VEC>
+template <typename T, int DP, bool VEC, int NCBT>
 __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfma(
     const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int64_t ntiles,
     const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
     double* __restrict__ obj_part, int64_t gpb, int64_t ngroups) {
-    typedef AssignCfg<T, DP> Cfg;
+    typedef AssignCfg<T, DP, NCBT> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
     constexpr int NCB = Cfg::NCB, TK = Cfg::TK, RB = Cfg::RB, KSTEPS = Cfg::KSTEPS, NRB = Cfg::NRB;
@@ -471,39 +475,42 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
+// Column blocks per wave for a launch: the default, unless the default
+// leaves fewer point groups than the chip has compute units (a mini-batch
+// against many centroids); then one, which doubles the groups, each reading
+// the centroid tiles for half as many points.
+constexpr int64_t kFewGroups = 256;
+
 template <typename T>
-static int64_t blocks_for(int64_t N, int DP) {
-    int pts = 0;
-    switch (DP) {
-        case 16: pts = AssignCfg<T, 16>::PTS; break;
-        case 32: pts = AssignCfg<T, 32>::PTS; break;
-        case 64: pts = AssignCfg<T, 64>::PTS; break;
-        case 128: pts = AssignCfg<T, 128>::PTS; break;
-        case 256: pts = AssignCfg<T, 256>::PTS; break;
-        default:
-            if constexpr (sizeof(T) == 2) pts = AssignCfg<T, 512>::PTS;
-            else pts = AssignCfg<T, 256>::PTS;  // float32 rows stop at 256 (checked by the caller)
-            break;
-    }
+static int ncb_for(int64_t B, int64_t N, int DP) {
+    const int def = default_ncb(DP, sizeof(T));
+    if (def == 1) return 1;
+    const int64_t pts = (int64_t)assign_waves(DP, sizeof(T)) * def * 32;
+    return B * ((N + pts - 1) / pts) < kFewGroups ? 1 : def;
+}
+
+template <typename T>
+static int64_t blocks_for(int64_t B, int64_t N, int DP) {
+    const int64_t pts = (int64_t)assign_waves(DP, sizeof(T)) * ncb_for<T>(B, N, DP) * 32;
     return (N + pts - 1) / pts;
 }
 
-int64_t assign_mfma_blocks(int64_t N, int DP, DType xt) {
-    if (xt == DType::F32) return blocks_for<float>(N, DP);
-    if (xt == DType::F16) return blocks_for<_Float16>(N, DP);
-    return blocks_for<bf16_t>(N, DP);
+int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt) {
+    if (xt == DType::F32) return blocks_for<float>(B, N, DP);
+    if (xt == DType::F16) return blocks_for<_Float16>(B, N, DP);
+    return blocks_for<bf16_t>(B, N, DP);
 }
 
 // Persistent blocks: as many as the device holds at once (compute units x
 // resident blocks per unit), each walking groups i, i + grid, ...
-template <typename T, int DP, bool VEC>
+template <typename T, int DP, bool VEC, int NCBT>
 static int64_t resident_blocks() {
     static int64_t n = 0;
     if (n == 0) {
         int dev = 0, cus = 0, per = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC>,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC, NCBT>,
                                                          64 * AssignCfg<T, DP>::WAVES, 0) != hipSuccess ||
             cus <= 0 || per <= 0)
             return 256;
@@ -512,21 +519,38 @@ static int64_t resident_blocks() {
     return n;
 }
 
+template <typename T, int DP, int NCBT>
+static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const void* blob, int64_t ntiles,
+                           const float* w, int32_t* labels, float* min_dist, double* obj_part, int64_t nblk,
+                           hipStream_t s) {
+    const int64_t ngroups = B * nblk;
+    const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
+    const int64_t P = vec ? resident_blocks<T, DP, true, NCBT>() : resident_blocks<T, DP, false, NCBT>();
+    dim3 grid((unsigned)(ngroups < P ? ngroups : P));
+    if (vec)
+        hipLaunchKernelGGL((k_assign_mfma<T, DP, true, NCBT>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s,
+                           (const T*)x, N, d, (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk,
+                           ngroups);
+    else
+        hipLaunchKernelGGL((k_assign_mfma<T, DP, false, NCBT>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s,
+                           (const T*)x, N, d, (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk,
+                           ngroups);
+    return hipGetLastError();
+}
+
+// nblk: point groups per problem, as assign_mfma_blocks(B, N, DP, xt) gives
+// them (the column blocks per wave follow from the same rule).
 template <typename T, int DP>
 static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
                            double* obj_part, int64_t nblk, hipStream_t s) {
-    const int64_t ngroups = B * nblk;
-    const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
-    const int64_t P = vec ? resident_blocks<T, DP, true>() : resident_blocks<T, DP, false>();
-    dim3 grid((unsigned)(ngroups < P ? ngroups : P));
-    if (vec)
-        hipLaunchKernelGGL((k_assign_mfma<T, DP, true>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s, (const T*)x, N, d,
-                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
-    else
-        hipLaunchKernelGGL((k_assign_mfma<T, DP, false>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s, (const T*)x, N, d,
-                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
-    return hipGetLastError();
+    if (nblk != blocks_for<T>(B, N, DP)) return hipErrorInvalidValue;
+    constexpr int DEF = default_ncb(DP, sizeof(T));
+    if constexpr (DEF == 2) {
+        if (ncb_for<T>(B, N, DP) == 1)
+            return launch_n<T, DP, 1>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+    }
+    return launch_n<T, DP, DEF>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
 }
 
 template <typename T>

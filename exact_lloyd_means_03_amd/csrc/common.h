@@ -93,7 +93,7 @@ hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, in
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
                               float* min_dist, double* obj_part, int64_t nblk, hipStream_t s);
-int64_t assign_mfma_blocks(int64_t N, int DP, DType xt);
+int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt);
 
 // obj_part (may be NULL): the objective partial of block j of row b goes to
 // obj_part[b * obj_stride + j].
@@ -160,7 +160,7 @@ hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_
                              float* C, double* F, double* G, hipStream_t st);
 bool emeans_split_supports(int64_t K);
 hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d, double dead_below, double eps,
-                               const float* u, double* P, int32_t* donor, hipStream_t st);
+                               const float* u, int32_t* list_j, int32_t* list_k, hipStream_t st);
 hipError_t launch_emeans_final(const double* F, const double* G, int64_t K, int d, float* C, int32_t* counts,
                                hipStream_t st);
 

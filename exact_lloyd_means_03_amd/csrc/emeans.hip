@@ -61,89 +61,150 @@ hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_
 // same, and the centroids become c_k (1 + eps sgn) and c_k (1 - eps sgn),
 // sgn = +1 on even and -1 on odd coordinates (S rescaled to match).
 //
-// Since the prefix is taken before any split, every donor can be found at
-// once.  Split j touches only rows j and k_j, so splits run in rounds: in a
-// round, a split goes ahead when it is the lowest pending split touching
-// each of its two rows; splits of one round touch disjoint rows, and every
-// lower split that shares a row with it has run in an earlier round, which
-// gives the ascending order's result.  One block; P [K+1] and donor [K]
-// are scratch in global memory (donor[j] is only ever touched by the thread
-// of j), the lowest pending split of every row is kept in LDS.
+// One block.  Thread t owns the clusters [t*per, t*per + per): it sums
+// their N and counts its dead ones, and a block scan gives every range its
+// exclusive prefix of N (kept in LDS) and the position of its dead clusters
+// in a list that comes out in ascending order.  Since the prefix is taken
+// before any split, every donor is found at once: a binary search over the
+// ranges' end prefixes in LDS, then the prefix within the range, summed in
+// the same order as the scan.  Split j touches only rows j and k_j, so the
+// splits run in rounds: in a round, a split goes ahead when it is the lowest
+// pending split touching each of its two rows; splits of one round touch
+// disjoint rows, and every lower split that shares a row with it has run in
+// an earlier round, which gives the ascending order's result.  The list of
+// (j, k_j) is scratch in global memory, each entry only ever touched by the
+// thread i % 1024 of its position i; the lowest pending split of every row
+// is kept in LDS.
 constexpr int kSplitThreads = 1024;
 constexpr int kSplitWaves = kSplitThreads / 64;
+constexpr int kSplitPer = (int)(kEmeansMaxK / kSplitThreads);  // clusters per thread at most
+
+template <typename V>
+__device__ __forceinline__ V block_exclusive_scan(V v, V* s_part, V* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    V incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const V t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_part[wave] = incl;
+    __syncthreads();
+    V run = incl - v;
+    V all = 0;
+    for (int w = 0; w < kSplitWaves; ++w) {
+        if (w < wave) run += s_part[w];
+        all += s_part[w];
+    }
+    *total = all;
+    return run;
+}
 
 __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S, double* __restrict__ Nc,
                                                          float* __restrict__ C, int64_t K, int d,
                                                          double dead_below, double eps,
-                                                         const float* __restrict__ u, double* __restrict__ P,
-                                                         int32_t* __restrict__ donor) {
+                                                         const float* __restrict__ u,
+                                                         int32_t* __restrict__ list_j, int32_t* __restrict__ list_k) {
     extern __shared__ int owner[];  // [K]
-    __shared__ double s_part[kSplitWaves];
+    __shared__ double s_dpart[kSplitWaves];
+    __shared__ int s_ipart[kSplitWaves];
+    __shared__ double s_start[kSplitThreads], s_end[kSplitThreads];
     __shared__ int s_wcnt[kSplitWaves];
-    __shared__ int s_list[kSplitThreads];
-    __shared__ int s_donor[kSplitThreads];
+    __shared__ int s_lj[kSplitThreads], s_lk[kSplitThreads];
     __shared__ int s_n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // exclusive prefix of N: thread t owns a contiguous range
-    const int64_t per = (K + kSplitThreads - 1) / kSplitThreads;
-    const int64_t j0 = tid * per < K ? tid * per : K, j1 = j0 + per < K ? j0 + per : K;
+    const int per = (int)((K + kSplitThreads - 1) / kSplitThreads);
+    const int64_t j0 = (int64_t)tid * per < K ? (int64_t)tid * per : K;
+    const int64_t j1 = j0 + per < K ? j0 + per : K;
+    double v[kSplitPer];
     double sum = 0.0;
-    for (int64_t j = j0; j < j1; ++j) sum += Nc[j];
-    double incl = sum;
+    int ndead = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
+    for (int i = 0; i < kSplitPer; ++i) {
+        v[i] = (i < per && j0 + i < j1) ? Nc[j0 + i] : 0.0;
     }
-    if (lane == 63) s_part[wave] = incl;
-    __syncthreads();
-    double run = incl - sum;
-    for (int v = 0; v < wave; ++v) run += s_part[v];
-    for (int64_t j = j0; j < j1; ++j) {
-        P[j] = run;
-        run += Nc[j];
+#pragma unroll
+    for (int i = 0; i < kSplitPer; ++i) {
+        if (i < per && j0 + i < j1) {
+            sum += v[i];
+            ndead += v[i] < dead_below;
+        }
     }
-    if (tid == kSplitThreads - 1) P[K] = run;  // the last thread's range ends at K
+    double total;
+    const double start = block_exclusive_scan(sum, s_dpart, &total);
+    __syncthreads();  // s_dpart is reused below
+    int ndead_all;
+    int pos = block_exclusive_scan(ndead, s_ipart, &ndead_all);
+    if (ndead_all == 0) return;  // uniform: the same total in every thread
+    // range t's prefix after its last cluster, formed as the searches below form it
+    double run = start;
+#pragma unroll
+    for (int i = 0; i < kSplitPer; ++i) {
+        if (i < per && j0 + i < j1) {
+            run += v[i];
+            if (v[i] < dead_below) list_j[pos++] = (int)(j0 + i);
+        }
+    }
+    s_start[tid] = start;
+    s_end[tid] = run;
     __syncthreads();
-    const double total = P[K];
-    // donors of the dead clusters (-1: nothing to do)
+    // donors (list_k = -1: nothing to do)
     int pending = 0;
-    for (int64_t j = tid; j < K; j += kSplitThreads) {
-        int dj = -1;
-        if (Nc[j] < dead_below) {
-            const double target = (double)u[j] * total;
-            int64_t lo = 0, len = K;  // first k with P[k + 1] > target (the last cluster if none)
-            while (len > 0) {
-                const int64_t h = len >> 1;
-                if (!(P[lo + h + 1] > target)) {
-                    lo += h + 1;
-                    len -= h + 1;
-                } else {
-                    len = h;
+    for (int i = tid; i < ndead_all; i += kSplitThreads) {
+        const int j = list_j[i];
+        const double target = (double)u[j] * total;
+        // first range whose end prefix exceeds the target
+        int lo = 0, len = kSplitThreads;
+        while (len > 0) {
+            const int h = len >> 1;
+            if (!(s_end[lo + h] > target)) {
+                lo += h + 1;
+                len -= h + 1;
+            } else {
+                len = h;
+            }
+        }
+        int64_t k = K - 1;  // the last cluster if no prefix exceeds the target
+        if (lo < kSplitThreads) {
+            const int64_t a0 = (int64_t)lo * per, a1 = a0 + per < K ? a0 + per : K;
+            double r = s_start[lo];
+            k = a1 - 1;
+            for (int64_t q = a0; q < a1; ++q) {
+                r += Nc[q];
+                if (r > target) {
+                    k = q;
+                    break;
                 }
             }
-            const int64_t k = lo < K ? lo : K - 1;
-            dj = k == j ? -1 : (int)k;
         }
-        donor[j] = dj;
+        const int dj = k == j ? -1 : (int)k;
+        list_k[i] = dj;
         pending |= dj >= 0;
     }
     while (__syncthreads_or(pending)) {
-        for (int64_t j = tid; j < K; j += kSplitThreads) owner[j] = 0x7fffffff;
-        __syncthreads();
-        for (int64_t j = tid; j < K; j += kSplitThreads) {
-            const int k = donor[j];
+        for (int i = tid; i < ndead_all; i += kSplitThreads) {
+            const int k = list_k[i];
             if (k >= 0) {
-                atomicMin(&owner[j], (int)j);
-                atomicMin(&owner[k], (int)j);
+                owner[list_j[i]] = 0x7fffffff;
+                owner[k] = 0x7fffffff;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < ndead_all; i += kSplitThreads) {
+            const int k = list_k[i];
+            if (k >= 0) {
+                const int j = list_j[i];
+                atomicMin(&owner[j], j);
+                atomicMin(&owner[k], j);
             }
         }
         __syncthreads();
         pending = 0;
-        for (int64_t base = 0; base < K; base += kSplitThreads) {
-            const int64_t j = base + tid;
-            const int k = j < K ? donor[j] : -1;
-            const bool ready = k >= 0 && owner[j] == (int)j && owner[k] == (int)j;
+        for (int base = 0; base < ndead_all; base += kSplitThreads) {
+            const int i = base + tid;
+            const int k = i < ndead_all ? list_k[i] : -1;
+            const int j = k >= 0 ? list_j[i] : -1;
+            const bool ready = k >= 0 && owner[j] == j && owner[k] == j;
             pending |= k >= 0 && !ready;
             // the window's ready splits, listed in LDS
             const unsigned long long mask = __ballot(ready);
@@ -151,14 +212,14 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
             __syncthreads();
             if (ready) {
                 int r = __popcll(mask & ((1ull << lane) - 1ull));
-                for (int v = 0; v < wave; ++v) r += s_wcnt[v];
-                s_list[r] = (int)j;
-                s_donor[r] = k;
-                donor[j] = -1;
+                for (int w = 0; w < wave; ++w) r += s_wcnt[w];
+                s_lj[r] = j;
+                s_lk[r] = k;
+                list_k[i] = -1;
             }
             if (tid == 0) {
                 int c = 0;
-                for (int v = 0; v < kSplitWaves; ++v) c += s_wcnt[v];
+                for (int w = 0; w < kSplitWaves; ++w) c += s_wcnt[w];
                 s_n = c;
             }
             __syncthreads();
@@ -166,7 +227,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
             if (n == 0) continue;  // uniform: s_n is the same for every thread
             for (int q = tid; q < n * d; q += kSplitThreads) {
                 const int r = q / d, c = q - r * d;
-                const int64_t jd = s_list[r], kd = s_donor[r];
+                const int64_t jd = s_lj[r], kd = s_lk[r];
                 const double nkc = Nc[kd];
                 if (!(nkc > 0.0)) continue;  // an empty donor: nothing moves
                 const double nk = nkc * 0.5;
@@ -181,7 +242,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
             }
             __syncthreads();  // every coordinate read the donor's old N before it changes
             if (tid < n) {
-                const int64_t jd = s_list[tid], kd = s_donor[tid];
+                const int64_t jd = s_lj[tid], kd = s_lk[tid];
                 const double nkc = Nc[kd];
                 if (nkc > 0.0) {
                     Nc[kd] = nkc * 0.5;
@@ -196,7 +257,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
 bool emeans_split_supports(int64_t K) { return K >= 1 && K <= kEmeansMaxK; }
 
 hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d, double dead_below, double eps,
-                               const float* u, double* P, int32_t* donor, hipStream_t st) {
+                               const float* u, int32_t* list_j, int32_t* list_k, hipStream_t st) {
     if (!emeans_split_supports(K)) return hipErrorInvalidValue;
     static bool attr = false;
     if (!attr) {
@@ -206,7 +267,7 @@ hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d
         attr = true;
     }
     hipLaunchKernelGGL(k_split, dim3(1), dim3(kSplitThreads), (size_t)K * sizeof(int), st, S, Nc, C, K, d,
-                       dead_below, eps, u, P, donor);
+                       dead_below, eps, u, list_j, list_k);
     return hipGetLastError();
 }
 

@@ -23,6 +23,12 @@
 // lines, which are merged in L2 before they reach HBM.
 // Runs of different chunks land in a segment in arrival order, so the order
 // inside a segment is unspecified; the set of indices is exact.
+//
+// Few labels per cluster (N <= 16 K, as in a mini-batch against many
+// clusters) would leave the chunked passes with a handful of blocks, each
+// walking all K bins with a chain of dependent atomics.  There every label
+// takes its own global atomic instead (k_count_direct, k_scatter_direct),
+// one thread per label over the whole grid.
 // Labels outside [0, K) are skipped by every pass.
 #include "common.h"
 
@@ -172,6 +178,29 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(const int32_t* __restr
     for (; i < i1; i += kSortThreads) place(i, L[i]);
 }
 
+constexpr int kDirectThreads = 256;
+
+static bool sort_direct(int64_t N, int64_t K) { return N <= 16 * K; }
+
+__global__ __launch_bounds__(kDirectThreads) void k_count_direct(const int32_t* __restrict__ labels, int64_t N,
+                                                                 int K, int32_t* __restrict__ counts) {
+    const int64_t b = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * kDirectThreads + threadIdx.x;
+    if (i >= N) return;
+    const int32_t l = labels[b * N + i];
+    if ((uint32_t)l < (uint32_t)K) atomicAdd(&counts[b * K + l], 1);
+}
+
+__global__ __launch_bounds__(kDirectThreads) void k_scatter_direct(const int32_t* __restrict__ labels, int64_t N,
+                                                                   int K, int32_t* __restrict__ cursor,
+                                                                   int32_t* __restrict__ perm) {
+    const int64_t b = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * kDirectThreads + threadIdx.x;
+    if (i >= N) return;
+    const int32_t l = labels[b * N + i];
+    if ((uint32_t)l < (uint32_t)K) perm[b * N + atomicAdd(&cursor[b * K + l], 1)] = (int32_t)i;
+}
+
 static hipError_t set_lds(const void* f, size_t bytes) {
     if (bytes <= 64 * 1024) return hipSuccess;
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -184,7 +213,12 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, i
     if (B == 0) return hipSuccess;
     const size_t lds = (size_t)K * sizeof(int32_t);
     hipError_t e;
-    if (N > 0) {
+    const bool direct = sort_direct(N, K);
+    const dim3 dgrid((unsigned)((N + kDirectThreads - 1) / kDirectThreads), (unsigned)B);
+    if (N > 0 && direct) {
+        hipLaunchKernelGGL(k_count_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, counts);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (N > 0) {
         if ((e = set_lds((const void*)k_count, lds)) != hipSuccess) return e;
         const int64_t CH = sort_chunk(B, N, K);
         dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
@@ -196,7 +230,10 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, i
     hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), scan_lds, s, counts, (int)K, offsets, cursor, TW,
                        npieces, piece_seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (N > 0) {
+    if (N > 0 && direct) {
+        hipLaunchKernelGGL(k_scatter_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, cursor, perm);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (N > 0) {
         if ((e = set_lds((const void*)k_scatter, lds)) != hipSuccess) return e;
         const int64_t CH = sort_chunk(B, N, K);
         dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);

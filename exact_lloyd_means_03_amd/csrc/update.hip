@@ -309,6 +309,8 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
 int segreduce_tw(int64_t B, int64_t N) {
     int64_t tw = 256;
     while (tw < 4096 && B * N / (tw * 2) >= 8192) tw *= 2;
+    // small jobs: shorter pieces, so that enough waves share the segments
+    while (tw > 32 && B * N / tw < 2048) tw /= 2;
     return (int)tw;
 }
 
