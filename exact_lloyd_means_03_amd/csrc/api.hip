@@ -43,7 +43,7 @@ static bool use_update_1d(DType xt, const void* x, const float* w, const int32_t
 
 Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     Workspace w{};
-    w.DP = padded_dim(d);
+    w.DP = padded_dim(d, xt != DType::F32);
     w.Kp = padded_k(K);
     const bool a1d = use_assign_1d(d, K);
     w.nblk_assign = a1d ? assign_1d_blocks(N) : assign_mfma_blocks(B, N, w.DP, xt);
@@ -527,7 +527,7 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
                                piece_seg, s),
                    "sort");
             KM_HIP(launch_segreduce_tw(t, xb, wb, 1, nc, (int)d, perm, offsets, K, sums, wsum, piece_seg,
-                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, s),
+                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, true, s),
                    "segreduce");
             KM_HIP(launch_add_i32(ctot, cnt, K, s), "add counts");
             KM_HIP(hipEventRecord(R->consumed[buf], s), "event");
@@ -597,6 +597,10 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
     // batch never has more pieces than the plan holds
     const int TW = segreduce_tw(1, P.mfull);
     const double dead_below = dead_frac * (double)P.mfull / (double)K;
+    // the batch's sums and counts start at zero; the moving average clears
+    // them after every batch
+    KM_HIP(launch_zero(sums, (size_t)K * d * sizeof(float), s), "zero");
+    KM_HIP(launch_zero(cnt, (size_t)K * sizeof(int32_t), s), "zero");
     for (int64_t st = 0; st < P.steps; ++st) {
         const int64_t e = st / P.nb, i0 = (st % P.nb) * batch;
         const int64_t m = (i0 + batch <= N) ? batch : N - i0;
@@ -616,13 +620,11 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
                    "assign_mfma");
         }
         if (objective) KM_HIP(launch_obj_reduce(part, 1, nblk, objective + st, 1, s), "obj_reduce");
-        KM_HIP(launch_zero(sums, (size_t)K * d * sizeof(float), s), "zero");
-        KM_HIP(launch_zero(cnt, (size_t)K * sizeof(int32_t), s), "zero");
         KM_HIP(launch_sort(lab, 1, m, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (m + TW - 1) / TW,
                            piece_seg, s),
                "sort");
         KM_HIP(launch_segreduce_tw(t, xb, nullptr, 1, m, (int)d, perm, offsets, K, sums, nullptr, piece_seg,
-                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, s),
+                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, false, s),
                "segreduce");
         const double a = emeans_step_size(alpha0, floor_frac, st, P.steps);
         KM_HIP(launch_emeans_ema(S, Nc, sums, cnt, K, (int)d, a, centroids, last ? F : nullptr, last ? G : nullptr,

@@ -139,6 +139,7 @@ struct AssignCfg {
     static constexpr int RB = DP * (int)sizeof(T);                       // bytes per centroid row
     static constexpr int CPR = RB / 16;                                   // 16-byte chunks per row
     static constexpr int SW = CPR < 32 ? CPR : 32;                        // XOR swizzle period (rows)
+    static constexpr bool XOR = (CPR & (CPR - 1)) == 0;                   // else the rotation swizzle
     static constexpr int TILE = tile_bytes(DP, sizeof(T));                // rows + the -|c|^2/2 floats
     static constexpr int NR = TK * RB / 1024;                             // 1 KB DMA instructions of rows
     static constexpr int HN_LANES = TK * 4 / 16;                          // lanes of the -|c|^2/2 instruction
@@ -167,19 +168,37 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, const vo
                  : "memory");
 }
 
+// LDS chunk position of global 16-byte chunk c of tile row r.  Rows of a
+// power-of-two number of chunks are XOR-swizzled, c ^ (r % SW) with SW =
+// min(chunks per row, 32), so the 32 rows read by one A-operand instruction
+// hit distinct banks without padding.  Rows of 12 chunks (96 16-bit
+// elements, 192 bytes) start on banks that repeat every 4 rows; they are
+// rotated by (r % 32) / 4 chunks, which puts the 16 rows read in one LDS
+// phase (4 row starts x 4 rotations) on distinct 16-byte bank groups.
+// Either way the swizzle of row r depends only on r % 32.
+template <typename Cfg>
+__device__ __forceinline__ int lds_chunk(int c, int r) {
+    if constexpr (Cfg::XOR) return c ^ (r % Cfg::SW);
+    else return (c + ((r & 31) >> 2)) % Cfg::CPR;
+}
+
+// The global chunk that LDS chunk position q of row r holds (the inverse).
+template <typename Cfg>
+__device__ __forceinline__ int global_chunk(int q, int r) {
+    if constexpr (Cfg::XOR) return q ^ (r % Cfg::SW);
+    else return (q + Cfg::CPR - ((r & 31) >> 2)) % Cfg::CPR;
+}
+
 // Source offset (within a tile) of the 16 bytes lane `lane` copies with the
-// DMA instruction i.  Row chunks are XOR-swizzled: LDS chunk position q of
-// row r holds global chunk q ^ (r % SW), SW = min(chunks per row, 32), so the
-// 32 rows read by one A-operand instruction hit distinct banks without
-// padding, and the swizzle of row r depends only on r % 32.  Bytes past the
-// rows (the -|c|^2/2 segment and padding) are copied unchanged.
+// DMA instruction i (the LDS side is contiguous).  Bytes past the rows (the
+// -|c|^2/2 segment and padding) are copied unchanged.
 template <typename T, int DP>
 __device__ __forceinline__ uint32_t dma_src(int i, int lane) {
     typedef AssignCfg<T, DP> Cfg;
     const int p = i * 1024 + lane * 16;
     if (p >= Cfg::TK * Cfg::RB) return (uint32_t)p;
     const int r = p / Cfg::RB, q = (p % Cfg::RB) / 16;
-    return (uint32_t)(r * Cfg::RB + ((q ^ (r % Cfg::SW)) * 16));
+    return (uint32_t)(r * Cfg::RB + global_chunk<Cfg>(q, r) * 16);
 }
 
 // Copy one tile (global bytes tile_g) into LDS buffer dst: wave w issues the
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
         const int ob = (ks * M::KS + half * M::EPL) * (int)sizeof(T);
-        aoff[ks] = col * RB + (((ob / 16) ^ (col % Cfg::SW)) * 16) + (ob % 16);
+        aoff[ks] = col * RB + lds_chunk<Cfg>(ob / 16, col) * 16 + (ob % 16);
     }
 
     // Epilogue of a finished 32-row block, cut into 8 pieces of 3-4 VALU
@@ -561,6 +580,11 @@ static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, 
         case 16: return launch_t<T, 16>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         case 32: return launch_t<T, 32>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         case 64: return launch_t<T, 64>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 96:
+            if constexpr (sizeof(T) == 2)
+                return launch_t<T, 96>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+            else
+                return hipErrorInvalidValue;
         case 128: return launch_t<T, 128>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         case 256: return launch_t<T, 256>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
         case 512:

@@ -20,11 +20,14 @@ typedef uint16_t bf16_t;  // bfloat16 bits in memory
 
 constexpr int kWave = 64;
 
-// Padded point dimension used by the matrix-core assignment for a given d.
-inline int padded_dim(int64_t d) {
+// Padded point dimension used by the matrix-core assignment for a given d:
+// powers of two, and 96 for 16-bit points (six 16-deep k-steps; the rows of
+// 12 16-byte chunks take a rotation swizzle in LDS instead of the XOR one).
+inline int padded_dim(int64_t d, bool wide16) {
     if (d <= 16) return 16;
     if (d <= 32) return 32;
     if (d <= 64) return 64;
+    if (wide16 && d <= 96) return 96;
     if (d <= 128) return 128;
     if (d <= 256) return 256;
     return 512;
@@ -115,15 +118,18 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
                        int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* perm,
                        int TW, int64_t npieces, int32_t* piece_seg, hipStream_t s);
 
+// Segment sums of the sorted points (sums / wsum must be zero on entry).
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K,
                             float* sums, float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
                             hipStream_t s);
 // The same with a given piece width TW (the sort must have used the same).
+// accumulate: add into sums / wsum that hold earlier contributions (else
+// they must be zero on entry, and complete segments are stored).
 hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                                const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                                float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
-                               hipStream_t s);
+                               bool accumulate, hipStream_t s);
 int64_t segreduce_pieces(int64_t B, int64_t N);
 int segreduce_tw(int64_t B, int64_t N);
 
@@ -156,8 +162,9 @@ hipError_t launch_optimal_1d(DType xt, const void* x, const float* w, int64_t B,
 
 // e-means state updates (float64 sums S [K][d] and counts N [K]).
 constexpr int64_t kEmeansMaxK = 32768;  // the split keeps one int per cluster in LDS
-hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_t* n, int64_t K, int d, double a,
-                             float* C, double* F, double* G, hipStream_t st);
+// Clears s and n after reading them.
+hipError_t launch_emeans_ema(double* S, double* Nc, float* s, int32_t* n, int64_t K, int d, double a, float* C,
+                             double* F, double* G, hipStream_t st);
 bool emeans_split_supports(int64_t K);
 hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d, double dead_below, double eps,
                                const float* u, int32_t* list_j, int32_t* list_k, hipStream_t st);

@@ -11,44 +11,38 @@
 namespace km {
 
 // S = (1 - a) S + a s, N = (1 - a) N + a n, c = S / N where N > 0.  With
-// `final` the batch's sums and counts are also added to the last-epoch
-// totals F, G.  One thread per (cluster, coordinate); the count by the
-// thread of coordinate 0.
+// F and G (the last epoch) the batch's sums and counts are also added to the
+// last-epoch totals.  One wave per cluster, lanes over coordinates.  The
+// batch's sums and count are cleared once read, ready for the next batch.
 __global__ __launch_bounds__(256) void k_ema(double* __restrict__ S, double* __restrict__ Nc,
-                                             const float* __restrict__ s, const int32_t* __restrict__ n,
-                                             int64_t K, int d, double a, float* __restrict__ C,
-                                             double* __restrict__ F, double* __restrict__ G) {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= K * d) return;
-    const int64_t j = q / d;
-    const double nj = (double)n[j];
-    const double Nn = (1.0 - a) * Nc[j] + a * nj;  // every thread of cluster j forms the same value
-    const double Sn = (1.0 - a) * S[q] + a * (double)s[q];
-    S[q] = Sn;
-    if (Nn > 0.0) C[q] = (float)(Sn / Nn);
-    if (F) {
-        F[q] += (double)s[q];
-        if (q % d == 0) G[j] += nj;
+                                             float* __restrict__ s, int32_t* __restrict__ n, int64_t K, int d,
+                                             double a, float* __restrict__ C, double* __restrict__ F,
+                                             double* __restrict__ G) {
+    const int lane = threadIdx.x & 63;
+    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= K) return;
+    const int32_t nj = n[j];
+    const double Nn = (1.0 - a) * Nc[j] + a * (double)nj;
+    for (int c = lane; c < d; c += 64) {
+        const int64_t q = j * d + c;
+        const float sq = s[q];
+        const double Sn = (1.0 - a) * S[q] + a * (double)sq;
+        S[q] = Sn;
+        if (Nn > 0.0) C[q] = (float)(Sn / Nn);
+        if (F) F[q] += (double)sq;
+        s[q] = 0.f;
+    }
+    if (lane == 0) {  // every lane has read n[j] and Nc[j] above
+        Nc[j] = Nn;
+        if (G) G[j] += (double)nj;
+        n[j] = 0;
     }
 }
 
-// The new counts, in a launch of their own: every coordinate thread of
-// k_ema reads the old count of its cluster.
-__global__ __launch_bounds__(256) void k_ema_counts(double* __restrict__ Nc, const int32_t* __restrict__ n,
-                                                    int64_t K, double a) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j < K) Nc[j] = (1.0 - a) * Nc[j] + a * (double)n[j];
-}
-
-hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_t* n, int64_t K, int d, double a,
-                             float* C, double* F, double* G, hipStream_t st) {
-    const int64_t total = K * d;
-    if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_ema, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, S, Nc, s, n, K, d, a, C, F,
-                       G);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ema_counts, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, Nc, n, K, a);
+hipError_t launch_emeans_ema(double* S, double* Nc, float* s, int32_t* n, int64_t K, int d, double a, float* C,
+                             double* F, double* G, hipStream_t st) {
+    if (K == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_ema, dim3((unsigned)((K + 3) / 4)), dim3(256), 0, st, S, Nc, s, n, K, d, a, C, F, G);
     return hipGetLastError();
 }
 
@@ -66,8 +60,7 @@ hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_
 // exclusive prefix of N (kept in LDS) and the position of its dead clusters
 // in a list that comes out in ascending order.  Since the prefix is taken
 // before any split, every donor is found at once: a binary search over the
-// ranges' end prefixes in LDS, then the prefix within the range, summed in
-// the same order as the scan.  Split j touches only rows j and k_j, so the
+// ranges' start prefixes in LDS, then the prefix within the range.  Split j touches only rows j and k_j, so the
 // splits run in rounds: in a round, a split goes ahead when it is the lowest
 // pending split touching each of its two rows; splits of one round touch
 // disjoint rows, and every lower split that shares a row with it has run in
@@ -78,6 +71,8 @@ hipError_t launch_emeans_ema(double* S, double* Nc, const float* s, const int32_
 constexpr int kSplitThreads = 1024;
 constexpr int kSplitWaves = kSplitThreads / 64;
 constexpr int kSplitPer = (int)(kEmeansMaxK / kSplitThreads);  // clusters per thread at most
+constexpr int kSplitU = 8;  // coordinates per thread in flight when splitting
+constexpr int kSplitL = 8;  // counts per thread in flight when scanning a range
 
 template <typename V>
 __device__ __forceinline__ V block_exclusive_scan(V v, V* s_part, V* total) {
@@ -108,56 +103,58 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
     extern __shared__ int owner[];  // [K]
     __shared__ double s_dpart[kSplitWaves];
     __shared__ int s_ipart[kSplitWaves];
-    __shared__ double s_start[kSplitThreads], s_end[kSplitThreads];
+    __shared__ double s_start[kSplitThreads + 1];
     __shared__ int s_wcnt[kSplitWaves];
     __shared__ int s_lj[kSplitThreads], s_lk[kSplitThreads];
+    __shared__ double s_nk[kSplitThreads];
     __shared__ int s_n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int per = (int)((K + kSplitThreads - 1) / kSplitThreads);
     const int64_t j0 = (int64_t)tid * per < K ? (int64_t)tid * per : K;
     const int64_t j1 = j0 + per < K ? j0 + per : K;
-    double v[kSplitPer];
+    // every thread loads `per` counts (per is the same for all, so the loads
+    // are not predicated and issue together); past K the index is clamped and
+    // the value ignored
+    static_assert(kSplitPer <= 32 && kSplitPer % kSplitL == 0, "one bit per cluster of a range");
     double sum = 0.0;
-    int ndead = 0;
+    uint32_t deadm = 0;  // bit i: cluster j0 + i is dead
+    for (int i0 = 0; i0 < per; i0 += kSplitL) {
+        double v[kSplitL];
 #pragma unroll
-    for (int i = 0; i < kSplitPer; ++i) {
-        v[i] = (i < per && j0 + i < j1) ? Nc[j0 + i] : 0.0;
-    }
+        for (int i = 0; i < kSplitL; ++i) v[i] = Nc[j0 + i0 + i < K ? j0 + i0 + i : K - 1];
 #pragma unroll
-    for (int i = 0; i < kSplitPer; ++i) {
-        if (i < per && j0 + i < j1) {
-            sum += v[i];
-            ndead += v[i] < dead_below;
+        for (int i = 0; i < kSplitL; ++i) {
+            if (i0 + i < per && j0 + i0 + i < j1) {
+                sum += v[i];
+                deadm |= (uint32_t)(v[i] < dead_below) << (i0 + i);
+            }
         }
     }
+    const int ndead = __popc(deadm);
     double total;
     const double start = block_exclusive_scan(sum, s_dpart, &total);
     __syncthreads();  // s_dpart is reused below
     int ndead_all;
     int pos = block_exclusive_scan(ndead, s_ipart, &ndead_all);
     if (ndead_all == 0) return;  // uniform: the same total in every thread
-    // range t's prefix after its last cluster, formed as the searches below form it
-    double run = start;
-#pragma unroll
-    for (int i = 0; i < kSplitPer; ++i) {
-        if (i < per && j0 + i < j1) {
-            run += v[i];
-            if (v[i] < dead_below) list_j[pos++] = (int)(j0 + i);
-        }
+    while (deadm) {  // ascending
+        const int i = __ffs(deadm) - 1;
+        deadm &= deadm - 1;
+        list_j[pos++] = (int)(j0 + i);
     }
     s_start[tid] = start;
-    s_end[tid] = run;
+    if (tid == 0) s_start[kSplitThreads] = total;
     __syncthreads();
     // donors (list_k = -1: nothing to do)
     int pending = 0;
     for (int i = tid; i < ndead_all; i += kSplitThreads) {
         const int j = list_j[i];
         const double target = (double)u[j] * total;
-        // first range whose end prefix exceeds the target
+        // first range whose end (the next range's start) exceeds the target
         int lo = 0, len = kSplitThreads;
         while (len > 0) {
             const int h = len >> 1;
-            if (!(s_end[lo + h] > target)) {
+            if (!(s_start[lo + h + 1] > target)) {
                 lo += h + 1;
                 len -= h + 1;
             } else {
@@ -168,12 +165,21 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
         if (lo < kSplitThreads) {
             const int64_t a0 = (int64_t)lo * per, a1 = a0 + per < K ? a0 + per : K;
             double r = s_start[lo];
+            bool found = false;
             k = a1 - 1;
-            for (int64_t q = a0; q < a1; ++q) {
-                r += Nc[q];
-                if (r > target) {
-                    k = q;
-                    break;
+            for (int q0 = 0; q0 < per && !found; q0 += kSplitL) {
+                double nv[kSplitL];  // kSplitL counts of the range at a time (clamped past K)
+#pragma unroll
+                for (int q = 0; q < kSplitL; ++q) nv[q] = Nc[a0 + q0 + q < K ? a0 + q0 + q : K - 1];
+#pragma unroll
+                for (int q = 0; q < kSplitL; ++q) {
+                    if (q0 + q < per && a0 + q0 + q < a1 && !found) {
+                        r += nv[q];
+                        if (r > target) {
+                            k = a0 + q0 + q;
+                            found = true;
+                        }
+                    }
                 }
             }
         }
@@ -215,6 +221,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
                 for (int w = 0; w < wave; ++w) r += s_wcnt[w];
                 s_lj[r] = j;
                 s_lk[r] = k;
+                s_nk[r] = Nc[k];  // the donor's count before this split
                 list_k[i] = -1;
             }
             if (tid == 0) {
@@ -225,25 +232,41 @@ __global__ __launch_bounds__(kSplitThreads) void k_split(double* __restrict__ S,
             __syncthreads();
             const int n = s_n;
             if (n == 0) continue;  // uniform: s_n is the same for every thread
-            for (int q = tid; q < n * d; q += kSplitThreads) {
-                const int r = q / d, c = q - r * d;
-                const int64_t jd = s_lj[r], kd = s_lk[r];
-                const double nkc = Nc[kd];
-                if (!(nkc > 0.0)) continue;  // an empty donor: nothing moves
-                const double nk = nkc * 0.5;
-                const double ck = S[kd * d + c] * 0.5 / nk;
-                const double sg = (c % 2 == 0) ? 1.0 : -1.0;
-                const float cj = (float)(ck * (1.0 + eps * sg));
-                const float ckn = (float)(ck * (1.0 - eps * sg));
-                C[jd * d + c] = cj;
-                C[kd * d + c] = ckn;
-                S[jd * d + c] = (double)cj * nk;
-                S[kd * d + c] = (double)ckn * nk;
+            // (split, coordinate) pairs, kSplitU per thread at a time: the
+            // donor sums of a batch are loaded before any store
+            for (int q0 = tid; q0 < n * d; q0 += kSplitU * kSplitThreads) {
+                double sk[kSplitU];
+#pragma unroll
+                for (int uu = 0; uu < kSplitU; ++uu) {
+                    const int q = q0 + uu * kSplitThreads;
+                    sk[uu] = 0.0;
+                    if (q < n * d) {
+                        const int r = q / d, c = q - r * d;
+                        sk[uu] = S[(int64_t)s_lk[r] * d + c];
+                    }
+                }
+#pragma unroll
+                for (int uu = 0; uu < kSplitU; ++uu) {
+                    const int q = q0 + uu * kSplitThreads;
+                    if (q >= n * d) break;
+                    const int r = q / d, c = q - r * d;
+                    const int64_t jd = s_lj[r], kd = s_lk[r];
+                    const double nkc = s_nk[r];
+                    if (!(nkc > 0.0)) continue;  // an empty donor: nothing moves
+                    const double nk = nkc * 0.5;
+                    const double ck = sk[uu] * 0.5 / nk;
+                    const double sg = (c % 2 == 0) ? 1.0 : -1.0;
+                    const float cj = (float)(ck * (1.0 + eps * sg));
+                    const float ckn = (float)(ck * (1.0 - eps * sg));
+                    C[jd * d + c] = cj;
+                    C[kd * d + c] = ckn;
+                    S[jd * d + c] = (double)cj * nk;
+                    S[kd * d + c] = (double)ckn * nk;
+                }
             }
-            __syncthreads();  // every coordinate read the donor's old N before it changes
             if (tid < n) {
                 const int64_t jd = s_lj[tid], kd = s_lk[tid];
-                const double nkc = Nc[kd];
+                const double nkc = s_nk[tid];
                 if (nkc > 0.0) {
                     Nc[kd] = nkc * 0.5;
                     Nc[jd] = nkc * 0.5;

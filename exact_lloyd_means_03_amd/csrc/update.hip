@@ -1,6 +1,6 @@
 // Second half of the sort-inverse update: reduce each cluster's contiguous
-// segment of perm on chip and add it to the cluster's sums with one atomic
-// per coordinate per reduced piece (technologypulse.uk "Flash-KMeans"
+// segment of perm on chip and write it to the cluster's sums once per
+// reduced piece (technologypulse.uk "Flash-KMeans"
 // article, bottleneck 2: one atomic per segment, O((K + N/B) d) atomics
 // instead of O(N d); wispaper.ai "Flash-KMeans" blog, "Sort-Inverse
 // Update": segmented reductions instead of scattered writes).
@@ -14,13 +14,18 @@
 // a 64-entry window of offsets held one per lane, so a wave never searches
 // device memory serially.
 //
-// Where the partial sums go: a segment that starts inside a piece is flushed
-// by that piece with one atomic per coordinate, and no other piece flushes it
-// that way.  A piece's first segment (which may have begun in earlier pieces)
-// is written to the piece's own slot instead, and a second, small kernel
-// folds runs of slots into the sums.  Without that split, the pieces of a
-// very large cluster (the head of a Zipf size distribution spans thousands
-// of pieces) would all finish together and serialize on the same addresses.
+// Where the partial sums go: a segment that starts inside a piece is stored
+// by that piece with plain stores, since no other piece writes it directly
+// (added with atomics instead when the sums accumulate over several
+// launches, as in the chunked streaming fit).
+// A piece's first segment (which may have begun in earlier pieces) is
+// written to the piece's own slot instead, and a second, small kernel adds
+// runs of slots into the sums with atomics after the first has finished.
+// Without that split, the pieces of a very large cluster (the head of a Zipf
+// size distribution spans thousands of pieces) would all finish together and
+// serialize on the same addresses; and device-wide float atomics are slow on
+// this chip (tens of billions per second), so a batch of short segments
+// flushed with atomics would be bound by them.
 //
 // Scalar points (d == 1) with a row that fits in LDS take a whole-row kernel
 // instead: the row's (x, w) pairs are placed in cluster order in LDS and each
@@ -69,8 +74,7 @@ __device__ __forceinline__ void unpack(const u32x4 u, float* out) {
 // point indices are first copied to LDS with coalesced loads, so the row
 // gathers that follow depend only on an LDS read, and U row steps (U*64/LPR
 // rows) are kept in flight.  The running sums survive chunk boundaries and
-// are flushed with one atomic per coordinate whenever a segment ends and at
-// the end of the piece.
+// are flushed whenever a segment ends and at the end of the piece.
 constexpr int kSegChunk = 512;
 
 template <typename T, bool VEC, bool WEIGHTED>
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                                                    const int32_t* __restrict__ piece_seg, int64_t npieces,
                                                    int K, int TW, float* __restrict__ sums,
                                                    float* __restrict__ wsum, float* __restrict__ slot,
-                                                   float* __restrict__ wslot) {
+                                                   float* __restrict__ wslot, bool accumulate) {
     constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 8;  // non-vector rows: 64 lanes x 8 = 512 elements
     constexpr int U = 8;  // row steps in flight
     __shared__ int32_t s_idx[4][kSegChunk];
@@ -144,17 +148,27 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                 if (lane == 0) wslot[b * npieces + piece] = wacc;
             }
             first = false;
-        } else {  // a segment that starts inside this piece: this is its only flush here
+        } else {
+            // a segment that starts inside this piece: no other piece writes
+            // it directly (later pieces hold its rest in their slots, which
+            // the fold adds after this launch), so a plain store suffices,
+            // unless the sums carry earlier launches' contributions
             float* sj = sums + (b * K + j) * (int64_t)d;
             if (gl == 0 && active) {
 #pragma unroll
                 for (int t = 0; t < EPL; ++t) {
                     const int k = VEC ? li * EPL + t : li + LPR * t;
-                    if (k < d) unsafeAtomicAdd(sj + k, acc[t]);
+                    if (k < d) {
+                        if (accumulate) unsafeAtomicAdd(sj + k, acc[t]);
+                        else sj[k] = acc[t];
+                    }
                 }
             }
             if constexpr (WEIGHTED) {
-                if (lane == 0) unsafeAtomicAdd(wsum + b * K + j, wacc);
+                if (lane == 0) {
+                    if (accumulate) unsafeAtomicAdd(wsum + b * K + j, wacc);
+                    else wsum[b * K + j] = wacc;
+                }
             }
         }
 #pragma unroll
@@ -319,13 +333,13 @@ hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, 
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                             float* wsum, const int32_t* piece_seg, float* slot, float* wslot, hipStream_t s) {
     return launch_segreduce_tw(xt, x, w, B, N, d, perm, offsets, K, sums, wsum, piece_seg, slot, wslot,
-                               segreduce_tw(B, N), s);
+                               segreduce_tw(B, N), false, s);
 }
 
 hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                                const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                                float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
-                               hipStream_t s) {
+                               bool accumulate, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
     const int64_t npieces = (N + TW - 1) / TW;
     const int esz = dtype_bytes(xt);
@@ -337,7 +351,7 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
     dim3 grid((unsigned)((npieces + 3) / 4), (unsigned)B);
 #define KM_SEG(T, V, W)                                                                                   \
     hipLaunchKernelGGL((k_segreduce<T, V, W>), grid, dim3(256), 0, s, (const T*)x, w, N, d, shift, perm, \
-                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot)
+                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot, accumulate)
 #define KM_SEG_T(T)                      \
     if (vec) {                           \
         if (w) KM_SEG(T, true, true);    \

@@ -81,6 +81,7 @@ def _oracle(x, init, batch, epochs, alpha0, floor, dead_frac, eps, u):
     ("f16", 12000, 128, 256, 4096, 2),   # several centroid tiles
     ("f32", 5000, 1, 12, 1200, 3),       # scalar points: the bracketing assignment
     ("bf16", 3000, 7, 10, 5000, 2),      # batch above N: one full batch per epoch
+    ("bf16", 8000, 96, 200, 2048, 2),    # 96-wide rows
 ])
 def test_emeans_trajectory_parity(km, dtype, N, d, K, batch, epochs):
     what = f"emeans {dtype} N{N} d{d} K{K} batch{batch}"

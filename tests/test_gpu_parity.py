@@ -55,6 +55,8 @@ def _assign_case(km, x, C, w=None, what=""):
     (1, 1, 8, 1), (1, 300, 128, 64), (2, 1000, 128, 65), (1, 513, 100, 300),
     (3, 257, 16, 7), (1, 700, 2, 5), (1, 400, 33, 130), (1, 300, 200, 40), (1, 260, 256, 70),
     (1, 2049, 64, 1000),
+    # 16-bit rows of 65..96 elements are padded to 96 (rotation-swizzled tiles)
+    (1, 700, 96, 300), (2, 515, 80, 257), (1, 400, 65, 33), (1, 1200, 96, 600),
 ])
 def test_assign_parity(km, dtype, B, N, d, K):
     x, C = _rand_problem(B, N, d, K, dtype, seed=B * 1000 + N + d + K)
