@@ -33,7 +33,7 @@ PEAK_VALU_GOPS = 256 * 4 * 16 * 2.4
 # and weight sum (fma, add), and the objective term (fma).
 OPS_1D_PER_POINT = 8
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_traffic.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_03_amd", "csrc", "assign_mfma.hip")
 
 
@@ -58,9 +58,9 @@ def _src_hash(path) -> str:
 
 def _traffic(wl):
     """HBM bytes per assignment launch from the committed rocprofv3 counter
-    summary, if it was taken on this workload with the current kernel source."""
+    summary of this workload, if it was taken with the current kernel source."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(os.path.join(TRAFFIC_DIR, f"assign_traffic__{wl.name}.json")))
     except (OSError, ValueError):
         return None
     if t.get("workload") != wl.name or t.get("kernel_src_sha") != _src_hash(ASSIGN_SRC):
@@ -488,7 +488,7 @@ def bench_emeans(args, km, wl):
                    "batch": batch, "epochs": E, "steps_per_run": T, "alpha0": wl.em_alpha0,
                    "floor": wl.em_floor, "dead_frac": wl.em_dead_frac, "eps": wl.em_eps},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": None, "kernel": "k_assign_mfma (one batch)", "algorithmic_per_launch": flops,
+                     "traffic": _traffic(wl), "kernel": "k_assign_mfma (one batch)", "algorithmic_per_launch": flops,
                      "avg_launch_ms": assign_ms},
         "run_ms_event": run_ms,
         "quality": {"emeans_mse_by_epochs": em_mse, "emeans_ms_by_epochs": em_ms,

@@ -442,10 +442,10 @@ int oracle_optimal_1d(const double *X, const double *w, int64_t B, int64_t N, in
  * a_t = a0 floor + a0 (1 - floor) (1 + cos(pi t / (T - 1))) / 2 (a0 when
  * T = 1); after a batch's update (before any of its splits), cluster j is
  * dead when N_j < dead_frac * min(batch, N) / K; dead clusters are handled
- * in ascending order, each
- * with the uniform u = uniforms[t * K + j], choosing the donor k as the
- * first index whose prefix of N (taken after the update, before any split
- * of this batch) exceeds u * sum(N), skipping k = j; the donor's S and N
+ * in ascending order, each with the uniform u = uniforms[t * K + j],
+ * choosing the donor k as the first index whose prefix of N (taken after
+ * the update, before any split of this batch) exceeds u * sum(N), skipping
+ * k = j and a donor whose N is zero at its turn; the donor's S and N
  * halve, the dead cluster gets the same S and N, and their centroids
  * become c_k (1 + eps s_c) and c_k (1 - eps s_c), s_c = +1 for even and -1
  * for odd coordinates (S rescaled to match).  Assignments use the

@@ -182,6 +182,24 @@ def test_emeans_split_skips_a_cluster_that_draws_itself(km):
     np.testing.assert_array_equal(cnt, ref["counts"])
 
 
+def test_emeans_deadness_is_decided_before_the_steps_splits(km):
+    """The oracle pin's case: a split halves a live cluster below the dead
+    line, and it is not split again in the same step."""
+    A = np.tile(np.array([1.9, 2.1], np.float32), 20)
+    x = torch.from_numpy(np.concatenate([A, np.full(60, 10.0, np.float32)])[:, None])
+    init = torch.tensor([[1000.0], [2.0], [10.0]])
+    u = np.zeros((2, 3), np.float32)
+    u[0, 0], u[0, 1] = 0.2, 0.9
+    got = _run(km, x, init, 100, 2, 0.5, 0.1, 0.45, 1e-3, u)
+    ref = _oracle(x, init, 100, 2, 0.5, 0.1, 0.45, 1e-3, u)
+    np.testing.assert_array_equal(got[1], ref["labels"])
+    # the GPU's batch sums are fp32: its centroid after step 0 is off by
+    # ~1e-7 of 2.0, which moves step 1's distances of ~0.1 by ~4e-6
+    # relative; a second split of cluster 1 would change J[1] by 4%
+    np.testing.assert_allclose(got[3], ref["J"], rtol=1e-4)
+    np.testing.assert_allclose(got[0], ref["centroids"], rtol=1e-5)
+
+
 @pytest.mark.parametrize("dtype,d,K,batch,epochs,dead_frac", [
     ("f16", 32, 256, 3000, 3, 0.2),
     ("bf16", 96, 512, 4096, 2, 0.1),

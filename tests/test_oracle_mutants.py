@@ -71,6 +71,8 @@ MUTANTS = [
     ("e-means: donor drawn from the top", "                const double target = (double)uniforms[t * K + j] * P[K];",
      "                const double target = (1.0 - (double)uniforms[t * K + j]) * P[K];"),
     ("e-means: schedule floor ignored", "alpha0 * floor_frac +\n", "alpha0 * 0.0 +\n"),
+    ("e-means: deadness re-read after each split", "                if (!dead[j]) continue;",
+     "                if (!(Nc[j] < dead_below)) continue;"),
 ]
 
 

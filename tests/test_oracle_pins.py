@@ -583,6 +583,35 @@ def test_emeans_dead_cluster_splits_the_drawn_donor(orc):
     np.testing.assert_array_equal(r["centroids"][2], init[2])
 
 
+def test_emeans_deadness_is_decided_before_the_steps_splits(orc):
+    """A live cluster that a split halves below the dead line is not split
+    again in the same step: which clusters are dead is fixed by the step's
+    moving averages, before any split.  Scalar points: 40 at 1.9 / 2.1
+    (cluster 1), 60 at 10 (cluster 2), cluster 0 far away.  After step 0
+    (a = 1/2, dead below 0.45 * 100 / 3 = 15) cluster 0 is dead and draws
+    cluster 1 (N = 20, halved to 10, now below the line); step 1's cost then
+    follows from the split pair around cluster 1's mean, computed here from
+    the definition.  Splitting cluster 1 again would move it onto cluster 2."""
+    A = np.tile(np.array([1.9, 2.1], np.float32), 20)
+    X = np.concatenate([A, np.full(60, 10.0, np.float32)])[:, None]
+    init = np.array([[1000.0], [2.0], [10.0]], np.float32)
+    u = np.zeros((2, 3), np.float32)
+    u[0, 0] = 0.2    # target 0.2 * 50 = 10 lies in cluster 1's share (0, 20]
+    u[0, 1] = 0.9    # used only if cluster 1 were (wrongly) split too: cluster 2
+    eps = 1e-3
+    r = _emeans(orc, X, init, batch=100, epochs=2, alpha0=0.5, floor_frac=0.1, dead_frac=0.45, eps=eps,
+                u=u.reshape(-1))
+    Ad = A.astype(np.float64)
+    ck = Ad.sum() / 40.0                          # cluster 1's mean, the donor's centroid
+    c0 = np.float32(ck * (1 + eps)).astype(np.float64)
+    c1 = np.float32(ck * (1 - eps)).astype(np.float64)
+    # step 1: the split pair takes the 40 points, cluster 2 keeps its own at distance 0
+    J1 = np.minimum((Ad - c0) ** 2, (Ad - c1) ** 2).sum()
+    assert abs(r["J"][1] - J1) <= 1e-9 * J1
+    J0 = ((Ad - 2.0) ** 2).sum()
+    assert abs(r["J"][0] - J0) <= 1e-9 * J0
+
+
 def test_emeans_final_means_are_the_last_epochs_update(orc):
     rng = np.random.default_rng(34)
     X = rng.normal(0, 1, (3000, 6)).astype(np.float32)
