@@ -288,7 +288,7 @@ hipError_t stream_res(int dev, StreamRes** out) {
 struct EmeansPlan {
     Workspace batch;  // the per-batch plan (B = 1, N = batch points)
     int64_t mfull = 0, nb = 0, steps = 0;
-    size_t S = 0, Nc = 0, F = 0, G = 0, list_j = 0, list_k = 0, total = 0;
+    size_t S = 0, Nc = 0, F = 0, G = 0, list_j = 0, list_k = 0, obj_part = 0, total = 0;
 };
 
 EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch, int32_t epochs) {
@@ -309,6 +309,18 @@ EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch,
     p.G = take((size_t)K * sizeof(double));
     p.list_j = take((size_t)K * sizeof(int32_t));
     p.list_k = take((size_t)K * sizeof(int32_t));
+    // objective partials of one batch's assignment: a shorter last batch can
+    // have more of them than a full one (fewer points per group when its
+    // groups would not fill the chip)
+    int64_t nblk = 1;
+    if (p.nb > 0) {
+        const int64_t mlast = N - (p.nb - 1) * batch;
+        for (const int64_t m : {p.mfull, mlast}) {
+            const int64_t n = use_assign_1d(d, K) ? assign_1d_blocks(m) : assign_mfma_blocks(1, m, p.batch.DP, xt);
+            if (n > nblk) nblk = n;
+        }
+    }
+    p.obj_part = take((size_t)nblk * sizeof(double));
     p.total = off;
     return p;
 }
@@ -592,7 +604,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
     int32_t* offsets = at<int32_t>(ws, W.offsets);
     int32_t* perm = at<int32_t>(ws, W.perm);
     int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
-    double* part = at<double>(ws, W.obj_part);
+    double* part = at<double>(ws, P.obj_part);
     // every batch uses the piece width of a full batch, so a shorter last
     // batch never has more pieces than the plan holds
     const int TW = segreduce_tw(1, P.mfull);

@@ -81,50 +81,73 @@ __global__ __launch_bounds__(kSortThreads) void k_count(const int32_t* __restric
 }
 
 // One block per batch: exclusive scan of K counts -> offsets and scatter
-// cursors.  The counts are staged in LDS with coalesced loads; each thread
-// scans a contiguous run of bins, and the 1024 run totals are scanned with
-// wave shuffles.  When piece_seg is given it also records, for every
-// reduction piece of TW sorted rows, the segment its first row falls in
-// (binary search over the offsets in LDS).
+// cursors.  The counts are staged in LDS with coalesced loads, eight in
+// flight per thread, and zero-padded to Kpad (a multiple of 4096).  Each
+// thread then scans a contiguous run of Kpad / 1024 bins with 16-byte LDS
+// accesses, and the run totals are scanned with wave shuffles and the 16
+// wave totals: one shuffle scan for the whole row.  When piece_seg is given
+// it also records, for every reduction piece of TW sorted rows, the segment
+// its first row falls in (binary search over the offsets in LDS).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+static int64_t scan_kpad(int64_t K) { return (K + 4095) / 4096 * 4096; }
+
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ counts, int K,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
                                                int TW, int64_t npieces, int32_t* __restrict__ piece_seg) {
-    extern __shared__ int32_t s_off[];  // [K + 1]
+    extern __shared__ __attribute__((aligned(16))) int32_t s_off[];  // [Kpad + 1]
     __shared__ int32_t s_wave[16];
+    constexpr int U = 8;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t b = blockIdx.x;
-    for (int j = tid; j < K; j += 1024) s_off[j] = counts[b * K + j];
+    const int Kpad = (K + 4095) / 4096 * 4096;
+    for (int j0 = tid; j0 < Kpad; j0 += 1024 * U) {
+        int32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * 1024;
+            v[u] = j < K ? counts[b * K + j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * 1024;
+            if (j < Kpad) s_off[j] = v[u];
+        }
+    }
     __syncthreads();
-    const int per = (K + 1023) / 1024;
-    const int j0 = tid * per;
-    const int j1 = (j0 + per < K) ? j0 + per : K;
-    int32_t s = 0;
-    for (int j = j0; j < j1; ++j) s += s_off[j];
-    int32_t v = s;  // inclusive scan of the run totals within the wave
+    const int per = Kpad / 1024;  // a multiple of 4
+    i32x4* run4 = (i32x4*)(s_off + tid * per);
+    int32_t sum = 0;
+    for (int q = 0; q < per / 4; ++q) {
+        const i32x4 v = run4[q];
+        sum += v[0] + v[1] + v[2] + v[3];
+    }
+    int32_t incl = sum;  // inclusive scan of the run totals within the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int32_t t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
+        const int32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
     }
-    if (lane == 63) s_wave[wid] = v;
+    if (lane == 63) s_wave[wid] = incl;
     __syncthreads();
-    if (wid == 0) {
-        int32_t t = lane < 16 ? s_wave[lane] : 0;
+    int32_t run = incl - sum, total = 0;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int32_t u = __shfl_up(t, o, 64);
-            if (lane >= o) t += u;
-        }
-        if (lane < 16) s_wave[lane] = t;
+    for (int w = 0; w < 16; ++w) {
+        const int32_t t = s_wave[w];
+        run += w < wid ? t : 0;
+        total += t;
     }
-    __syncthreads();
-    int32_t run = v - s + (wid > 0 ? s_wave[wid - 1] : 0);
-    const int32_t total = s_wave[15];
-    for (int j = j0; j < j1; ++j) {
-        const int32_t c = s_off[j];
-        s_off[j] = run;
-        run += c;
+    for (int q = 0; q < per / 4; ++q) {
+        const i32x4 v = run4[q];
+        i32x4 o;
+        o[0] = run;
+        o[1] = run + v[0];
+        o[2] = o[1] + v[1];
+        o[3] = o[2] + v[2];
+        run = o[3] + v[3];
+        run4[q] = o;
     }
+    __syncthreads();  // the last run's store of s_off[K .. Kpad) before s_off[K] is set
     if (tid == 0) s_off[K] = total;
     __syncthreads();
     for (int j = tid; j <= K; j += 1024) offsets[b * (K + 1) + j] = s_off[j];
@@ -225,7 +248,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, i
         hipLaunchKernelGGL(k_count, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const size_t scan_lds = (size_t)(K + 1) * sizeof(int32_t);
+    const size_t scan_lds = (size_t)(scan_kpad(K) + 1) * sizeof(int32_t);
     if ((e = set_lds((const void*)k_scan, scan_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), scan_lds, s, counts, (int)K, offsets, cursor, TW,
                        npieces, piece_seg);

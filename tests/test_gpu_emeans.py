@@ -95,6 +95,24 @@ def test_emeans_trajectory_parity(km, dtype, N, d, K, batch, epochs):
     parity.check_centroids(cen[None], ref["centroids"][None], what)
 
 
+def test_emeans_short_last_batch_with_more_groups(km):
+    """A last batch just short of the full one can be assigned in more point
+    groups than the full batch (one column block per wave when its groups
+    would not fill the chip): 131072 points make 256 groups of 512, 130000
+    make 508 groups of 256.  Every group's objective partial must fit the
+    workspace; the labels stay in the workspace here, next to the partials."""
+    N, d, K, batch = 131072 + 130000, 16, 64, 131072
+    x, init = _separated(N, d, K, "f16", seed=77)
+    T = 2
+    cen, _, cnt, J = km.kmeans_emeans(x.cuda(), init.cuda(), batch, 1, 0.6, 0.1, 0.0, 0.0)
+    torch.cuda.synchronize()
+    ref = _oracle(x, init, batch, 1, 0.6, 0.1, 0.0, 0.0, None)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), ref["counts"])
+    np.testing.assert_allclose(J.cpu().numpy(), ref["J"], rtol=1e-3)
+    parity.check_centroids(cen.cpu().numpy()[None], ref["centroids"][None], "short last batch")
+    assert J.numel() == T
+
+
 def test_emeans_full_batch_unit_steps_is_lloyd(km):
     """batch >= N, alpha = 1 at every step, no splits: each step is one Lloyd
     iteration, so the run is kmeans_fit with n_iter = epochs."""
