@@ -517,7 +517,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the batched problems are independent per GPU, see the design notes)", file=sys.stderr)
+              "(the batched problems are independent per GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -18,8 +18,7 @@
  *   - github LeanModels/LeanQuant issue #1 "1D k-means", the kmeans_fit diff:
  *     per-point sample weights; the weighted centroid is sum(w x) / sum(w).
  *
- * Readings where the pages are silent (each one is listed with its reason in
- * the design notes of the repository):
+ * Readings where the pages are silent:
  *   - distance is the squared Euclidean distance, summed in fp64 as
  *     sum_k (x_k - c_k)^2 with k ascending;
  *   - ties go to the smallest centroid index (j ascending, strict '<');
@@ -435,7 +434,7 @@ int oracle_optimal_1d(const double *X, const double *w, int64_t B, int64_t N, in
  *   - "Proportional Splitting Resurrects Thousands of Dead Centers": a dead
  *     cluster takes over half of a live cluster drawn with probability
  *     proportional to its size, and the two are split apart.
- * Readings (listed with their reasons in the design notes): batches are
+ * Readings where the article is silent: batches are
  * consecutive slices of `batch` points in storage order (the caller fixes
  * the order); S and N start at zero and a centroid moves only once its N
  * is positive; a step t of T = epochs * ceil(N / batch) uses

@@ -1,6 +1,6 @@
 """GPU-vs-oracle comparison helpers shared by the GPU tests.
 
-Tolerances (each is derived in the design notes):
+Tolerances:
   * labels: equal, except points whose oracle top-2 gap (d2 - d1) is at most
     1e-4 * d1 (near ties), where either label is correct;
   * counts: equal (teacher forced: both sides get the same labels);
