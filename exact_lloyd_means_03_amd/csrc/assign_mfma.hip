@@ -128,10 +128,10 @@ __device__ __forceinline__ typename Mf<T>::frag load_point_frag(const T* row, in
 // read from LDS feeds two MFMAs), one for long rows.
 constexpr int default_ncb(int DP, int elem_bytes) { return DP * elem_bytes <= 512 ? 2 : 1; }
 
-template <typename T, int DP, int NCBT = default_ncb(DP, sizeof(T))>
+template <typename T, int DP, int NCBT = default_ncb(DP, sizeof(T)), int WAVEST = assign_waves(DP, sizeof(T))>
 struct AssignCfg {
     static constexpr int NCB = NCBT;                                      // 32-point blocks per wave
-    static constexpr int WAVES = assign_waves(DP, sizeof(T));
+    static constexpr int WAVES = WAVEST;
     static constexpr int PTS = WAVES * NCB * 32;                         // points per block
     static constexpr int TK = tile_rows(DP, sizeof(T));                   // centroid rows per tile
     static_assert(TK % 64 == 0, "tiles hold an even number of 32-row blocks");
@@ -192,9 +192,8 @@ __device__ __forceinline__ int global_chunk(int q, int r) {
 // Source offset (within a tile) of the 16 bytes lane `lane` copies with the
 // DMA instruction i (the LDS side is contiguous).  Bytes past the rows (the
 // -|c|^2/2 segment and padding) are copied unchanged.
-template <typename T, int DP>
+template <typename Cfg>
 __device__ __forceinline__ uint32_t dma_src(int i, int lane) {
-    typedef AssignCfg<T, DP> Cfg;
     const int p = i * 1024 + lane * 16;
     if (p >= Cfg::TK * Cfg::RB) return (uint32_t)p;
     const int r = p / Cfg::RB, q = (p % Cfg::RB) / 16;
@@ -206,9 +205,8 @@ __device__ __forceinline__ uint32_t dma_src(int i, int lane) {
 // last instruction (i = NR) carries the -|c|^2/2 floats on its first
 // HN_LANES lanes only.  Waves may issue different numbers of instructions;
 // each waits for all of its own before the barrier that publishes the tile.
-template <typename T, int DP>
+template <typename Cfg>
 __device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave, int lane, const uint32_t* voff) {
-    typedef AssignCfg<T, DP> Cfg;
 #pragma unroll
     for (int n = 0; n < Cfg::NIW; ++n) {
         const int i = n * Cfg::WAVES + wave;
@@ -217,12 +215,12 @@ __device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave
     }
 }
 
-template <typename T, int DP, bool VEC, int NCBT>
-__global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfma(
+template <typename T, int DP, bool VEC, int NCBT, int WAVEST>
+__global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
     const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int64_t ntiles,
     const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
     double* __restrict__ obj_part, int64_t gpb, int64_t ngroups) {
-    typedef AssignCfg<T, DP, NCBT> Cfg;
+    typedef AssignCfg<T, DP, NCBT, WAVEST> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
     constexpr int NCB = Cfg::NCB, TK = Cfg::TK, RB = Cfg::RB, KSTEPS = Cfg::KSTEPS, NRB = Cfg::NRB;
@@ -241,9 +239,9 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
     // per-lane DMA source offsets (the same for every tile)
     uint32_t voff[Cfg::NIW];
 #pragma unroll
-    for (int n = 0; n < Cfg::NIW; ++n) voff[n] = dma_src<T, DP>(n * Cfg::WAVES + wave, lane);
+    for (int n = 0; n < Cfg::NIW; ++n) voff[n] = dma_src<Cfg>(n * Cfg::WAVES + wave, lane);
     // start the first tile's DMA before the point loads
-    dma_tile<T, DP>(Bb, s_tile[0], wave, lane, voff);
+    dma_tile<Cfg>(Bb, s_tile[0], wave, lane, voff);
     int par = 0;  // the buffer that holds a group's first tile
 
     // ---- points of this wave: B operand fragments + squared norms -------
@@ -427,7 +425,7 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
             const char* src = t + 1 < ntiles ? Bb + (t + 1) * (int64_t)Cfg::TILE
                               : has_next     ? Bn
                                              : Bb + t * (int64_t)Cfg::TILE;
-            dma_tile<T, DP>(src, s_tile[(par + t + 1) & 1], wave, lane, voff);
+            dma_tile<Cfg>(src, s_tile[(par + t + 1) & 1], wave, lane, voff);
 #pragma unroll
             for (int rb = 0; rb < NRB; rb += 2) {
                 const int32_t blk0 = (int32_t)(t * NRB) + rb;
@@ -494,23 +492,32 @@ __global__ __launch_bounds__(64 * assign_waves(DP, sizeof(T))) void k_assign_mfm
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// Column blocks per wave for a launch: the default, unless the default
-// leaves fewer point groups than the chip has compute units (a mini-batch
-// against many centroids); then one, which doubles the groups, each reading
-// the centroid tiles for half as many points.
+// Point groups of a launch: WAVES waves of NCB 32-point column blocks.  The
+// default shape, unless it leaves fewer groups than the chip has compute
+// units (a mini-batch against many centroids); then one column block per
+// wave, which doubles the groups, each reading the centroid tiles for half
+// as many points.
 constexpr int64_t kFewGroups = 256;
 
+struct GroupShape {
+    int ncb, waves;
+};
+
 template <typename T>
-static int ncb_for(int64_t B, int64_t N, int DP) {
-    const int def = default_ncb(DP, sizeof(T));
-    if (def == 1) return 1;
-    const int64_t pts = (int64_t)assign_waves(DP, sizeof(T)) * def * 32;
-    return B * ((N + pts - 1) / pts) < kFewGroups ? 1 : def;
+static GroupShape group_shape(int64_t B, int64_t N, int DP) {
+    const int def = default_ncb(DP, sizeof(T)), wv = assign_waves(DP, sizeof(T));
+    if (def == 1) return {1, wv};
+    const int64_t pts = (int64_t)wv * def * 32;
+    if (B * ((N + pts - 1) / pts) >= kFewGroups) return {def, wv};
+    // two column blocks on half the waves (the same points per group) timed
+    // the same within noise on batches of 32768..100000 points
+    return {1, wv};
 }
 
 template <typename T>
 static int64_t blocks_for(int64_t B, int64_t N, int DP) {
-    const int64_t pts = (int64_t)assign_waves(DP, sizeof(T)) * ncb_for<T>(B, N, DP) * 32;
+    const GroupShape g = group_shape<T>(B, N, DP);
+    const int64_t pts = (int64_t)g.waves * g.ncb * 32;
     return (N + pts - 1) / pts;
 }
 
@@ -522,15 +529,15 @@ int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt) {
 
 // Persistent blocks: as many as the device holds at once (compute units x
 // resident blocks per unit), each walking groups i, i + grid, ...
-template <typename T, int DP, bool VEC, int NCBT>
+template <typename T, int DP, bool VEC, int NCBT, int WV>
 static int64_t resident_blocks() {
     static int64_t n = 0;
     if (n == 0) {
         int dev = 0, cus = 0, per = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC, NCBT>,
-                                                         64 * AssignCfg<T, DP>::WAVES, 0) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC, NCBT, WV>,
+                                                         64 * WV, 0) != hipSuccess ||
             cus <= 0 || per <= 0)
             return 256;
         n = (int64_t)cus * per;
@@ -538,38 +545,37 @@ static int64_t resident_blocks() {
     return n;
 }
 
-template <typename T, int DP, int NCBT>
+template <typename T, int DP, int NCBT, int WV>
 static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const void* blob, int64_t ntiles,
                            const float* w, int32_t* labels, float* min_dist, double* obj_part, int64_t nblk,
                            hipStream_t s) {
     const int64_t ngroups = B * nblk;
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
-    const int64_t P = vec ? resident_blocks<T, DP, true, NCBT>() : resident_blocks<T, DP, false, NCBT>();
+    const int64_t P = vec ? resident_blocks<T, DP, true, NCBT, WV>() : resident_blocks<T, DP, false, NCBT, WV>();
     dim3 grid((unsigned)(ngroups < P ? ngroups : P));
     if (vec)
-        hipLaunchKernelGGL((k_assign_mfma<T, DP, true, NCBT>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s,
-                           (const T*)x, N, d, (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk,
-                           ngroups);
+        hipLaunchKernelGGL((k_assign_mfma<T, DP, true, NCBT, WV>), grid, dim3(64 * WV), 0, s, (const T*)x, N, d,
+                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
     else
-        hipLaunchKernelGGL((k_assign_mfma<T, DP, false, NCBT>), grid, dim3(64 * AssignCfg<T, DP>::WAVES), 0, s,
-                           (const T*)x, N, d, (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk,
-                           ngroups);
+        hipLaunchKernelGGL((k_assign_mfma<T, DP, false, NCBT, WV>), grid, dim3(64 * WV), 0, s, (const T*)x, N, d,
+                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
     return hipGetLastError();
 }
 
 // nblk: point groups per problem, as assign_mfma_blocks(B, N, DP, xt) gives
-// them (the column blocks per wave follow from the same rule).
+// them (the group shape follows from the same rule).
 template <typename T, int DP>
 static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
                            double* obj_part, int64_t nblk, hipStream_t s) {
     if (nblk != blocks_for<T>(B, N, DP)) return hipErrorInvalidValue;
-    constexpr int DEF = default_ncb(DP, sizeof(T));
+    constexpr int DEF = default_ncb(DP, sizeof(T)), WV = assign_waves(DP, sizeof(T));
     if constexpr (DEF == 2) {
-        if (ncb_for<T>(B, N, DP) == 1)
-            return launch_n<T, DP, 1>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        const GroupShape g = group_shape<T>(B, N, DP);
+        if (g.ncb == 1)
+            return launch_n<T, DP, 1, WV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
     }
-    return launch_n<T, DP, DEF>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+    return launch_n<T, DP, DEF, WV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
 }
 
 template <typename T>
