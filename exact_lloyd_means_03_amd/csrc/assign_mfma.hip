@@ -37,6 +37,8 @@
 //     pipeline runs on from one group into the next (the next group's first
 //     tile loads during the current group's last tile), which matters when
 //     K is small and a group walks few tiles.
+#include <atomic>
+
 #include "common.h"
 
 namespace km {
@@ -528,20 +530,28 @@ int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt) {
 }
 
 // Persistent blocks: as many as the device holds at once (compute units x
-// resident blocks per unit), each walking groups i, i + grid, ...
+// resident blocks per unit), each walking groups i, i + grid, ...  Cached
+// per device and kernel; concurrent first calls compute the same value.
+constexpr int kMaxDevices = 64;
+
 template <typename T, int DP, bool VEC, int NCBT, int WV>
 static int64_t resident_blocks() {
-    static int64_t n = 0;
-    if (n == 0) {
-        int dev = 0, cus = 0, per = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC, NCBT, WV>,
-                                                         64 * WV, 0) != hipSuccess ||
-            cus <= 0 || per <= 0)
-            return 256;
-        n = (int64_t)cus * per;
+    static std::atomic<int64_t> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached) {
+        const int64_t n = cache[dev].load(std::memory_order_relaxed);
+        if (n > 0) return n;
     }
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)k_assign_mfma<T, DP, VEC, NCBT, WV>,
+                                                     64 * WV, 0) != hipSuccess ||
+        cus <= 0 || per <= 0)
+        return 256;
+    const int64_t n = (int64_t)cus * per;
+    if (cached) cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 

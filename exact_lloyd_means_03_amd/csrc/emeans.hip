@@ -282,13 +282,10 @@ bool emeans_split_supports(int64_t K) { return K >= 1 && K <= kEmeansMaxK; }
 hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d, double dead_below, double eps,
                                const float* u, int32_t* list_j, int32_t* list_k, hipStream_t st) {
     if (!emeans_split_supports(K)) return hipErrorInvalidValue;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_split, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kEmeansMaxK * sizeof(int)));
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    // set on every call: the attribute belongs to the current device
+    hipError_t e = hipFuncSetAttribute((const void*)k_split, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kEmeansMaxK * sizeof(int)));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_split, dim3(1), dim3(kSplitThreads), (size_t)K * sizeof(int), st, S, Nc, C, K, d,
                        dead_below, eps, u, list_j, list_k);
     return hipGetLastError();
