@@ -80,6 +80,7 @@ def _oracle(x, init, batch, epochs, alpha0, floor, dead_frac, eps, u):
     ("f32", 6000, 33, 24, 1000, 2),      # padded rows
     ("f16", 12000, 128, 256, 4096, 2),   # several centroid tiles
     ("f32", 5000, 1, 12, 1200, 3),       # scalar points: the bracketing assignment
+    ("f16", 4001, 1, 5, 1001, 2),        # scalar points, K <= 16, batches not 4-aligned
     ("bf16", 3000, 7, 10, 5000, 2),      # batch above N: one full batch per epoch
     ("bf16", 8000, 96, 200, 2048, 2),    # 96-wide rows
 ])
