@@ -3,8 +3,10 @@ shapes, padded widths 16 … 512 including 96, piece widths, the direct and the
 chunked label sort, the d = 1 paths) with combinations no hand-picked case
 lists.  Each case runs the assignment against the oracle (labels up to near
 ties, min_dist, objective), the update of random labels against the oracle
-(counts exact, centroids per the Lloyd tolerance, empty clusters unchanged)
-and the label sort (segment sets exact).  The shapes are drawn from a fixed
+(counts exact, centroids per the Lloyd tolerance, empty clusters unchanged),
+the label sort (segment sets exact) and one fit iteration (its labels and
+objective like the assignment's, its update against the oracle's update of
+the same labels).  The shapes are drawn from a fixed
 seed, so every run checks the same cases.
 """
 import numpy as np
@@ -80,3 +82,14 @@ def test_random_shape(km, i, dtype, B, N, d, K, weighted):
     cnt, off, perm = km.kmeans_sort_labels(torch.from_numpy(lab).cuda(), K)
     torch.cuda.synchronize()
     parity.check_perm(lab, K, cnt.cpu().numpy(), off.cpu().numpy(), perm.cpu().numpy())
+
+    # one fit iteration: its assignment is the one above, its update that of
+    # its own labels (teacher forced)
+    cen, flab, fcnt, J = km.kmeans_fit(xd, Cd, 1, weights=wd)
+    torch.cuda.synchronize()
+    fl = flab.cpu().numpy()
+    parity.check_labels(fl, lab_ref, d1, d2, what + " fit")
+    parity.check_objective(J.cpu().numpy()[:, 0], (wn * d1).sum(-1), what + " fit")
+    ref_c, ref_n, _, _ = oracle.update(X, None if w is None else w.numpy(), fl, C.numpy())
+    np.testing.assert_array_equal(fcnt.cpu().numpy(), ref_n, err_msg=what + " fit")
+    parity.check_centroids(cen.cpu().numpy(), ref_c, what + " fit")
