@@ -79,3 +79,21 @@ def test_linspace_init_endpoints():
     np.testing.assert_array_equal(p.init[:, 0, 0], x.min(dim=1).values)
     np.testing.assert_array_equal(p.init[:, -1, 0], x.max(dim=1).values)
     assert torch.all(p.w >= 0.1) and torch.all(p.w <= 1.0)
+
+
+def test_emeans_uniforms_deterministic_and_in_range():
+    a = workloads.emeans_uniforms(7, 16, 1000)
+    b = workloads.emeans_uniforms(7, 16, 1000)
+    assert a.dtype == np.float32 and a.shape == (16, 1000)
+    np.testing.assert_array_equal(a, b)
+    assert a.min() >= 0.0 and a.max() < 1.0
+    assert not np.array_equal(a, workloads.emeans_uniforms(8, 16, 1000))
+    # roughly uniform: mean and quartiles
+    assert abs(a.mean() - 0.5) < 0.01
+    np.testing.assert_allclose(np.quantile(a, [0.25, 0.5, 0.75]), [0.25, 0.5, 0.75], atol=0.01)
+
+
+def test_emeans_workload_fields():
+    wl = workloads.WORKLOADS["emeans-n1m-k16384-d96-bf16"]
+    assert wl.em_batch > 0 and wl.em_epochs > 0 and 0 < wl.em_alpha0 <= 1 and 0 <= wl.em_floor <= 1
+    assert wl.N % wl.em_batch == 0 and wl.d == 96 and wl.K == 16384
