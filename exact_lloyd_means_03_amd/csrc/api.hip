@@ -143,10 +143,11 @@ P* at(void* ws, size_t off) {
 }
 
 // Assignment of all B*N points against C; optional per-block objective
-// partials reduced into obj_out[b * obj_stride].
+// partials reduced into obj_out[b * obj_stride].  prep = false: the tile
+// blob already holds C (written by the previous update's fused divide).
 km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, const float* C, int64_t K,
                      const float* w, int32_t* labels, float* min_dist, double* obj_out, int64_t obj_stride,
-                     const Workspace& W, void* ws, hipStream_t s) {
+                     const Workspace& W, void* ws, hipStream_t s, bool prep = true) {
     double* part = obj_out ? at<double>(ws, W.obj_part) : nullptr;
     if (use_assign_1d(d, K)) {
         if (obj_out && N > 0 && W.nblk_assign == 1) {
@@ -159,7 +160,7 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
                "assign_1d");
     } else {
         void* blob = at<void>(ws, W.chat);
-        KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, blob, s), "prep");
+        if (prep) KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, blob, s), "prep");
         KM_HIP(launch_assign_mfma(xt, x, B, N, (int)d, W.DP, blob, W.Kp, w, labels, min_dist, part,
                                   W.nblk_assign, s),
                "assign_mfma");
@@ -183,9 +184,11 @@ km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32
     return KM_OK;
 }
 
+// prep_next: also write c_new to the tile blob for the next assignment
+// (the divide fused with the prep; matrix-core path only).
 km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t N, int64_t d,
                      const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
-                     const Workspace& W, void* ws, hipStream_t s) {
+                     const Workspace& W, void* ws, hipStream_t s, bool prep_next = false) {
     int32_t* cnt = counts ? counts : at<int32_t>(ws, W.counts);
     if (use_update_1d(xt, x, w, labels, d, N, K)) {
         KM_HIP(launch_update_1d_row(xt, x, w, B, N, labels, K, c_old, c_new, cnt, s), "update_1d_row");
@@ -202,7 +205,12 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
     KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr, piece_seg,
                             at<float>(ws, W.slot), at<float>(ws, W.wslot), s),
            "segreduce");
-    KM_HIP(launch_divide(sums, w ? wsum : nullptr, cnt, B, K, (int)d, c_old, c_new, s), "divide");
+    if (prep_next && !use_assign_1d(d, K))
+        KM_HIP(launch_divide_prep(xt, sums, w ? wsum : nullptr, cnt, B, K, (int)d, W.DP, W.Kp, c_old, c_new,
+                                  at<void>(ws, W.chat), s),
+               "divide");
+    else
+        KM_HIP(launch_divide(sums, w ? wsum : nullptr, cnt, B, K, (int)d, c_old, c_new, s), "divide");
     return KM_OK;
 }
 
@@ -415,9 +423,13 @@ km_status kmeans_fit(const void* x, km_dtype xt, const float* weights, int64_t B
                "copy init");
     int32_t* lab = labels ? labels : at<int32_t>(workspace, W.labels);
     for (int32_t t = 0; t < n_iter; ++t) {
+        // from the second iteration on, the previous update's divide wrote the
+        // centroid tiles, unless the update took the scalar-row path
+        const bool fused = t > 0 && !use_update_1d((DType)xt, x, weights, lab, d, N, K);
         KM_TRY(run_assign(x, (DType)xt, B, N, d, centroids, K, weights, lab, nullptr,
-                          objective ? objective + t : nullptr, n_iter, W, workspace, s));
-        KM_TRY(run_update(x, (DType)xt, weights, B, N, d, lab, K, centroids, centroids, counts, W, workspace, s));
+                          objective ? objective + t : nullptr, n_iter, W, workspace, s, !fused));
+        KM_TRY(run_update(x, (DType)xt, weights, B, N, d, lab, K, centroids, centroids, counts, W, workspace, s,
+                          t + 1 < n_iter));
     }
     return KM_OK;
 }
@@ -505,7 +517,8 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
     KM_HIP(hipStreamWaitEvent(R->copy, R->start, 0), "event wait");
     int64_t g = 0;  // chunk counter over all iterations: buffer g % 2
     for (int32_t it = 0; it < n_iter; ++it) {
-        KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, at<void>(ws, W.chat), s), "prep");
+        // later iterations find their centroid tiles written by the previous divide
+        if (it == 0) KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, at<void>(ws, W.chat), s), "prep");
         // sums and wsum are adjacent in the plan: clear both with one fill
         KM_HIP(launch_zero(sums, W.offsets - W.sums, s), "zero");
         KM_HIP(launch_zero(ctot, (size_t)K * sizeof(int32_t), s), "zero");
@@ -545,7 +558,12 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
             KM_HIP(hipEventRecord(R->consumed[buf], s), "event");
         }
         if (objective) KM_HIP(launch_obj_reduce(obj_all, 1, P.nblk_total, objective + it, 1, s), "obj_reduce");
-        KM_HIP(launch_divide(sums, wsum, ctot, 1, K, (int)d, centroids, centroids, s), "divide");
+        if (it + 1 < n_iter)
+            KM_HIP(launch_divide_prep(t, sums, wsum, ctot, 1, K, (int)d, W.DP, W.Kp, centroids, centroids,
+                                      at<void>(ws, W.chat), s),
+                   "divide");
+        else
+            KM_HIP(launch_divide(sums, wsum, ctot, 1, K, (int)d, centroids, centroids, s), "divide");
     }
     if (counts) KM_HIP(hipMemcpyAsync(counts, ctot, (size_t)K * sizeof(int32_t), hipMemcpyDeviceToDevice, s), "copy");
     return KM_OK;

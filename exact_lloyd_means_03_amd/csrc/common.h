@@ -136,6 +136,11 @@ int segreduce_tw(int64_t B, int64_t N);
 hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* counts,
                          int64_t B, int64_t K, int d, const float* c_old, float* c_new,
                          hipStream_t s);
+// The divide fused with the prep of the next assignment (the tile layout of
+// launch_prep, from the new centroids).
+hipError_t launch_divide_prep(DType xt, const float* sums, const float* wsum, const int32_t* counts, int64_t B,
+                              int64_t K, int d, int DP, int64_t Kp, const float* c_old, float* c_new, void* blob,
+                              hipStream_t s);
 
 // Whole fits of scalar rows kept on chip (one block per row, all iterations).
 bool fit_1d_rows_fits(int64_t N, int64_t K);

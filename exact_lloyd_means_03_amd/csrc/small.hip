@@ -13,6 +13,36 @@
 
 namespace km {
 
+// One element of a tile row: the centroid coordinate rounded to the point
+// dtype (IEEE round to nearest even), stored; returns the rounded value.
+template <typename T>
+__device__ __forceinline__ float tile_elem(float v, T* out) {
+    if constexpr (sizeof(T) == 4) {
+        *out = v;
+        return v;
+    } else if constexpr (__is_same(T, _Float16)) {
+        const _Float16 h = (_Float16)v;  // v_cvt_f16_f32: round to nearest even
+        *out = h;
+        return (float)h;
+    } else {
+        const uint16_t h = f32_to_bf16_rne(v);
+        *out = h;
+        return bf16_to_f32(h);
+    }
+}
+
+// Where padded centroid row `row` of [B][Kp] lives in the tile layout: its
+// elements, and the slot of its -|c|^2/2.
+template <typename T>
+__device__ __forceinline__ void tile_row(char* blob, int64_t row, int DP, T** out, float** hn) {
+    const int TR = tile_rows(DP, (int)sizeof(T));
+    const int64_t tile = row / TR;  // batches hold whole tiles (Kp is a multiple of every tile size)
+    const int i = (int)(row % TR);
+    char* tbase = blob + tile * tile_bytes(DP, (int)sizeof(T));
+    *out = (T*)(tbase + (int64_t)i * DP * (int)sizeof(T));
+    *hn = (float*)(tbase + (int64_t)TR * DP * (int)sizeof(T)) + i;
+}
+
 // One wave per padded centroid row; 4 rows per 256-thread block.  Writes the
 // tile layout the matrix-core assignment copies to LDS: per tile, the rows in
 // the point dtype (zero padded to DP), then -|c|^2/2 of each row (-inf for
@@ -26,34 +56,74 @@ __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ C, int64
     const int64_t b = row / Kp, j = row - b * Kp;
     const bool real = j < K;
     const float* c = C + (b * K + j) * (int64_t)d;
-    const int TR = tile_rows(DP, (int)sizeof(T));
-    const int64_t tile = row / TR;  // batches hold whole tiles (Kp is a multiple of every tile size)
-    const int i = (int)(row % TR);
-    const int tb = tile_bytes(DP, (int)sizeof(T));
-    char* tbase = blob + tile * tb;
-    T* out = (T*)(tbase + (int64_t)i * DP * (int)sizeof(T));
+    T* out;
+    float* hn;
+    tile_row<T>(blob, row, DP, &out, &hn);
     float ss = 0.f;
     for (int k = lane; k < DP; k += 64) {
-        float v = (real && k < d) ? c[k] : 0.f;
-        float r;
-        if constexpr (sizeof(T) == 4) {
-            r = v;
-            out[k] = v;
-        } else if constexpr (__is_same(T, _Float16)) {
-            _Float16 h = (_Float16)v;  // v_cvt_f16_f32: round to nearest even
-            r = (float)h;
-            out[k] = h;
-        } else {
-            uint16_t h = f32_to_bf16_rne(v);
-            r = bf16_to_f32(h);
-            out[k] = h;
-        }
+        const float r = tile_elem<T>((real && k < d) ? c[k] : 0.f, out + k);
         ss = fmaf(r, r, ss);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    float* hn = (float*)(tbase + (int64_t)TR * DP * (int)sizeof(T));
-    if (lane == 0) hn[i] = real ? -0.5f * ss : -INFINITY;
+    if (lane == 0) *hn = real ? -0.5f * ss : -INFINITY;
+}
+
+// The divide of an update fused with the prep of the next assignment: per
+// padded row, c_new = S / W where the cluster has points (IEEE float32
+// division), c_old otherwise, and the same row written to the tile layout as
+// k_prep writes it.  c_new may alias c_old (each element is read, then
+// written, by one lane).
+template <typename T>
+__global__ __launch_bounds__(256) void k_divide_prep(const float* __restrict__ sums,
+                                                     const float* __restrict__ wsum,
+                                                     const int32_t* __restrict__ counts, int64_t BKp,
+                                                     int64_t K, int64_t Kp, int d, int DP, const float* c_old,
+                                                     float* c_new, char* __restrict__ blob) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= BKp) return;
+    const int64_t b = row / Kp, j = row - b * Kp;
+    const bool real = j < K;
+    const int64_t bj = b * K + j;
+    const int32_t n = real ? counts[bj] : 0;
+    const float W = n > 0 ? (wsum ? wsum[bj] : (float)n) : 1.f;
+    T* out;
+    float* hn;
+    tile_row<T>(blob, row, DP, &out, &hn);
+    float ss = 0.f;
+    for (int k = lane; k < DP; k += 64) {
+        float v = 0.f;
+        if (real && k < d) {
+            const int64_t i = bj * d + k;
+            v = n > 0 ? sums[i] / W : c_old[i];
+            c_new[i] = v;
+        }
+        const float r = tile_elem<T>(v, out + k);
+        ss = fmaf(r, r, ss);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) *hn = real ? -0.5f * ss : -INFINITY;
+}
+
+hipError_t launch_divide_prep(DType xt, const float* sums, const float* wsum, const int32_t* counts, int64_t B,
+                              int64_t K, int d, int DP, int64_t Kp, const float* c_old, float* c_new, void* blob,
+                              hipStream_t s) {
+    const int64_t rows = B * Kp;
+    if (rows == 0) return hipSuccess;
+    dim3 grid((unsigned)((rows + 3) / 4));
+    char* p = (char*)blob;
+    if (xt == DType::F32)
+        hipLaunchKernelGGL(k_divide_prep<float>, grid, dim3(256), 0, s, sums, wsum, counts, rows, K, Kp, d, DP,
+                           c_old, c_new, p);
+    else if (xt == DType::F16)
+        hipLaunchKernelGGL(k_divide_prep<_Float16>, grid, dim3(256), 0, s, sums, wsum, counts, rows, K, Kp, d, DP,
+                           c_old, c_new, p);
+    else
+        hipLaunchKernelGGL(k_divide_prep<bf16_t>, grid, dim3(256), 0, s, sums, wsum, counts, rows, K, Kp, d, DP,
+                           c_old, c_new, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,
