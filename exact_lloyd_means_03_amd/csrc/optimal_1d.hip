@@ -62,7 +62,7 @@ static int pow2_at_least(int n) {
 static size_t opt1d_lds_bytes(int N) {
     const size_t nd = (size_t)N + 1, np = (size_t)pow2_at_least(N);
     const size_t ne = np > nd ? np : nd, nb = np / 2 > 0 ? np / 2 : 1;
-    return 2 * nd * sizeof(double) + ne * sizeof(double) + nb * sizeof(uint64_t) + nd * sizeof(uint16_t) +
+    return 2 * nd * sizeof(double) + ne * sizeof(double) + 2 * nb * sizeof(uint64_t) + nd * sizeof(uint16_t) +
            (nb + 1) * sizeof(uint16_t);
 }
 
@@ -104,8 +104,11 @@ __global__ __launch_bounds__(kOpt1DThreads) void k_optimal_1d(
     double* P1 = P0 + (N + 1);
     double* E = P1 + (N + 1);
     uint64_t* keys = (uint64_t*)E;
-    uint64_t* s_best = (uint64_t*)(E + (NP > N + 1 ? NP : N + 1));
-    uint16_t* cut = (uint16_t*)(s_best + NB);
+    // per-level minimum keys, two levels' worth: a level's results are
+    // written out while the next level's ranges are formed
+    uint64_t* s_best_a = (uint64_t*)(E + (NP > N + 1 ? NP : N + 1));
+    uint64_t* s_best_b = s_best_a + NB;
+    uint16_t* cut = (uint16_t*)(s_best_b + NB);
     uint16_t* s_off = cut + (N + 1);
     double* Eg = Eg_all + b * (N + 1);
     uint16_t* cutg = cut_all + b * (int64_t)K * (N + 1);
@@ -191,20 +194,40 @@ __global__ __launch_bounds__(kOpt1DThreads) void k_optimal_1d(
         const int n = N - k + 1;  // j - k in [0, n)
         int L = 1;
         while ((1 << L) - 1 < n) ++L;  // a complete tree of 2^L - 1 >= n nodes
+        uint64_t* s_best = s_best_a;       // this level's keys
+        uint64_t* s_best_prev = s_best_b;  // the previous level's
+        // the cut and E_k of node sp of a level with spacing hh, from its key
+        auto finish = [&](int hh, int sp, const uint64_t* sb) {
+            const int jp = (2 * sp + 1) * hh - 1;
+            if (jp >= n) return;
+            const int j = k + jp;
+            const int bi = (int)(sb[sp] & 0xfff);
+            const double s1 = P1[j] - P1[bi];
+            Eg[j] = E[bi] - s1 * s1 / (P0[j] - P0[bi]);
+            cutg[(int64_t)(k - 1) * (N + 1) + j] = (uint16_t)bi;
+            cut[j] = (uint16_t)bi;
+        };
         for (int l = 0; l < L; ++l) {
             const int nsub = 1 << l, h = 1 << (L - 1 - l);
-            // node s of this level: j = k + (2s+1)h - 1, its range of cuts
+            // node s of this level: j = k + (2s+1)h - 1, its range of cuts.  Its
+            // parent (node s/2 of the previous level) is its right neighbour
+            // for even s and its left one for odd s; the parent's cut is read
+            // from the previous level's key, since it is written to cut[] only
+            // during this level's first phase.
             auto node = [&](int sn, int& j, int& ilo) -> int {  // returns the range length (0: no node)
                 const int jp = (2 * sn + 1) * h - 1;
                 if (jp >= n) return 0;
                 j = k + jp;
-                ilo = jp - h >= 0 ? (int)cut[j - h] : k - 1;
-                const int ihi = jp + h < n ? (int)cut[j + h] : N - 1;
+                const int par = l > 0 ? (int)(s_best_prev[sn >> 1] & 0xfff) : 0;
+                ilo = jp - h >= 0 ? ((sn & 1) ? par : (int)cut[j - h]) : k - 1;
+                const int ihi = jp + h < n ? ((sn & 1) ? (int)cut[j + h] : par) : N - 1;
                 int imax = ihi < j - 1 ? ihi : j - 1;
                 if (imax < ilo) imax = ilo;  // only where rounding breaks the order of the cuts
                 return imax - ilo + 1;
             };
-            // (a) range lengths, four consecutive nodes per thread, and their exclusive scan
+            // (a) range lengths, four consecutive nodes per thread, and their
+            // exclusive scan; the left child of every node of the previous
+            // level writes that node's cut and E_k
             int len[4], sum = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -212,6 +235,7 @@ __global__ __launch_bounds__(kOpt1DThreads) void k_optimal_1d(
                 int j, ilo;
                 len[q] = sn < nsub ? node(sn, j, ilo) : 0;
                 if (sn < nsub) s_best[sn] = ~(uint64_t)0;
+                if (l > 0 && sn < nsub && (sn & 1) == 0) finish(2 * h, sn >> 1, s_best_prev);
                 sum += len[q];
             }
             int incl = sum;
@@ -269,21 +293,13 @@ __global__ __launch_bounds__(kOpt1DThreads) void k_optimal_1d(
                 atomicMin(&s_best[sn], best);
             }
             __syncthreads();
-            // (c) the cut and E_k of every node of the level
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int sn = 4 * tid + q;
-                int j, ilo;
-                if (sn < nsub && node(sn, j, ilo) > 0) {
-                    const int bi = (int)(s_best[sn] & 0xfff);
-                    const double s1 = P1[j] - P1[bi];
-                    Eg[j] = E[bi] - s1 * s1 / (P0[j] - P0[bi]);
-                    cutg[(int64_t)(k - 1) * (N + 1) + j] = (uint16_t)bi;
-                    cut[j] = (uint16_t)bi;
-                }
-            }
-            __syncthreads();
+            uint64_t* tmp = s_best;
+            s_best = s_best_prev;
+            s_best_prev = tmp;
         }
+        // (c) the cut and E_k of every node of the last level
+        for (int sn = tid; sn < (1 << (L - 1)); sn += kOpt1DThreads) finish(1, sn, s_best_prev);
+        __syncthreads();
         // E_k back into LDS (the barrier makes this block's device-memory
         // writes visible to all of its threads)
         for (int j = k + tid; j <= N; j += kOpt1DThreads) E[j] = Eg[j];
