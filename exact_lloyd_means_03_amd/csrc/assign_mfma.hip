@@ -14,8 +14,9 @@
 //   * centroid tiles of up to 256 rows (64 KB, followed by their -|c|^2/2
 //     values) move from device memory to LDS by direct DMA
 //     (global_load_lds_dwordx4), double-buffered, and are shared by the 8 (or
-//     4) waves of the block; rows are XOR-swizzled in 16-byte chunks so the
-//     32 A-operand rows read by one instruction fall in distinct banks;
+//     4) waves of the block; rows are swizzled in 16-byte chunks (XOR, or a
+//     rotation for 96-wide rows) so the A-operand rows read together fall in
+//     distinct banks;
 //   * software pipeline over 32-row blocks: the MFMAs of block s are issued
 //     next to the epilogue of block s-1, so the matrix core and the vector
 //     ALU work at the same time;
@@ -36,7 +37,9 @@
 //     once, and each walks groups of points i, i + grid, ...; the tile
 //     pipeline runs on from one group into the next (the next group's first
 //     tile loads during the current group's last tile), which matters when
-//     K is small and a group walks few tiles.
+//     K is small and a group walks few tiles;
+//   * a launch with fewer groups than compute units (a mini-batch against
+//     many centroids) takes one column block per wave, doubling the groups.
 #include <atomic>
 
 #include "common.h"
