@@ -488,7 +488,9 @@ def bench_emeans(args, km, wl):
                    "batch": batch, "epochs": E, "steps_per_run": T, "alpha0": wl.em_alpha0,
                    "floor": wl.em_floor, "dead_frac": wl.em_dead_frac, "eps": wl.em_eps},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": _traffic(wl), "kernel": "k_assign_mfma (one batch)", "algorithmic_per_launch": flops,
+                     "traffic": _traffic(wl),
+                     "kernel": "k_assign_mfma + k_assign_merge (one batch, centroid tiles in slices)",
+                     "algorithmic_per_launch": flops,
                      "avg_launch_ms": assign_ms},
         "run_ms_event": run_ms,
         "quality": {"emeans_mse_by_epochs": em_mse, "emeans_ms_by_epochs": em_ms,

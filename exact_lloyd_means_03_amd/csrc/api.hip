@@ -46,7 +46,7 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     w.DP = padded_dim(d, xt != DType::F32);
     w.Kp = padded_k(K);
     const bool a1d = use_assign_1d(d, K);
-    w.nblk_assign = a1d ? assign_1d_blocks(N) : assign_mfma_blocks(B, N, w.DP, xt);
+    w.nblk_assign = a1d ? assign_1d_blocks(N) : assign_mfma_blocks(B, N, w.DP, xt, w.Kp);
     if (w.nblk_assign < 1) w.nblk_assign = 1;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -58,6 +58,7 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     w.chat = take(a1d ? 0 : Bz * (w.Kp / tile_rows(w.DP, dtype_bytes(xt))) *
                                 (size_t)tile_bytes(w.DP, dtype_bytes(xt)));
     w.obj_part = take(Bz * w.nblk_assign * sizeof(double));
+    w.split = take(a1d ? 0 : assign_mfma_scratch_bytes(B, N, w.DP, xt, w.Kp));
     w.labels = take(Bz * N * sizeof(int32_t));
     w.counts = take(Bz * K * sizeof(int32_t));
     w.sums = take(Bz * K * d * sizeof(float));
@@ -162,7 +163,7 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
         void* blob = at<void>(ws, W.chat);
         if (prep) KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, blob, s), "prep");
         KM_HIP(launch_assign_mfma(xt, x, B, N, (int)d, W.DP, blob, W.Kp, w, labels, min_dist, part,
-                                  W.nblk_assign, s),
+                                  W.nblk_assign, at<void>(ws, W.split), s),
                "assign_mfma");
     }
     if (obj_out) {
@@ -229,7 +230,7 @@ constexpr int64_t kStreamAlign = 4096;  // chunk sizes: a multiple of every assi
 struct StreamPlan {
     Workspace chunk;  // the per-chunk plan (B = 1, N = chunk points)
     int64_t chunk_n = 0, nchunks = 0, nblk_chunk = 0, nblk_total = 0;
-    size_t xbuf[2] = {0, 0}, wbuf[2] = {0, 0}, obj_all = 0, counts_total = 0, total = 0;
+    size_t xbuf[2] = {0, 0}, wbuf[2] = {0, 0}, obj_all = 0, counts_total = 0, split = 0, total = 0;
 };
 
 StreamPlan plan_stream(int64_t N, int64_t d, int64_t K, DType xt, int64_t chunk) {
@@ -242,7 +243,7 @@ StreamPlan plan_stream(int64_t N, int64_t d, int64_t K, DType xt, int64_t chunk)
     p.chunk = plan_workspace(1, c, d, K, xt);
     p.nblk_chunk = p.chunk.nblk_assign;
     const int64_t last = N - (p.nchunks > 0 ? (p.nchunks - 1) * c : 0);
-    const int64_t nblk_last = p.nchunks > 0 ? assign_mfma_blocks(1, last, p.chunk.DP, xt) : 0;
+    const int64_t nblk_last = p.nchunks > 0 ? assign_mfma_blocks(1, last, p.chunk.DP, xt, p.chunk.Kp) : 0;
     p.nblk_total = p.nchunks > 0 ? (p.nchunks - 1) * p.nblk_chunk + nblk_last : 1;
     size_t off = p.chunk.total;
     auto take = [&](size_t bytes) {
@@ -254,6 +255,11 @@ StreamPlan plan_stream(int64_t N, int64_t d, int64_t K, DType xt, int64_t chunk)
     for (int i = 0; i < 2; ++i) p.wbuf[i] = take((size_t)c * sizeof(float));
     p.obj_all = take((size_t)p.nblk_total * sizeof(double));
     p.counts_total = take((size_t)K * sizeof(int32_t));
+    // assignment scratch of a full and of the last chunk (a short last chunk
+    // may cut the centroids into slices where a full one does not)
+    const size_t sc = assign_mfma_scratch_bytes(1, c, p.chunk.DP, xt, p.chunk.Kp),
+                 sl = p.nchunks > 0 ? assign_mfma_scratch_bytes(1, last, p.chunk.DP, xt, p.chunk.Kp) : 0;
+    p.split = take(sc > sl ? sc : sl);
     p.total = off;
     return p;
 }
@@ -296,7 +302,7 @@ hipError_t stream_res(int dev, StreamRes** out) {
 struct EmeansPlan {
     Workspace batch;  // the per-batch plan (B = 1, N = batch points)
     int64_t mfull = 0, nb = 0, steps = 0;
-    size_t S = 0, Nc = 0, F = 0, G = 0, list_j = 0, list_k = 0, obj_part = 0, total = 0;
+    size_t S = 0, Nc = 0, F = 0, G = 0, list_j = 0, list_k = 0, obj_part = 0, split = 0, total = 0;
 };
 
 EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch, int32_t epochs) {
@@ -320,15 +326,21 @@ EmeansPlan plan_emeans(int64_t N, int64_t d, int64_t K, DType xt, int64_t batch,
     // objective partials of one batch's assignment: a shorter last batch can
     // have more of them than a full one (fewer points per group when its
     // groups would not fill the chip)
+    // (the same for the assignment scratch)
     int64_t nblk = 1;
+    size_t split = 0;
     if (p.nb > 0) {
         const int64_t mlast = N - (p.nb - 1) * batch;
         for (const int64_t m : {p.mfull, mlast}) {
-            const int64_t n = use_assign_1d(d, K) ? assign_1d_blocks(m) : assign_mfma_blocks(1, m, p.batch.DP, xt);
+            const bool a1d = use_assign_1d(d, K);
+            const int64_t n = a1d ? assign_1d_blocks(m) : assign_mfma_blocks(1, m, p.batch.DP, xt, p.batch.Kp);
             if (n > nblk) nblk = n;
+            const size_t sb = a1d ? 0 : assign_mfma_scratch_bytes(1, m, p.batch.DP, xt, p.batch.Kp);
+            if (sb > split) split = sb;
         }
     }
     p.obj_part = take((size_t)nblk * sizeof(double));
+    p.split = take(split);
     p.total = off;
     return p;
 }
@@ -538,7 +550,8 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
             KM_HIP(hipStreamWaitEvent(s, R->copied[buf], 0), "event wait");
             int32_t* lab = labels ? labels + p0 : at<int32_t>(ws, W.labels);
             KM_HIP(launch_assign_mfma(t, xb, 1, nc, (int)d, W.DP, at<void>(ws, W.chat), W.Kp, wb, lab, nullptr,
-                                      obj_all + ci * P.nblk_chunk, assign_mfma_blocks(1, nc, W.DP, t), s),
+                                      obj_all + ci * P.nblk_chunk, assign_mfma_blocks(1, nc, W.DP, t, W.Kp),
+                                      at<void>(ws, P.split), s),
                    "assign_mfma");
             int32_t* cnt = at<int32_t>(ws, W.counts);
             int32_t* offsets = at<int32_t>(ws, W.offsets);
@@ -643,10 +656,11 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
             KM_HIP(launch_assign_1d(t, xb, 1, m, centroids, K, nullptr, lab, nullptr, part, nblk, nblk, s),
                    "assign_1d");
         } else {
-            nblk = assign_mfma_blocks(1, m, W.DP, t);
+            nblk = assign_mfma_blocks(1, m, W.DP, t, W.Kp);
             void* blob = at<void>(ws, W.chat);
             KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, blob, s), "prep");
-            KM_HIP(launch_assign_mfma(t, xb, 1, m, (int)d, W.DP, blob, W.Kp, nullptr, lab, nullptr, part, nblk, s),
+            KM_HIP(launch_assign_mfma(t, xb, 1, m, (int)d, W.DP, blob, W.Kp, nullptr, lab, nullptr, part, nblk,
+                                      at<void>(ws, P.split), s),
                    "assign_mfma");
         }
         if (objective) KM_HIP(launch_obj_reduce(part, 1, nblk, objective + st, 1, s), "obj_reduce");

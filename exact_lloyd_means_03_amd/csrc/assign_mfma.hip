@@ -39,7 +39,13 @@
 //     tile loads during the current group's last tile), which matters when
 //     K is small and a group walks few tiles;
 //   * a launch with fewer groups than compute units (a mini-batch against
-//     many centroids) takes one column block per wave, doubling the groups.
+//     many centroids) cuts the centroid tiles into slices of at least 8
+//     tiles: each (group, slice) unit writes its points' best value and
+//     index to scratch, and k_assign_merge keeps, per point, the best over
+//     the slices (the earlier slice on equal values, so the smallest index
+//     still wins ties).  Groups keep their full width, so every A fragment
+//     read from LDS still feeds two matrix-core instructions.  With too few
+//     tiles to slice, one column block per wave doubles the groups instead.
 #include <atomic>
 
 #include "common.h"
@@ -222,9 +228,9 @@ __device__ __forceinline__ void dma_tile(const char* tile_g, char* dst, int wave
 
 template <typename T, int DP, bool VEC, int NCBT, int WAVEST>
 __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
-    const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int64_t ntiles,
+    const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int ntiles, int tps,
     const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
-    double* __restrict__ obj_part, int64_t gpb, int64_t ngroups) {
+    double* __restrict__ obj_part, int64_t gpb, int64_t bgroups, int64_t ngroups, float* __restrict__ split) {
     typedef AssignCfg<T, DP, NCBT, WAVEST> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
@@ -235,11 +241,24 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
-    // groups of PTS points, g = b * gpb + pg; block i takes groups i, i + gridDim.x, ...
+    // Work units: group pg of PTS points of problem b against centroid slice
+    // sl (tiles [sl * tps, sl * tps + tps) of the problem's ntiles), unit
+    // g = sl * bgroups + b * gpb + pg; block i takes units i, i + gridDim.x, ...
+    // With one slice (tps = ntiles) a unit is a whole point group.
     int64_t g = blockIdx.x;
     if (g >= ngroups) return;
-    int64_t b = g / gpb, pg = g % gpb;
-    const char* Bb = blob + b * ntiles * (int64_t)Cfg::TILE;
+    int64_t b, pg;
+    int t0;
+    auto decode = [&](int64_t u, int64_t& bb, int64_t& pgg, int& tt) {
+        const int sl = (int)(u / bgroups);
+        const int64_t r = u - sl * bgroups;
+        bb = r / gpb;
+        pgg = r - bb * gpb;
+        tt = sl * tps;
+    };
+    decode(g, b, pg, t0);
+    int nt = ntiles - t0 < tps ? ntiles - t0 : tps;  // tiles of this unit's slice
+    const char* Bb = blob + (b * ntiles + t0) * (int64_t)Cfg::TILE;
 
     // per-lane DMA source offsets (the same for every tile)
     uint32_t voff[Cfg::NIW];
@@ -408,8 +427,10 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
         // group's last tile, its points while this group's outputs are written
         const int64_t gn = g + gridDim.x;
         const bool has_next = gn < ngroups;
-        const int64_t bn = has_next ? gn / gpb : b;
-        const char* Bn = blob + bn * ntiles * (int64_t)Cfg::TILE;
+        int64_t bn = b, pgn = pg;
+        int t0n = t0;
+        if (has_next) decode(gn, bn, pgn, t0n);
+        const char* Bn = blob + (bn * ntiles + t0n) * (int64_t)Cfg::TILE;
 
         // Software pipeline over 32-row blocks (acc0 / acc1 alternate).  The loop
         // body is one basic block: every iteration issues one tile DMA (the next
@@ -422,18 +443,18 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc1[cb][r] = -INFINITY;
         int32_t blk1 = 0;
-        for (int64_t t = 0; t < ntiles; ++t) {
+        for (int t = 0; t < nt; ++t) {
             const char* tile = s_tile[(par + t) & 1];
             F a0 = lda_at(tile, 0, 0);
             F a1 = KSTEPS > 1 ? lda_at(tile, 0, 1) : lda_at(tile, 1, 0);
             f32x16 h = ldh_at(tile, 0);
-            const char* src = t + 1 < ntiles ? Bb + (t + 1) * (int64_t)Cfg::TILE
-                              : has_next     ? Bn
-                                             : Bb + t * (int64_t)Cfg::TILE;
+            const char* src = t + 1 < nt ? Bb + (t + 1) * (int64_t)Cfg::TILE
+                              : has_next ? Bn
+                                         : Bb + t * (int64_t)Cfg::TILE;
             dma_tile<Cfg>(src, s_tile[(par + t + 1) & 1], wave, lane, voff);
 #pragma unroll
             for (int rb = 0; rb < NRB; rb += 2) {
-                const int32_t blk0 = (int32_t)(t * NRB) + rb;
+                const int32_t blk0 = (t0 + t) * NRB + rb;
                 mma_block(tile, rb, acc0, acc1, blk1, a0, a1, h);
                 mma_block(tile, rb + 1, acc1, acc0, blk0, a0, a1, h);
                 blk1 = blk0 + 1;
@@ -442,7 +463,7 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             __syncthreads();
         }
-        par = (int)((par + ntiles) & 1);
+        par = (par + nt) & 1;
         epilogue(acc1, blk1);
 
         // ---- recover the row, merge the two half-waves that share a point ----
@@ -462,16 +483,33 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
         }
         // the next group's points load while this group's outputs are written
         // (xx keeps this group's norms until then)
-        if (has_next) load_points(bn, gn % gpb);
+        if (has_next) load_points(bn, pgn);
         double obj = 0.0;
+        if (split) {
+            // one slice of the centroids: its best value and centroid per
+            // point (and, from the first slice, the point's squared norm) for
+            // k_assign_merge; split holds [nslice][B*N] values, then as many
+            // indices, then [B*N] norms
+            const int64_t BN = bgroups / gpb * N, sl = t0 / tps, ns = (ntiles + tps - 1) / tps;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            const int64_t p = pg * Cfg::PTS + (wave * NCB + cb) * 32 + col;
-            if (half == 0 && p < N) {
-                const float dist = fmaxf(xx[cb] - 2.f * best[cb], 0.f);
-                labels[b * N + p] = bidx[cb];
-                if (min_dist) min_dist[b * N + p] = dist;
-                obj += (double)(w ? w[b * N + p] : 1.f) * (double)dist;
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int64_t p = pg * Cfg::PTS + (wave * NCB + cb) * 32 + col;
+                if (half == 0 && p < N) {
+                    split[sl * BN + b * N + p] = best[cb];
+                    ((int32_t*)split)[(ns + sl) * BN + b * N + p] = bidx[cb];
+                    if (sl == 0) split[2 * ns * BN + b * N + p] = xx[cb];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int64_t p = pg * Cfg::PTS + (wave * NCB + cb) * 32 + col;
+                if (half == 0 && p < N) {
+                    const float dist = fmaxf(xx[cb] - 2.f * best[cb], 0.f);
+                    labels[b * N + p] = bidx[cb];
+                    if (min_dist) min_dist[b * N + p] = dist;
+                    obj += (double)(w ? w[b * N + p] : 1.f) * (double)dist;
+                }
             }
         }
         if (obj_part) {
@@ -489,7 +527,9 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
         if (!has_next) break;
         g = gn;
         b = bn;
-        pg = gn % gpb;
+        pg = pgn;
+        t0 = t0n;
+        nt = ntiles - t0 < tps ? ntiles - t0 : tps;
         Bb = Bn;
         point_norms();
     }
@@ -497,39 +537,103 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// Point groups of a launch: WAVES waves of NCB 32-point column blocks.  The
-// default shape, unless it leaves fewer groups than the chip has compute
-// units (a mini-batch against many centroids); then one column block per
-// wave, which doubles the groups, each reading the centroid tiles for half
-// as many points.
+// Work units of a launch.  A point group is WAVES waves of NCB 32-point
+// column blocks.  With at least as many groups as the chip has compute units
+// a unit is a group against all centroid tiles.  With fewer (a mini-batch
+// against many centroids) the tiles are cut into slices of at least
+// kMinSliceTiles tiles, so that groups x slices reach the compute units while
+// each group keeps its full width (every A fragment read from LDS still feeds
+// NCB matrix-core instructions); k_assign_merge then picks each point's best
+// over the slices.  Too few tiles to slice: one column block per wave, which
+// doubles the groups, each reading the tiles for half as many points.
 constexpr int64_t kFewGroups = 256;
+constexpr int64_t kMinSliceTiles = 8;
 
 struct GroupShape {
     int ncb, waves;
+    int64_t nslice, tps;  // centroid slices, tiles per slice (the last one may hold fewer)
 };
 
 template <typename T>
-static GroupShape group_shape(int64_t B, int64_t N, int DP) {
+static GroupShape group_shape(int64_t B, int64_t N, int DP, int64_t ntiles) {
     const int def = default_ncb(DP, sizeof(T)), wv = assign_waves(DP, sizeof(T));
-    if (def == 1) return {1, wv};
     const int64_t pts = (int64_t)wv * def * 32;
-    if (B * ((N + pts - 1) / pts) >= kFewGroups) return {def, wv};
+    const int64_t groups = B * ((N + pts - 1) / pts);
+    if (groups >= kFewGroups || groups == 0) return {def, wv, 1, ntiles};
+    int64_t ns = (kFewGroups + groups - 1) / groups;
+    if (ns > ntiles / kMinSliceTiles) ns = ntiles / kMinSliceTiles;
+    if (ns >= 2) {
+        const int64_t tps = (ntiles + ns - 1) / ns;
+        return {def, wv, (ntiles + tps - 1) / tps, tps};
+    }
     // two column blocks on half the waves (the same points per group) timed
     // the same within noise on batches of 32768..100000 points
-    return {1, wv};
+    return {1, wv, 1, ntiles};
 }
 
 template <typename T>
-static int64_t blocks_for(int64_t B, int64_t N, int DP) {
-    const GroupShape g = group_shape<T>(B, N, DP);
+static GroupShape shape_for(int64_t B, int64_t N, int DP, int64_t Kp) {
+    return group_shape<T>(B, N, DP, Kp / tile_rows(DP, sizeof(T)));
+}
+
+static int64_t groups_per_problem(const GroupShape& g, int64_t N) {
     const int64_t pts = (int64_t)g.waves * g.ncb * 32;
     return (N + pts - 1) / pts;
 }
 
-int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt) {
-    if (xt == DType::F32) return blocks_for<float>(B, N, DP);
-    if (xt == DType::F16) return blocks_for<_Float16>(B, N, DP);
-    return blocks_for<bf16_t>(B, N, DP);
+static GroupShape shape_of(int64_t B, int64_t N, int DP, DType xt, int64_t Kp) {
+    if (xt == DType::F32) return shape_for<float>(B, N, DP, Kp);
+    if (xt == DType::F16) return shape_for<_Float16>(B, N, DP, Kp);
+    return shape_for<bf16_t>(B, N, DP, Kp);
+}
+
+int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt, int64_t Kp) {
+    return groups_per_problem(shape_of(B, N, DP, xt, Kp), N);
+}
+
+size_t assign_mfma_scratch_bytes(int64_t B, int64_t N, int DP, DType xt, int64_t Kp) {
+    const GroupShape g = shape_of(B, N, DP, xt, Kp);
+    if (g.nslice < 2) return 0;
+    return (size_t)(2 * g.nslice + 1) * (size_t)(B * N) * 4;
+}
+
+// One block per point group: the best (largest x.c - |c|^2/2) over the
+// slices, the earlier slice on equal values (its centroid indices are the
+// smaller ones, and within a slice the unit already kept the smallest index),
+// then the outputs as the one-slice kernel writes them.
+__global__ __launch_bounds__(256) void k_assign_merge(const float* __restrict__ sv, const int32_t* __restrict__ si,
+                                                      const float* __restrict__ sxx, int64_t nslice, int64_t BN,
+                                                      int64_t N, int pts, int64_t gpb, const float* __restrict__ w,
+                                                      int32_t* __restrict__ labels, float* __restrict__ min_dist,
+                                                      double* __restrict__ obj_part) {
+    __shared__ double s_obj[4];
+    const int64_t grp = blockIdx.x, b = grp / gpb, pg = grp - b * gpb;
+    double obj = 0.0;
+    for (int q = threadIdx.x; q < pts; q += 256) {
+        const int64_t p = pg * pts + q;
+        if (p >= N) break;
+        const int64_t i = b * N + p;
+        float bv = sv[i];
+        int32_t bi = si[i];
+        for (int64_t sl = 1; sl < nslice; ++sl) {
+            const float v = sv[sl * BN + i];
+            if (v > bv) {
+                bv = v;
+                bi = si[sl * BN + i];
+            }
+        }
+        const float dist = fmaxf(sxx[i] - 2.f * bv, 0.f);
+        labels[i] = bi;
+        if (min_dist) min_dist[i] = dist;
+        obj += (double)(w ? w[i] : 1.f) * (double)dist;
+    }
+    if (obj_part) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) obj += __shfl_xor(obj, o, 64);
+        if ((threadIdx.x & 63) == 0) s_obj[threadIdx.x >> 6] = obj;
+        __syncthreads();
+        if (threadIdx.x == 0) obj_part[grp] = s_obj[0] + s_obj[1] + s_obj[2] + s_obj[3];
+    }
 }
 
 // Persistent blocks: as many as the device holds at once (compute units x
@@ -560,55 +664,73 @@ static int64_t resident_blocks() {
 
 template <typename T, int DP, int NCBT, int WV>
 static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const void* blob, int64_t ntiles,
-                           const float* w, int32_t* labels, float* min_dist, double* obj_part, int64_t nblk,
-                           hipStream_t s) {
-    const int64_t ngroups = B * nblk;
+                           const GroupShape& gs, const float* w, int32_t* labels, float* min_dist,
+                           double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
+    const int64_t bgroups = B * nblk, ngroups = bgroups * gs.nslice;
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
     const int64_t P = vec ? resident_blocks<T, DP, true, NCBT, WV>() : resident_blocks<T, DP, false, NCBT, WV>();
     dim3 grid((unsigned)(ngroups < P ? ngroups : P));
+    const bool split = gs.nslice > 1;
+    const int64_t BN = B * N;
+    float* sv = split ? (float*)scratch : nullptr;
+    const int32_t* si = split ? (const int32_t*)scratch + gs.nslice * BN : nullptr;
+    const float* sxx = split ? (const float*)scratch + 2 * gs.nslice * BN : nullptr;
+    double* part = split ? nullptr : obj_part;
     if (vec)
         hipLaunchKernelGGL((k_assign_mfma<T, DP, true, NCBT, WV>), grid, dim3(64 * WV), 0, s, (const T*)x, N, d,
-                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
+                           (const char*)blob, (int)ntiles, (int)gs.tps, w, labels, min_dist, part, nblk, bgroups,
+                           ngroups, sv);
     else
         hipLaunchKernelGGL((k_assign_mfma<T, DP, false, NCBT, WV>), grid, dim3(64 * WV), 0, s, (const T*)x, N, d,
-                           (const char*)blob, ntiles, w, labels, min_dist, obj_part, nblk, ngroups);
+                           (const char*)blob, (int)ntiles, (int)gs.tps, w, labels, min_dist, part, nblk, bgroups,
+                           ngroups, sv);
+    if (!split) return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_assign_merge, dim3((unsigned)bgroups), dim3(256), 0, s, sv, si, sxx, gs.nslice, BN, N,
+                       WV * NCBT * 32, nblk, w, labels, min_dist, obj_part);
     return hipGetLastError();
 }
 
-// nblk: point groups per problem, as assign_mfma_blocks(B, N, DP, xt) gives
-// them (the group shape follows from the same rule).
+// nblk: point groups per problem, as assign_mfma_blocks(B, N, DP, xt, Kp)
+// gives them (the group shape follows from the same rule); scratch: at least
+// assign_mfma_scratch_bytes(B, N, DP, xt, Kp) bytes (4-byte aligned).
 template <typename T, int DP>
 static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
-                           double* obj_part, int64_t nblk, hipStream_t s) {
-    if (nblk != blocks_for<T>(B, N, DP)) return hipErrorInvalidValue;
+                           double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
+    const GroupShape g = group_shape<T>(B, N, DP, ntiles);
+    if (nblk != groups_per_problem(g, N)) return hipErrorInvalidValue;
+    if (g.nslice > 1 && scratch == nullptr) return hipErrorInvalidValue;
     constexpr int DEF = default_ncb(DP, sizeof(T)), WV = assign_waves(DP, sizeof(T));
     if constexpr (DEF == 2) {
-        const GroupShape g = group_shape<T>(B, N, DP);
         if (g.ncb == 1)
-            return launch_n<T, DP, 1, WV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+            return launch_n<T, DP, 1, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk,
+                                          scratch, s);
     }
-    return launch_n<T, DP, DEF, WV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+    return launch_n<T, DP, DEF, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk, scratch, s);
 }
 
 template <typename T>
 static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, const void* blob,
                             int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
-                            double* obj_part, int64_t nblk, hipStream_t s) {
+                            double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
     switch (DP) {
-        case 16: return launch_t<T, 16>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
-        case 32: return launch_t<T, 32>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
-        case 64: return launch_t<T, 64>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 16: return launch_t<T, 16>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+        case 32: return launch_t<T, 32>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+        case 64: return launch_t<T, 64>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
         case 96:
             if constexpr (sizeof(T) == 2)
-                return launch_t<T, 96>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+                return launch_t<T, 96>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
             else
                 return hipErrorInvalidValue;
-        case 128: return launch_t<T, 128>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
-        case 256: return launch_t<T, 256>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+        case 128:
+            return launch_t<T, 128>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+        case 256:
+            return launch_t<T, 256>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
         case 512:
             if constexpr (sizeof(T) == 2)
-                return launch_t<T, 512>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, s);
+                return launch_t<T, 512>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
             else
                 return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
@@ -617,13 +739,14 @@ static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, 
 
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
-                              float* min_dist, double* obj_part, int64_t nblk, hipStream_t s) {
+                              float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
+    const int64_t ntiles = Kp / tile_rows(DP, dtype_bytes(xt));
     if (xt == DType::F32)
-        return launch_dp<float>(DP, x, B, N, d, blob, Kp / tile_rows(DP, 4), w, labels, min_dist, obj_part, nblk, s);
+        return launch_dp<float>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
     if (xt == DType::F16)
-        return launch_dp<_Float16>(DP, x, B, N, d, blob, Kp / tile_rows(DP, 2), w, labels, min_dist, obj_part, nblk, s);
-    return launch_dp<bf16_t>(DP, x, B, N, d, blob, Kp / tile_rows(DP, 2), w, labels, min_dist, obj_part, nblk, s);
+        return launch_dp<_Float16>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+    return launch_dp<bf16_t>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
 }
 
 }  // namespace km

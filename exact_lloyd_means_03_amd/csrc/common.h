@@ -70,6 +70,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 struct Workspace {
     size_t chat;       // [B][Kp/tile_rows] tiles: rows x DP in the point dtype + -|c|^2/2 segment
     size_t obj_part;   // [B][nblk_assign] double: per-block objective partials
+    size_t split;      // matrix-core assignment scratch (centroid slices)
     size_t labels;     // [B][N] int32: labels of the current assignment (fit)
     size_t counts;     // [B][K] int32
     size_t offsets;    // [B][K+1] int32
@@ -93,10 +94,14 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt);
 hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, int DP, int64_t Kp,
                        void* blob, hipStream_t s);
 
+// Matrix-core assignment.  nblk = assign_mfma_blocks(...) point groups per
+// problem (one objective partial each); scratch: assign_mfma_scratch_bytes(...)
+// bytes (zero unless the launch cuts the centroids into slices).
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
-                              float* min_dist, double* obj_part, int64_t nblk, hipStream_t s);
-int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt);
+                              float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s);
+int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
+size_t assign_mfma_scratch_bytes(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
 
 // obj_part (may be NULL): the objective partial of block j of row b goes to
 // obj_part[b * obj_stride + j].

@@ -83,6 +83,7 @@ def _oracle(x, init, batch, epochs, alpha0, floor, dead_frac, eps, u):
     ("f16", 4001, 1, 5, 1001, 2),        # scalar points, K <= 16, batches not 4-aligned
     ("bf16", 3000, 7, 10, 5000, 2),      # batch above N: one full batch per epoch
     ("bf16", 8000, 96, 200, 2048, 2),    # 96-wide rows
+    ("f16", 8192, 32, 4096, 2048, 1),    # 4 point groups, 16 tiles: centroid slices
 ])
 def test_emeans_trajectory_parity(km, dtype, N, d, K, batch, epochs):
     what = f"emeans {dtype} N{N} d{d} K{K} batch{batch}"

@@ -308,3 +308,52 @@ def test_k_greater_than_n(km):
     parity.check_labels(lab.cpu().numpy(), ref["labels"], ref["d1"], ref["d2"], "K>N")
     parity.check_centroids(cen.cpu().numpy(), ref["centroids"], "K>N")
     assert int(cnt.sum()) == 50
+
+
+# Few point groups against many centroid tiles: the launch cuts the tiles into
+# slices (at least 8 tiles each) and merges each point's best over the slices.
+@pytest.mark.parametrize("dtype,B,N,d,K,weighted", [
+    ("f16", 1, 3000, 128, 4096, False),   # 6 groups, 16 tiles: 2 slices
+    ("bf16", 1, 1500, 96, 16384, True),   # 64 tiles: 8 slices
+    ("f16", 1, 1000, 512, 2048, False),   # 64-row tiles, one column block per wave: 4 slices
+    ("f32", 1, 1000, 256, 1700, True),    # 28 tiles: slices of 10, 10 and 8
+    ("f16", 3, 700, 64, 4096, True),      # several problems
+    ("bf16", 1, 1, 128, 8192, False),     # one point
+    ("f32", 2, 777, 61, 3000, False),     # padded rows, ragged groups
+])
+def test_assign_centroid_slices(km, dtype, B, N, d, K, weighted):
+    what = f"slices {dtype} B{B} N{N} d{d} K{K} w{weighted}"
+    x, C = _rand_problem(B, N, d, K, dtype, seed=N + d + K)
+    w = torch.rand(B, N, generator=torch.Generator().manual_seed(K)) * 0.9 + 0.1 if weighted else None
+    _assign_case(km, x, C, w, what)
+
+
+def test_assign_centroid_slices_ties_across_slices(km):
+    """The second half of the centroids repeats the first, so every point's
+    best value is reached in both slices; the merged label is the smaller
+    index, as the textbook scan in ascending centroid order gives."""
+    B, N, d, K = 1, 2500, 128, 4096
+    x, C = _rand_problem(B, N, d, K, "f16", seed=5)
+    C[:, K // 2:] = C[:, :K // 2]
+    x[0, :100] = C[0, 7:107].to(torch.float16)  # points exactly on centroids as well
+    gl = _assign_case(km, x, C, None, "ties across slices")
+    assert (gl < K // 2).all()
+
+
+def test_fit_with_centroid_slices(km):
+    """Two fit iterations on a sliced launch: the fused divide writes the
+    tiles that the next sliced assignment reads."""
+    x, C = _rand_problem(1, 3000, 128, 4096, "bf16", seed=11)
+    xd, Cd = x.cuda(), C.cuda()
+    c1, l1, n1, J1 = km.kmeans_fit(xd, Cd, 1)
+    c2, l2, n2, J2 = km.kmeans_fit(xd, Cd, 2)
+    torch.cuda.synchronize()
+    X, Chat, lab_ref, d1, d2 = parity.oracle_assign(workloads.raw_bits(x), "bf16", C.numpy())
+    parity.check_labels(l1.cpu().numpy(), lab_ref, d1, d2, "fit slices it 1")
+    ref_c, ref_n, _, _ = oracle.update(X, None, l1.cpu().numpy(), C.numpy())
+    np.testing.assert_array_equal(n1.cpu().numpy(), ref_n)
+    parity.check_centroids(c1.cpu().numpy(), ref_c, "fit slices it 1")
+    # the second iteration: the oracle's assignment at the GPU's first centroids
+    X, Chat, lab_ref, d1, d2 = parity.oracle_assign(workloads.raw_bits(x), "bf16", c1.cpu().numpy())
+    parity.check_labels(l2.cpu().numpy(), lab_ref, d1, d2, "fit slices it 2")
+    parity.check_objective(J2.cpu().numpy()[:, 1], d1.sum(-1), "fit slices it 2")

@@ -91,6 +91,28 @@ def test_stream_fit_parity(km, dtype, d, weighted, chunk, pinned):
         parity.check_centroids(cen.cpu().numpy()[None], cf.cpu().numpy(), what)
 
 
+def test_stream_fit_centroid_slices(km):
+    """Chunks of 4096 points (8 groups) and a last chunk of 100 points
+    against 4096 centroids: both assignments cut the centroid tiles into
+    slices, and the last chunk's slices use the scratch sized for it."""
+    N, d, K, chunk = 2 * 4096 + 100, 128, 4096, 4096
+    x, _, init0 = _problem(N, d, K, "f16", False, seed=3)
+    xh = x[0].contiguous().pin_memory()
+    init = init0[0].cuda()
+    cen1, lab1, cnt1, J1 = km.kmeans_fit_stream(xh, init, 1, chunk=chunk, labels=True)
+    torch.cuda.synchronize()
+    X, Chat, lab_ref, d1, d2 = parity.oracle_assign(workloads.raw_bits(x), "f16", init0.numpy())
+    gl = lab1.cpu().numpy()[None]
+    parity.check_labels(gl, lab_ref, d1, d2, "stream slices")
+    parity.check_objective(J1.cpu().numpy(), d1.sum(-1), "stream slices")
+    ref_c, ref_n, _, _ = oracle.update(X, None, gl, init0.numpy())
+    np.testing.assert_array_equal(cnt1.cpu().numpy()[None], ref_n)
+    parity.check_centroids(cen1.cpu().numpy()[None], ref_c, "stream slices")
+    _, lab_f1, _, J_f1 = km.kmeans_fit(x.cuda(), init0.cuda(), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(lab_f1[0], lab1), "the first assignment is the same computation"
+
+
 def test_stream_fit_no_iterations_and_no_labels(km):
     x, _, init0 = _problem(10000, 32, 16, "f16", False, seed=5)
     xh = x[0].contiguous().pin_memory()
