@@ -59,6 +59,7 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
                                 (size_t)tile_bytes(w.DP, dtype_bytes(xt)));
     w.obj_part = take(Bz * w.nblk_assign * sizeof(double));
     w.split = take(a1d ? 0 : assign_mfma_scratch_bytes(B, N, w.DP, xt, w.Kp));
+    w.seg_short = take(Bz * sizeof(int32_t));
     w.labels = take(Bz * N * sizeof(int32_t));
     w.counts = take(Bz * K * sizeof(int32_t));
     w.sums = take(Bz * K * d * sizeof(float));
@@ -175,12 +176,15 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
     return KM_OK;
 }
 
-// piece_seg (may be NULL): also record the first segment of every reduction piece.
+// piece_seg (may be NULL): also record the first segment of every reduction
+// piece; short_flag (may be NULL): also flag the problems whose clusters are
+// all short enough for the one-segment-per-row-group reduction.
 km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts, int32_t* offsets,
-                   int32_t* perm, int32_t* piece_seg, const Workspace& W, void* ws, hipStream_t s) {
+                   int32_t* perm, int32_t* piece_seg, int32_t* short_flag, const Workspace& W, void* ws,
+                   hipStream_t s) {
     KM_HIP(launch_zero(counts, (size_t)B * K * sizeof(int32_t), s), "zero");
     KM_HIP(launch_sort(labels, B, N, K, counts, offsets, at<int32_t>(ws, W.cursor), perm, segreduce_tw(B, N),
-                       segreduce_pieces(B, N), piece_seg, s),
+                       segreduce_pieces(B, N), piece_seg, short_flag, s),
            "sort");
     return KM_OK;
 }
@@ -202,9 +206,10 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
     int32_t* offsets = at<int32_t>(ws, W.offsets);
     int32_t* perm = at<int32_t>(ws, W.perm);
     int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
-    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, W, ws, s));
+    int32_t* short_flag = at<int32_t>(ws, W.seg_short);
+    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, short_flag, W, ws, s));
     KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr, piece_seg,
-                            at<float>(ws, W.slot), at<float>(ws, W.wslot), s),
+                            at<float>(ws, W.slot), at<float>(ws, W.wslot), short_flag, s),
            "segreduce");
     if (prep_next && !use_assign_1d(d, K))
         KM_HIP(launch_divide_prep(xt, sums, w ? wsum : nullptr, cnt, B, K, (int)d, W.DP, W.Kp, c_old, c_new,
@@ -394,7 +399,7 @@ km_status kmeans_sort_labels(const int32_t* labels, int64_t B, int64_t N, int64_
     int32_t* cnt = counts ? counts : at<int32_t>(workspace, W.counts);
     int32_t* ofs = offsets ? offsets : at<int32_t>(workspace, W.offsets);
     int32_t* pm = perm ? perm : at<int32_t>(workspace, W.perm);
-    return run_sort(labels, B, N, K, cnt, ofs, pm, nullptr, W, workspace, (hipStream_t)stream);
+    return run_sort(labels, B, N, K, cnt, ofs, pm, nullptr, nullptr, W, workspace, (hipStream_t)stream);
 }
 
 km_status kmeans_update(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d,
@@ -562,10 +567,10 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
             // last chunk never has more pieces than the plan holds
             const int TW = segreduce_tw(1, c);
             KM_HIP(launch_sort(lab, 1, nc, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (nc + TW - 1) / TW,
-                               piece_seg, s),
+                               piece_seg, nullptr, s),
                    "sort");
             KM_HIP(launch_segreduce_tw(t, xb, wb, 1, nc, (int)d, perm, offsets, K, sums, wsum, piece_seg,
-                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, true, s),
+                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, true, nullptr, s),
                    "segreduce");
             KM_HIP(launch_add_i32(ctot, cnt, K, s), "add counts");
             KM_HIP(hipEventRecord(R->consumed[buf], s), "event");
@@ -665,10 +670,11 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
         }
         if (objective) KM_HIP(launch_obj_reduce(part, 1, nblk, objective + st, 1, s), "obj_reduce");
         KM_HIP(launch_sort(lab, 1, m, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (m + TW - 1) / TW,
-                           piece_seg, s),
+                           piece_seg, at<int32_t>(ws, W.seg_short), s),
                "sort");
         KM_HIP(launch_segreduce_tw(t, xb, nullptr, 1, m, (int)d, perm, offsets, K, sums, nullptr, piece_seg,
-                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, false, s),
+                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, false,
+                                   at<int32_t>(ws, W.seg_short), s),
                "segreduce");
         const double a = emeans_step_size(alpha0, floor_frac, st, P.steps);
         KM_HIP(launch_emeans_ema(S, Nc, sums, cnt, K, (int)d, a, centroids, last ? F : nullptr, last ? G : nullptr,

@@ -71,6 +71,7 @@ struct Workspace {
     size_t chat;       // [B][Kp/tile_rows] tiles: rows x DP in the point dtype + -|c|^2/2 segment
     size_t obj_part;   // [B][nblk_assign] double: per-block objective partials
     size_t split;      // matrix-core assignment scratch (centroid slices)
+    size_t seg_short;  // [B] int32: the sort's short-segment flags
     size_t labels;     // [B][N] int32: labels of the current assignment (fit)
     size_t counts;     // [B][K] int32
     size_t offsets;    // [B][K+1] int32
@@ -118,23 +119,31 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // dst[i] += src[i], i < n.
 hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 
-// piece_seg may be NULL (then TW and npieces are ignored).
+// Longest segment (points of one cluster) that the short-segment reduction
+// takes, and the largest mean segment length for which it is tried.
+constexpr int kShortSegMax = 64;
+constexpr int64_t kShortSegMean = 16;
+
+// piece_seg may be NULL (then TW and npieces are ignored).  short_flag (may
+// be NULL): per problem, 1 when no cluster has more than kShortSegMax points.
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
                        int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* perm,
-                       int TW, int64_t npieces, int32_t* piece_seg, hipStream_t s);
+                       int TW, int64_t npieces, int32_t* piece_seg, int32_t* short_flag, hipStream_t s);
 
 // Segment sums of the sorted points (sums / wsum must be zero on entry).
+// short_flag (may be NULL): the sort's flags; with them, problems whose
+// clusters are all short are reduced one segment per row group instead.
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K,
                             float* sums, float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
-                            hipStream_t s);
+                            const int32_t* short_flag, hipStream_t s);
 // The same with a given piece width TW (the sort must have used the same).
 // accumulate: add into sums / wsum that hold earlier contributions (else
 // they must be zero on entry, and complete segments are stored).
 hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                                const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                                float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
-                               bool accumulate, hipStream_t s);
+                               bool accumulate, const int32_t* short_flag, hipStream_t s);
 int64_t segreduce_pieces(int64_t B, int64_t N);
 int segreduce_tw(int64_t B, int64_t N);
 

@@ -10,7 +10,9 @@
 //   1. k_count   -- each block histograms a chunk of labels in LDS and adds
 //                   its non-zero bins to counts[b][.] (one global atomic per
 //                   non-empty bin per chunk);
-//   2. k_scan    -- exclusive prefix of counts -> offsets, and scatter cursors;
+//   2. k_scan    -- exclusive prefix of counts -> offsets, and scatter cursors
+//                   (and, if asked, whether every cluster is short enough for
+//                   the one-segment-per-row-group reduction);
 //   3. k_scatter -- each block re-histograms its chunk, reserves one
 //                   contiguous run per non-empty bin with a single global
 //                   atomic on that bin's cursor, then places its indices in
@@ -94,13 +96,16 @@ static int64_t scan_kpad(int64_t K) { return (K + 4095) / 4096 * 4096; }
 
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ counts, int K,
                                                int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
-                                               int TW, int64_t npieces, int32_t* __restrict__ piece_seg) {
+                                               int TW, int64_t npieces, int32_t* __restrict__ piece_seg,
+                                               int32_t* __restrict__ short_flag) {
     extern __shared__ __attribute__((aligned(16))) int32_t s_off[];  // [Kpad + 1]
     __shared__ int32_t s_wave[16];
+    __shared__ int32_t s_wmax[16];
     constexpr int U = 8;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t b = blockIdx.x;
     const int Kpad = (K + 4095) / 4096 * 4096;
+    int32_t vmax = 0;  // the largest count (for the short-segment flag)
     for (int j0 = tid; j0 < Kpad; j0 += 1024 * U) {
         int32_t v[U];
 #pragma unroll
@@ -112,9 +117,23 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
         for (int u = 0; u < U; ++u) {
             const int j = j0 + u * 1024;
             if (j < Kpad) s_off[j] = v[u];
+            vmax = v[u] > vmax ? v[u] : vmax;
         }
     }
+    if (short_flag) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const int32_t t = __shfl_xor(vmax, o, 64);
+            vmax = t > vmax ? t : vmax;
+        }
+        if (lane == 0) s_wmax[wid] = vmax;
+    }
     __syncthreads();
+    if (short_flag && tid == 0) {
+        int32_t m = 0;
+        for (int w = 0; w < 16; ++w) m = s_wmax[w] > m ? s_wmax[w] : m;
+        short_flag[b] = m <= kShortSegMax ? 1 : 0;
+    }
     const int per = Kpad / 1024;  // a multiple of 4
     i32x4* run4 = (i32x4*)(s_off + tid * per);
     int32_t sum = 0;
@@ -231,7 +250,7 @@ static hipError_t set_lds(const void* f, size_t bytes) {
 
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts,
                        int32_t* offsets, int32_t* cursor, int32_t* perm, int TW, int64_t npieces,
-                       int32_t* piece_seg, hipStream_t s) {
+                       int32_t* piece_seg, int32_t* short_flag, hipStream_t s) {
     // counts must be zero on entry (the caller clears it with the other accumulators)
     if (B == 0) return hipSuccess;
     const size_t lds = (size_t)K * sizeof(int32_t);
@@ -251,7 +270,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, i
     const size_t scan_lds = (size_t)(scan_kpad(K) + 1) * sizeof(int32_t);
     if ((e = set_lds((const void*)k_scan, scan_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), scan_lds, s, counts, (int)K, offsets, cursor, TW,
-                       npieces, piece_seg);
+                       npieces, piece_seg, short_flag);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (N > 0 && direct) {
         hipLaunchKernelGGL(k_scatter_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, cursor, perm);

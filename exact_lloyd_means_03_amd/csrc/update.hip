@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                                                    const int32_t* __restrict__ piece_seg, int64_t npieces,
                                                    int K, int TW, float* __restrict__ sums,
                                                    float* __restrict__ wsum, float* __restrict__ slot,
-                                                   float* __restrict__ wslot, bool accumulate) {
+                                                   float* __restrict__ wslot, bool accumulate,
+                                                   const int32_t* __restrict__ skip) {
     constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 8;  // non-vector rows: 64 lanes x 8 = 512 elements
     constexpr int U = 8;  // row steps in flight
     __shared__ int32_t s_idx[4][kSegChunk];
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
     const int64_t piece = (int64_t)blockIdx.x * 4 + wv;
     const int64_t b = blockIdx.y;
     if (piece >= npieces) return;
+    if (skip && skip[b]) return;  // reduced by k_segsum_short
     const int32_t* offb = offsets + b * (K + 1);
     const int32_t total = offb[K];
     const int64_t q0 = piece * (int64_t)TW;
@@ -258,11 +260,12 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
                                                     const int32_t* __restrict__ piece_seg,
                                                     const int32_t* __restrict__ offsets, int64_t npieces, int K,
                                                     int TW, int d, float* __restrict__ sums,
-                                                    float* __restrict__ wsum) {
+                                                    float* __restrict__ wsum, const int32_t* __restrict__ skip) {
     constexpr int U = 8;
     const int lane = threadIdx.x & 63;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t b = blockIdx.y;
+    if (skip && skip[b]) return;  // reduced by k_segsum_short
     const int32_t total = offsets[b * (K + 1) + K];
     const int64_t np = ((int64_t)total + TW - 1) / TW;  // pieces that hold rows
     const int64_t p0 = g * kFoldG;
@@ -320,6 +323,97 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
 
 // Rows per wave piece: enough pieces to fill the chip, and long pieces when
 // there is plenty of work (fewer atomics on the largest clusters).
+// Problems whose clusters are all short (at most kShortSegMax points, as a
+// mini-batch against many centroids has them: 65536 points in 16384 clusters
+// hold 4 on average): one row group of LPR lanes per segment, so a wave
+// reduces 64 / LPR segments side by side instead of walking them one after
+// another, each with its own load latency.  The group loads its segment's
+// point indices and rows kSegShortU at a time, adds the rows in sorted order
+// and stores the sum; an empty cluster gets zeros.  Every cluster's sum is
+// written exactly once, with plain stores, so there are no slots, no fold and
+// no atomics.  The kernel runs only where the sort's flag is set for the
+// problem; k_segreduce and k_fold_slots return at once there.
+constexpr int kSegShortU = 8;
+
+template <typename T, bool VEC, bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_segsum_short(const T* __restrict__ X, const float* __restrict__ w,
+                                                      int64_t N, int d, int lpr_shift,
+                                                      const int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ offsets, int K,
+                                                      const int32_t* __restrict__ short_flag,
+                                                      float* __restrict__ sums, float* __restrict__ wsum) {
+    constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 8;
+    constexpr int U = kSegShortU;
+    const int64_t b = blockIdx.y;
+    if (!short_flag[b]) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int LPR = 1 << lpr_shift, RPW = 64 >> lpr_shift;
+    const int gl = lane >> lpr_shift, li = lane & (LPR - 1);
+    const int64_t j = ((int64_t)blockIdx.x * 4 + wv) * RPW + gl;  // this group's cluster
+    if (j >= K) return;
+    const int nvec = VEC ? d / EPL : 0;
+    const bool active = VEC ? (li < nvec) : true;
+    const T* Xb = X + b * N * (int64_t)d;
+    const float* wb = WEIGHTED ? w + b * N : nullptr;
+    const int32_t* pb = perm + b * N;
+    const int32_t o0 = offsets[b * (K + 1) + j], o1 = offsets[b * (K + 1) + j + 1];
+    float acc[EPL];
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
+    float wacc = 0.f;
+    for (int32_t r0 = o0; r0 < o1; r0 += U) {
+        int32_t idx[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) idx[u] = r0 + u < o1 ? pb[r0 + u] : -1;
+        u32x4 raw[U];
+        float vs[U][VEC ? 1 : EPL];
+        float wi[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = idx[u] >= 0;
+            const T* row = Xb + (int64_t)(ok ? idx[u] : 0) * d;
+            if constexpr (VEC) {
+                raw[u] = (ok && active) ? __builtin_nontemporal_load((const u32x4*)(row + li * EPL))
+                                        : u32x4{0u, 0u, 0u, 0u};
+            } else {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) {
+                    const int k = li + LPR * t;
+                    vs[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
+                }
+            }
+            if constexpr (WEIGHTED) wi[u] = ok ? wb[idx[u]] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (idx[u] < 0) break;
+            float v[EPL];
+            if constexpr (VEC) unpack<T>(raw[u], v);
+            else {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) v[t] = vs[u][t];
+            }
+#pragma unroll
+            for (int t = 0; t < EPL; ++t) {
+                if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[t], acc[t]);
+                else acc[t] += v[t];
+            }
+            if constexpr (WEIGHTED) wacc += wi[u];
+        }
+    }
+    float* sj = sums + (b * K + j) * (int64_t)d;
+    if (active) {
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) {
+            const int k = VEC ? li * EPL + t : li + LPR * t;
+            if (k < d) sj[k] = acc[t];
+        }
+    }
+    if constexpr (WEIGHTED) {
+        if (li == 0) wsum[b * K + j] = wacc;
+    }
+}
+
 int segreduce_tw(int64_t B, int64_t N) {
     int64_t tw = 256;
     while (tw < 4096 && B * N / (tw * 2) >= 8192) tw *= 2;
@@ -331,16 +425,21 @@ int segreduce_tw(int64_t B, int64_t N) {
 // piece_seg: the first segment of every piece, written by the scan of the sort.
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
-                            float* wsum, const int32_t* piece_seg, float* slot, float* wslot, hipStream_t s) {
+                            float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
+                            const int32_t* short_flag, hipStream_t s) {
     return launch_segreduce_tw(xt, x, w, B, N, d, perm, offsets, K, sums, wsum, piece_seg, slot, wslot,
-                               segreduce_tw(B, N), false, s);
+                               segreduce_tw(B, N), false, short_flag, s);
 }
 
 hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                                const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                                float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
-                               bool accumulate, hipStream_t s) {
+                               bool accumulate, const int32_t* short_flag, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
+    // short segments on average: try the one-segment-per-row-group kernel
+    // (it runs where the sort found every cluster short; the piece kernels
+    // run elsewhere)
+    const int32_t* skip = (short_flag && !accumulate && N <= kShortSegMean * K) ? short_flag : nullptr;
     const int64_t npieces = (N + TW - 1) / TW;
     const int esz = dtype_bytes(xt);
     const int epl = 16 / esz;
@@ -348,10 +447,32 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
     int lanes = vec ? d / epl : (d < 64 ? d : 64);
     int shift = 0;
     while ((1 << shift) < lanes) ++shift;
+    if (skip) {
+        const int64_t per_block = 4 * (64 >> shift);  // clusters per block: one per row group
+        dim3 sgrid((unsigned)((K + per_block - 1) / per_block), (unsigned)B);
+#define KM_SHORT(T, V, W)                                                                                   \
+    hipLaunchKernelGGL((k_segsum_short<T, V, W>), sgrid, dim3(256), 0, s, (const T*)x, w, N, d, shift, perm, \
+                       offsets, (int)K, short_flag, sums, wsum)
+#define KM_SHORT_T(T)                     \
+    if (vec) {                            \
+        if (w) KM_SHORT(T, true, true);   \
+        else KM_SHORT(T, true, false);    \
+    } else {                              \
+        if (w) KM_SHORT(T, false, true);  \
+        else KM_SHORT(T, false, false);   \
+    }
+        if (xt == DType::F32) { KM_SHORT_T(float) }
+        else if (xt == DType::F16) { KM_SHORT_T(_Float16) }
+        else { KM_SHORT_T(bf16_t) }
+#undef KM_SHORT_T
+#undef KM_SHORT
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     dim3 grid((unsigned)((npieces + 3) / 4), (unsigned)B);
 #define KM_SEG(T, V, W)                                                                                   \
     hipLaunchKernelGGL((k_segreduce<T, V, W>), grid, dim3(256), 0, s, (const T*)x, w, N, d, shift, perm, \
-                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot, accumulate)
+                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot, accumulate, skip)
 #define KM_SEG_T(T)                      \
     if (vec) {                           \
         if (w) KM_SEG(T, true, true);    \
@@ -370,10 +491,10 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
     dim3 fgrid((unsigned)((npieces + 4 * kFoldG - 1) / (4 * kFoldG)), (unsigned)B);
     if (w)
         hipLaunchKernelGGL(k_fold_slots<true>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
-                           (int)K, TW, d, sums, wsum);
+                           (int)K, TW, d, sums, wsum, skip);
     else
         hipLaunchKernelGGL(k_fold_slots<false>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
-                           (int)K, TW, d, sums, wsum);
+                           (int)K, TW, d, sums, wsum, skip);
     return hipGetLastError();
 }
 

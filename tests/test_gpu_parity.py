@@ -185,6 +185,37 @@ def test_update_parity(km, dtype, B, N, d, K, weighted):
     np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
 
 
+@pytest.mark.parametrize("dtype,d,weighted", [("bf16", 96, False), ("f16", 128, True), ("f32", 33, True),
+                                              ("f16", 512, False), ("bf16", 7, False)])
+@pytest.mark.parametrize("big", [0, 64, 65, 300])
+def test_update_short_segments(km, dtype, d, weighted, big):
+    """Few points per cluster (N = 4K on average): problems whose clusters all
+    hold at most 64 points are reduced one segment per row group; a cluster
+    of 65 or more points sends the problem to the piece kernels.  Two
+    problems in one call, the second always short, so the per-problem choice
+    is exercised both ways; one cluster of each problem is empty."""
+    B, K = 2, 1000
+    N = 4 * K
+    x, C = _rand_problem(B, N, d, K, dtype, seed=d + big)
+    rng = np.random.default_rng(d + big + 1)
+    lab = rng.integers(1, K, size=(B, N)).astype(np.int32)  # cluster 0 empty ...
+    if big:
+        lab[0, :big] = 5  # ... except in the first problem, where cluster 5 gets at least `big` points
+        lab[0, big:][lab[0, big:] == 5] = 6
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, (B, N)).astype(np.float32)) if weighted else None
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(lab).cuda(), C.cuda(),
+                                     weights=None if w is None else w.cuda())
+    X = oracle.decode(workloads.raw_bits(x), dtype)
+    ref_c, ref_n, _, _ = oracle.update(X, None if w is None else w.numpy(), lab, C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    if big:
+        assert ref_n[0, 5] == big
+    parity.check_centroids(c_new.cpu().numpy(), ref_c, f"short segments {dtype} d{d} w{weighted} big{big}")
+    empty = ref_n == 0
+    assert empty[:, 0].all()
+    np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
+
+
 @pytest.mark.parametrize("dtype,d,weighted", [("bf16", 128, False), ("f16", 64, True), ("f32", 1, True)])
 def test_update_parity_zipf_sizes(km, dtype, d, weighted):
     """Cluster sizes with a power-law tail: the largest segments span hundreds
