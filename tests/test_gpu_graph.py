@@ -109,3 +109,37 @@ def test_emeans_in_a_graph(km):
     with torch.cuda.graph(g):
         km.kmeans_emeans(*args, uniforms=u, centroids=cen, labels=lab, counts=cnt, objective=obj, ws=ws)
     _replays(g, (cen, lab, cnt, obj), eager, "kmeans_emeans")
+
+
+def test_emeans_sliced_and_short_paths_in_a_graph(km):
+    """Batches of 2048 points against 4096 centroids: the assignment cuts the
+    centroid tiles into slices and merges them, and the reduction takes the
+    one-segment-per-row-group path chosen on the device by the sort's flag;
+    both run inside the captured graph."""
+    N, d, K, batch, epochs = 8192, 32, 4096, 2048, 2
+    wl = workloads.small("gmm-n1m-k8192-d128-f16", N=N, d=d, K=K, n_iter=1, seed=23, ncomp=K // 4)
+    p = workloads.generate(wl)
+    x, init = p.x[0].cuda(), p.init[0].cuda()
+    T = km.emeans_steps(N, batch, epochs)
+    u = torch.from_numpy(workloads.emeans_uniforms(23, T, K)).cuda()
+    L = km.load()
+    ws = torch.empty(int(L.kmeans_emeans_workspace_bytes(N, d, K, 1, batch)), dtype=torch.uint8, device="cuda")
+    args = (x, init, batch, epochs, 0.5, 0.1, 0.2, 1e-2)
+    c0, l0, n0, j0 = km.kmeans_emeans(*args, uniforms=u, labels=True, ws=ws)
+    eager = (c0.clone(), l0.clone(), n0.clone(), j0.clone())
+    torch.cuda.synchronize()
+
+    cen = torch.empty_like(init)
+    lab = torch.empty((N,), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((K,), dtype=torch.int32, device="cuda")
+    obj = torch.empty((T,), dtype=torch.float64, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        km.kmeans_emeans(*args, uniforms=u, centroids=cen, labels=lab, counts=cnt, objective=obj, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        km.kmeans_emeans(*args, uniforms=u, centroids=cen, labels=lab, counts=cnt, objective=obj, ws=ws)
+    _replays(g, (cen, lab, cnt, obj), eager, "kmeans_emeans sliced + short")
