@@ -13,10 +13,12 @@
  *     "FlashAssign: Materialization-Free Assignment").  Scalar points (d = 1)
  *     take a binary search over the sorted centroids instead.
  *   - update: the label vector is argsorted by cluster id so that each cluster
- *     is a contiguous segment, every segment is reduced on chip, and the
- *     reduced pieces are combined with a few atomic adds per coordinate
- *     instead of one per point; the point matrix is never permuted in memory (technologypulse.uk article, "bottleneck 2";
- *     wispaper.ai blog, "Sort-Inverse Update").  The new centroid is the mean
+ *     is a contiguous segment, and every segment is reduced on chip and
+ *     stored once; only the pieces of a cluster that spans several reduction
+ *     pieces are combined with a few atomic adds per coordinate, instead of
+ *     one per point.  The point matrix is never permuted in memory
+ *     (technologypulse.uk article, "bottleneck 2"; wispaper.ai blog,
+ *     "Sort-Inverse Update").  The new centroid is the mean
  *     of its points (daily.steinslab.io "e-means" article, "Breaking 70 Years
  *     of Full-Batch Inertia": centroid = S_j / N_j); a cluster with no points
  *     keeps its previous centroid.
