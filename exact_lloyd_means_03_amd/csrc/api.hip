@@ -668,7 +668,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
                                       at<void>(ws, P.split), s),
                    "assign_mfma");
         }
-        if (objective) KM_HIP(launch_obj_reduce(part, 1, nblk, objective + st, 1, s), "obj_reduce");
+        // the batch's objective partials are summed by the moving-average kernel below
         KM_HIP(launch_sort(lab, 1, m, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (m + TW - 1) / TW,
                            piece_seg, at<int32_t>(ws, W.seg_short), s),
                "sort");
@@ -678,7 +678,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
                "segreduce");
         const double a = emeans_step_size(alpha0, floor_frac, st, P.steps);
         KM_HIP(launch_emeans_ema(S, Nc, sums, cnt, K, (int)d, a, centroids, last ? F : nullptr, last ? G : nullptr,
-                                 s),
+                                 part, nblk, objective ? objective + st : nullptr, s),
                "ema");
         if (dead_frac > 0.0)
             KM_HIP(launch_emeans_split(S, Nc, centroids, K, (int)d, dead_below, eps, uniforms + st * K,

@@ -181,9 +181,11 @@ hipError_t launch_optimal_1d(DType xt, const void* x, const float* w, int64_t B,
 
 // e-means state updates (float64 sums S [K][d] and counts N [K]).
 constexpr int64_t kEmeansMaxK = 32768;  // the split keeps one int per cluster in LDS
-// Clears s and n after reading them.
+// Clears s and n after reading them.  obj_out (may be NULL): also the sum
+// of the nobj objective partials obj_part.
 hipError_t launch_emeans_ema(double* S, double* Nc, float* s, int32_t* n, int64_t K, int d, double a, float* C,
-                             double* F, double* G, hipStream_t st);
+                             double* F, double* G, const double* obj_part, int64_t nobj, double* obj_out,
+                             hipStream_t st);
 bool emeans_split_supports(int64_t K);
 hipError_t launch_emeans_split(double* S, double* Nc, float* C, int64_t K, int d, double dead_below, double eps,
                                const float* u, int32_t* list_j, int32_t* list_k, hipStream_t st);

@@ -14,13 +14,24 @@ namespace km {
 // F and G (the last epoch) the batch's sums and counts are also added to the
 // last-epoch totals.  One wave per cluster, lanes over coordinates.  The
 // batch's sums and count are cleared once read, ready for the next batch.
+// With obj_out, the wave of cluster 0 also sums the batch assignment's
+// nobj objective partials into *obj_out (lane-strided sums, then a fixed
+// shuffle tree), which saves a launch per step.
 __global__ __launch_bounds__(256) void k_ema(double* __restrict__ S, double* __restrict__ Nc,
                                              float* __restrict__ s, int32_t* __restrict__ n, int64_t K, int d,
                                              double a, float* __restrict__ C, double* __restrict__ F,
-                                             double* __restrict__ G) {
+                                             double* __restrict__ G, const double* __restrict__ obj_part,
+                                             int64_t nobj, double* __restrict__ obj_out) {
     const int lane = threadIdx.x & 63;
     const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (j >= K) return;
+    if (j == 0 && obj_out) {
+        double acc = 0.0;
+        for (int64_t i = lane; i < nobj; i += 64) acc += obj_part[i];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (lane == 0) *obj_out = acc;
+    }
     const int32_t nj = n[j];
     const double Nn = (1.0 - a) * Nc[j] + a * (double)nj;
     for (int c = lane; c < d; c += 64) {
@@ -40,9 +51,11 @@ __global__ __launch_bounds__(256) void k_ema(double* __restrict__ S, double* __r
 }
 
 hipError_t launch_emeans_ema(double* S, double* Nc, float* s, int32_t* n, int64_t K, int d, double a, float* C,
-                             double* F, double* G, hipStream_t st) {
+                             double* F, double* G, const double* obj_part, int64_t nobj, double* obj_out,
+                             hipStream_t st) {
     if (K == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_ema, dim3((unsigned)((K + 3) / 4)), dim3(256), 0, st, S, Nc, s, n, K, d, a, C, F, G);
+    hipLaunchKernelGGL(k_ema, dim3((unsigned)((K + 3) / 4)), dim3(256), 0, st, S, Nc, s, n, K, d, a, C, F, G,
+                       obj_part, nobj, obj_out);
     return hipGetLastError();
 }
 
