@@ -656,6 +656,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
         const void* xb = (const char*)x + i0 * d * es;
         int32_t* lab = (last && labels) ? labels + i0 : at<int32_t>(ws, W.labels);
         int64_t nblk;
+        bool counted = false;
         if (use_assign_1d(d, K)) {
             nblk = assign_1d_blocks(m);
             KM_HIP(launch_assign_1d(t, xb, 1, m, centroids, K, nullptr, lab, nullptr, part, nblk, nblk, s),
@@ -664,13 +665,16 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
             nblk = assign_mfma_blocks(1, m, W.DP, t, W.Kp);
             void* blob = at<void>(ws, W.chat);
             KM_HIP(launch_prep(t, centroids, 1, K, (int)d, W.DP, W.Kp, blob, s), "prep");
+            // a sliced launch's merge also counts the labels (cnt is zero here:
+            // cleared before the first step and by the moving average after each)
+            counted = assign_mfma_merges(1, m, W.DP, t, W.Kp);
             KM_HIP(launch_assign_mfma(t, xb, 1, m, (int)d, W.DP, blob, W.Kp, nullptr, lab, nullptr, part, nblk,
-                                      at<void>(ws, P.split), s),
+                                      at<void>(ws, P.split), s, counted ? cnt : nullptr, K),
                    "assign_mfma");
         }
         // the batch's objective partials are summed by the moving-average kernel below
         KM_HIP(launch_sort(lab, 1, m, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (m + TW - 1) / TW,
-                           piece_seg, at<int32_t>(ws, W.seg_short), s),
+                           piece_seg, at<int32_t>(ws, W.seg_short), s, counted),
                "sort");
         KM_HIP(launch_segreduce_tw(t, xb, nullptr, 1, m, (int)d, perm, offsets, K, sums, nullptr, piece_seg,
                                    at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, false,

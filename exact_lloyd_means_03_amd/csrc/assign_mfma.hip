@@ -591,6 +591,10 @@ int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt, int64_t Kp) {
     return groups_per_problem(shape_of(B, N, DP, xt, Kp), N);
 }
 
+bool assign_mfma_merges(int64_t B, int64_t N, int DP, DType xt, int64_t Kp) {
+    return shape_of(B, N, DP, xt, Kp).nslice > 1;
+}
+
 size_t assign_mfma_scratch_bytes(int64_t B, int64_t N, int DP, DType xt, int64_t Kp) {
     const GroupShape g = shape_of(B, N, DP, xt, Kp);
     if (g.nslice < 2) return 0;
@@ -600,12 +604,14 @@ size_t assign_mfma_scratch_bytes(int64_t B, int64_t N, int DP, DType xt, int64_t
 // One block per point group: the best (largest x.c - |c|^2/2) over the
 // slices, the earlier slice on equal values (its centroid indices are the
 // smaller ones, and within a slice the unit already kept the smallest index),
-// then the outputs as the one-slice kernel writes them.
+// then the outputs as the one-slice kernel writes them.  counts (may be
+// NULL, [B][K], zero on entry): also count the labels, one atomic each.
 __global__ __launch_bounds__(256) void k_assign_merge(const float* __restrict__ sv, const int32_t* __restrict__ si,
                                                       const float* __restrict__ sxx, int64_t nslice, int64_t BN,
                                                       int64_t N, int pts, int64_t gpb, const float* __restrict__ w,
                                                       int32_t* __restrict__ labels, float* __restrict__ min_dist,
-                                                      double* __restrict__ obj_part) {
+                                                      double* __restrict__ obj_part, int32_t* __restrict__ counts,
+                                                      int64_t K) {
     __shared__ double s_obj[4];
     const int64_t grp = blockIdx.x, b = grp / gpb, pg = grp - b * gpb;
     double obj = 0.0;
@@ -624,6 +630,7 @@ __global__ __launch_bounds__(256) void k_assign_merge(const float* __restrict__ 
         }
         const float dist = fmaxf(sxx[i] - 2.f * bv, 0.f);
         labels[i] = bi;
+        if (counts && (uint64_t)bi < (uint64_t)K) atomicAdd(&counts[b * K + bi], 1);
         if (min_dist) min_dist[i] = dist;
         obj += (double)(w ? w[i] : 1.f) * (double)dist;
     }
@@ -665,7 +672,8 @@ static int64_t resident_blocks() {
 template <typename T, int DP, int NCBT, int WV>
 static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const void* blob, int64_t ntiles,
                            const GroupShape& gs, const float* w, int32_t* labels, float* min_dist,
-                           double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
+                           double* obj_part, int64_t nblk, void* scratch, int32_t* counts, int64_t K,
+                           hipStream_t s) {
     const int64_t bgroups = B * nblk, ngroups = bgroups * gs.nslice;
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
     const int64_t P = vec ? resident_blocks<T, DP, true, NCBT, WV>() : resident_blocks<T, DP, false, NCBT, WV>();
@@ -688,7 +696,7 @@ static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const voi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_assign_merge, dim3((unsigned)bgroups), dim3(256), 0, s, sv, si, sxx, gs.nslice, BN, N,
-                       WV * NCBT * 32, nblk, w, labels, min_dist, obj_part);
+                       WV * NCBT * 32, nblk, w, labels, min_dist, obj_part, counts, K);
     return hipGetLastError();
 }
 
@@ -698,7 +706,8 @@ static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const voi
 template <typename T, int DP>
 static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
-                           double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
+                           double* obj_part, int64_t nblk, void* scratch, int32_t* counts, int64_t K,
+                           hipStream_t s) {
     const GroupShape g = group_shape<T>(B, N, DP, ntiles);
     if (nblk != groups_per_problem(g, N)) return hipErrorInvalidValue;
     if (g.nslice > 1 && scratch == nullptr) return hipErrorInvalidValue;
@@ -706,47 +715,50 @@ static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const voi
     if constexpr (DEF == 2) {
         if (g.ncb == 1)
             return launch_n<T, DP, 1, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk,
-                                          scratch, s);
+                                          scratch, counts, K, s);
     }
-    return launch_n<T, DP, DEF, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk, scratch, s);
+    return launch_n<T, DP, DEF, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk, scratch,
+                                    counts, K, s);
 }
 
 template <typename T>
 static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, const void* blob,
                             int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
-                            double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
+                            double* obj_part, int64_t nblk, void* scratch, int32_t* counts, int64_t K,
+                            hipStream_t s) {
+#define KM_LT(DPV) \
+    launch_t<T, DPV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, counts, K, s)
     switch (DP) {
-        case 16: return launch_t<T, 16>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
-        case 32: return launch_t<T, 32>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
-        case 64: return launch_t<T, 64>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+        case 16: return KM_LT(16);
+        case 32: return KM_LT(32);
+        case 64: return KM_LT(64);
         case 96:
-            if constexpr (sizeof(T) == 2)
-                return launch_t<T, 96>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
-            else
-                return hipErrorInvalidValue;
-        case 128:
-            return launch_t<T, 128>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
-        case 256:
-            return launch_t<T, 256>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+            if constexpr (sizeof(T) == 2) return KM_LT(96);
+            else return hipErrorInvalidValue;
+        case 128: return KM_LT(128);
+        case 256: return KM_LT(256);
         case 512:
-            if constexpr (sizeof(T) == 2)
-                return launch_t<T, 512>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
-            else
-                return hipErrorInvalidValue;
+            if constexpr (sizeof(T) == 2) return KM_LT(512);
+            else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
+#undef KM_LT
 }
 
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
-                              float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s) {
+                              float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s,
+                              int32_t* counts, int64_t K) {
     if (B == 0 || N == 0) return hipSuccess;
     const int64_t ntiles = Kp / tile_rows(DP, dtype_bytes(xt));
     if (xt == DType::F32)
-        return launch_dp<float>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+        return launch_dp<float>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch,
+                                counts, K, s);
     if (xt == DType::F16)
-        return launch_dp<_Float16>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
-    return launch_dp<bf16_t>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, s);
+        return launch_dp<_Float16>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch,
+                                   counts, K, s);
+    return launch_dp<bf16_t>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, counts,
+                             K, s);
 }
 
 }  // namespace km

@@ -97,11 +97,15 @@ hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, in
 
 // Matrix-core assignment.  nblk = assign_mfma_blocks(...) point groups per
 // problem (one objective partial each); scratch: assign_mfma_scratch_bytes(...)
-// bytes (zero unless the launch cuts the centroids into slices).
+// bytes (zero unless the launch cuts the centroids into slices).  counts
+// (may be NULL, [B][K], zero on entry): where assign_mfma_merges(...), the
+// merge also counts the labels; elsewhere it is ignored.
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
-                              float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s);
+                              float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s,
+                              int32_t* counts = nullptr, int64_t K = 0);
 int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
+bool assign_mfma_merges(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
 size_t assign_mfma_scratch_bytes(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
 
 // obj_part (may be NULL): the objective partial of block j of row b goes to
@@ -126,9 +130,11 @@ constexpr int64_t kShortSegMean = 16;
 
 // piece_seg may be NULL (then TW and npieces are ignored).  short_flag (may
 // be NULL): per problem, 1 when no cluster has more than kShortSegMax points.
+// counted: counts already hold the labels' histogram (the count pass is skipped).
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
                        int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* perm,
-                       int TW, int64_t npieces, int32_t* piece_seg, int32_t* short_flag, hipStream_t s);
+                       int TW, int64_t npieces, int32_t* piece_seg, int32_t* short_flag, hipStream_t s,
+                       bool counted = false);
 
 // Segment sums of the sorted points (sums / wsum must be zero on entry).
 // short_flag (may be NULL): the sort's flags; with them, problems whose

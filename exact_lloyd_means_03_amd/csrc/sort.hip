@@ -250,17 +250,17 @@ static hipError_t set_lds(const void* f, size_t bytes) {
 
 hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts,
                        int32_t* offsets, int32_t* cursor, int32_t* perm, int TW, int64_t npieces,
-                       int32_t* piece_seg, int32_t* short_flag, hipStream_t s) {
+                       int32_t* piece_seg, int32_t* short_flag, hipStream_t s, bool counted) {
     // counts must be zero on entry (the caller clears it with the other accumulators)
     if (B == 0) return hipSuccess;
     const size_t lds = (size_t)K * sizeof(int32_t);
     hipError_t e;
     const bool direct = sort_direct(N, K);
     const dim3 dgrid((unsigned)((N + kDirectThreads - 1) / kDirectThreads), (unsigned)B);
-    if (N > 0 && direct) {
+    if (N > 0 && direct && !counted) {
         hipLaunchKernelGGL(k_count_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else if (N > 0) {
+    } else if (N > 0 && !counted) {
         if ((e = set_lds((const void*)k_count, lds)) != hipSuccess) return e;
         const int64_t CH = sort_chunk(B, N, K);
         dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
