@@ -5,7 +5,6 @@ package.  The k-means library never imports it, and it imports nothing from
 the library.
 """
 from .oracle import (  # noqa: F401
-    DTYPES, assign, decode, emeans, fit, lib, load_library, near_tie, num_threads, objective, optimal_1d, round_to,
-    update,
-    using_library,
+    DTYPES, assign, decode, emeans, fit, lib, load_library, near_tie, num_threads, objective, objective_bits,
+    optimal_1d, round_to, update, update_bits, using_library,
 )

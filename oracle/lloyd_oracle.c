@@ -256,6 +256,98 @@ void oracle_objective(const double *X, const double *w, const int32_t *labels,
 }
 
 /* ----------------------------------------------------------------------- *
+ * The update stage and the objective of given labels, read straight from
+ * the stored bits of the points (each element decoded exactly to fp64 where
+ * it is used), for point sets too large to hold decoded in fp64.  The
+ * arithmetic is that of oracle_update and oracle_objective, term for term
+ * and in the same order, so the results are identical:
+ *   - update: for every (b, k) the sum S_jk = sum_i w_i x_ik runs over i
+ *     ascending, as in oracle_update; the work is divided over coordinates
+ *     (one (b, k) pair per task), which does not change any sum.  W_j and
+ *     the counts are accumulated by the task of coordinate 0.
+ *   - objective: the per-point terms w_i * sum_k (x_ik - c_{l_i,k})^2 are
+ *     computed in parallel into a buffer, then added in point order.
+ * x: float32 bits, or uint16 bits of fp16 / bf16.  w [B,N] fp32 or NULL.
+ * Returns 0, or -1 when memory runs out (objective) or a label is out of
+ * range (update).
+ * ----------------------------------------------------------------------- */
+static double orc_elem(const void *x, int dtype, int64_t idx)
+{
+    if (dtype == ORC_F32) return (double)((const float *)x)[idx];
+    return oracle_decode_one(((const uint16_t *)x)[idx], dtype);
+}
+
+int oracle_update_bits(const void *x, int dtype, const float *w, const int32_t *labels,
+                       int64_t B, int64_t N, int64_t d, int64_t K,
+                       const float *c_old, float *c_new, int32_t *counts,
+                       double *S_out, double *W_out)
+{
+    for (int64_t i = 0; i < B * N; ++i)
+        if (labels[i] < 0 || labels[i] >= K) return -1;
+    double *S = (double *)calloc((size_t)(B * K * d), sizeof(double));
+    double *W = (double *)calloc((size_t)(B * K), sizeof(double));
+    int64_t *Nj = (int64_t *)calloc((size_t)(B * K), sizeof(int64_t));
+    if (!S || !W || !Nj) {
+        free(S); free(W); free(Nj);
+        return -1;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bk = 0; bk < B * d; ++bk) {
+        const int64_t b = bk / d, k = bk % d;
+        for (int64_t i = 0; i < N; ++i) {
+            const int64_t j = labels[b * N + i];
+            const double wi = w ? (double)w[b * N + i] : 1.0;
+            if (k == 0) {
+                Nj[b * K + j] += 1;
+                W[b * K + j] += wi;
+            }
+            S[(b * K + j) * d + k] += wi * orc_elem(x, dtype, (b * N + i) * d + k);
+        }
+    }
+    for (int64_t bj = 0; bj < B * K; ++bj) {
+        for (int64_t k = 0; k < d; ++k)
+            c_new[bj * d + k] = Nj[bj] > 0 ? (float)(S[bj * d + k] / W[bj]) : c_old[bj * d + k];
+        counts[bj] = (int32_t)Nj[bj];
+        if (W_out) W_out[bj] = W[bj];
+        if (S_out)
+            for (int64_t k = 0; k < d; ++k) S_out[bj * d + k] = S[bj * d + k];
+    }
+    free(S);
+    free(W);
+    free(Nj);
+    return 0;
+}
+
+int oracle_objective_bits(const void *x, int dtype, const float *w, const int32_t *labels,
+                          int64_t B, int64_t N, int64_t d, const double *C, int64_t K, double *J)
+{
+    double *term = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    if (!term) return -1;
+    for (int64_t b = 0; b < B; ++b) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < N; ++i) {
+            const int64_t j = labels[b * N + i];
+            if (j < 0 || j >= K) {
+                term[i] = 0.0;
+                continue;
+            }
+            const double *c = C + (b * K + j) * d;
+            double D = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                const double t = orc_elem(x, dtype, (b * N + i) * d + k) - c[k];
+                D += t * t;
+            }
+            term[i] = (w ? (double)w[b * N + i] : 1.0) * D;
+        }
+        double s = 0.0;
+        for (int64_t i = 0; i < N; ++i) s += term[i];
+        J[b] = s;
+    }
+    free(term);
+    return 0;
+}
+
+/* ----------------------------------------------------------------------- *
  * n_iter Lloyd iterations from init [B,K,d] fp32.  x holds the stored bits
  * (float32, or uint16 for fp16/bf16).  w [B,N] fp32 or NULL.
  * Outputs: C_out [B,K,d] (centroids after the last update), labels_out and

@@ -38,6 +38,10 @@ def load_library(path: str):
     L.oracle_assign.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     L.oracle_update.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, p, p]
     L.oracle_objective.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+    L.oracle_update_bits.argtypes = [p, C.c_int, p, p, i64, i64, i64, i64, p, p, p, p, p]
+    L.oracle_update_bits.restype = C.c_int
+    L.oracle_objective_bits.argtypes = [p, C.c_int, p, p, i64, i64, i64, p, i64, p]
+    L.oracle_objective_bits.restype = C.c_int
     L.oracle_fit.argtypes = [p, C.c_int, p, i64, i64, i64, i64, p, C.c_int32,
                              p, p, p, p, p, p]
     L.oracle_fit.restype = C.c_int
@@ -54,9 +58,10 @@ def lib():
     """The loaded oracle library; compiled first if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("KM_ORACLE_LIBRARY") or _build.LIB
+        if not os.path.exists(path):
             _build.build()
-        _lib = load_library(_build.LIB)
+        _lib = load_library(path)
     return _lib
 
 
@@ -147,6 +152,54 @@ def objective(X: np.ndarray, w, labels: np.ndarray, Chat: np.ndarray) -> np.ndar
     wd = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
     J = np.empty(B, np.float64)
     lib().oracle_objective(_ptr(X), _ptr(wd), _ptr(labels), B, N, d, _ptr(Chat), K, _ptr(J))
+    return J
+
+
+def _bits(x_bits: np.ndarray, dtype: str) -> np.ndarray:
+    want = np.float32 if dtype == "f32" else np.uint16
+    if x_bits.dtype != want:
+        raise TypeError(f"stored bits of {dtype} must be {np.dtype(want).name}")
+    return np.ascontiguousarray(x_bits)
+
+
+def update_bits(x_bits: np.ndarray, dtype: str, w, labels: np.ndarray, c_old: np.ndarray):
+    """The update stage of `update`, reading the points as stored bits
+    x_bits [B,N,d] (float32, or uint16 for fp16 / bf16) instead of decoded
+    fp64 (same arithmetic, same order, same results).  w [B,N] float32 or
+    None.  Returns (c_new fp32, counts int32 [B,K], S fp64, W fp64)."""
+    x_bits = _bits(x_bits, dtype)
+    B, N, d = x_bits.shape
+    c_old = np.ascontiguousarray(c_old, dtype=np.float32)
+    K = c_old.shape[1]
+    assert c_old.shape == (B, K, d)
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    assert labels.shape == (B, N)
+    w32 = None if w is None else np.ascontiguousarray(w, dtype=np.float32)
+    c_new = np.empty_like(c_old)
+    counts = np.empty((B, K), np.int32)
+    S = np.empty((B, K, d), np.float64)
+    W = np.empty((B, K), np.float64)
+    rc = lib().oracle_update_bits(_ptr(x_bits), DTYPES[dtype], _ptr(w32), _ptr(labels), B, N, d, K, _ptr(c_old),
+                                  _ptr(c_new), _ptr(counts), _ptr(S), _ptr(W))
+    if rc != 0:
+        raise ValueError("oracle_update_bits: label out of range, or out of host memory")
+    return c_new, counts, S, W
+
+
+def objective_bits(x_bits: np.ndarray, dtype: str, w, labels: np.ndarray, Chat: np.ndarray) -> np.ndarray:
+    """`objective` of given labels, reading the points as stored bits
+    (same terms, added in the same order)."""
+    x_bits = _bits(x_bits, dtype)
+    B, N, d = x_bits.shape
+    Chat = np.ascontiguousarray(Chat, dtype=np.float64)
+    K = Chat.shape[1]
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    w32 = None if w is None else np.ascontiguousarray(w, dtype=np.float32)
+    J = np.empty(B, np.float64)
+    rc = lib().oracle_objective_bits(_ptr(x_bits), DTYPES[dtype], _ptr(w32), _ptr(labels), B, N, d, _ptr(Chat), K,
+                                     _ptr(J))
+    if rc != 0:
+        raise MemoryError("oracle_objective_bits ran out of host memory")
     return J
 
 

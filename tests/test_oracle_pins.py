@@ -151,6 +151,32 @@ def test_update_matches_bincount(orc):
             np.testing.assert_array_equal(c_new[b, K - 2:], c_old[b, K - 2:])
 
 
+def test_update_and_objective_from_bits_equal_the_decoded_forms(orc):
+    """The bit-reading update and objective (for point sets too large to
+    decode to fp64) give exactly the results of the decoded forms, which the
+    closed forms above pin."""
+    rng = np.random.default_rng(21)
+    B, N, d, K = 3, 700, 9, 13
+    for dt in ("f32", "f16", "bf16"):
+        x32 = rng.standard_normal((B, N, d)).astype(np.float32)
+        bits = orc.round_to(x32, dt)
+        X = orc.decode(bits, dt)
+        w = rng.uniform(0.1, 1.0, size=(B, N)).astype(np.float32)
+        labels = rng.integers(0, K - 1, size=(B, N)).astype(np.int32)  # cluster K-1 empty
+        c_old = rng.standard_normal((B, K, d)).astype(np.float32)
+        Chat = orc.decode(orc.round_to(c_old, dt), dt)
+        for weights in (None, w):
+            want = orc.update(X, None if weights is None else weights.astype(np.float64), labels, c_old)
+            got = orc.update_bits(bits, dt, weights, labels, c_old)
+            for a, b_ in zip(got, want):
+                np.testing.assert_array_equal(a, b_)
+            Jw = orc.objective(X, None if weights is None else weights.astype(np.float64), labels, Chat)
+            Jb = orc.objective_bits(bits, dt, weights, labels, Chat)
+            np.testing.assert_array_equal(Jb, Jw)
+    with pytest.raises(ValueError):
+        orc.update_bits(bits, "bf16", None, np.full((B, N), K, np.int32), c_old)
+
+
 # ------------------------------------------------------- whole iterations
 
 def _fit_f32(orc, X32, K_init, n_iter, w=None):
