@@ -68,6 +68,18 @@ def _traffic(wl):
     return t.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (the "model name" line that lscpu also shows)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(p, target_s: float):
     """Time the CPU oracle on a bounded sample and extrapolate to one Lloyd
     iteration over the whole workload: with one batch, n points against all
@@ -121,10 +133,48 @@ def cpu_baseline(p, target_s: float):
         "value": 1.0 / per_iter,
         "unit": "iter/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{what}: one oracle assignment against all K={wl.K} centroids plus the update, "
                    f"{t:.2f} s, extrapolated linearly to one iteration over all {wl.B * wl.N} points"),
     }
+
+
+def bench_update(km, wl, reps: int = 5) -> dict:
+    """The update stage (kmeans_update: argsort, segmented reduction, divide)
+    on a workload's points with the labels of its first assignment: device
+    time per call from HIP events around each of `reps` calls, against the
+    update's algorithmic bytes and the HBM peak."""
+    import torch
+
+    import workloads
+
+    p = workloads.generate(wl)
+    dev = torch.device("cuda", 0)
+    x = p.x.to(dev)
+    C = p.init.to(dev)
+    B, N, d, K = wl.B, wl.N, wl.d, wl.K
+    ws = km.workspace(B, N, d, K, x.dtype, dev)
+    labels, _, _ = km.kmeans_assign(x, C, ws=ws)
+    c_new = torch.empty_like(C)
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    km.kmeans_update(x, labels, C, c_new=c_new, counts=counts, ws=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(reps):
+        km.kmeans_update(x, labels, C, c_new=c_new, counts=counts, ws=ws)
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    ms = sum(ev[r].elapsed_time(ev[r + 1]) for r in range(reps)) / reps
+    ub = update_bytes(wl)
+    out = {"workload": wl.name, "avg_ms": ms, "calls": reps, "algorithmic_bytes": ub,
+           "GB/s": ub / (ms * 1e-3) / 1e9, "frac_hbm": ub / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "largest_cluster": int(counts.max()),
+           "timing": "HIP events around each kmeans_update call (argsort, segmented reduction, divide)"}
+    del x, C, ws, labels, c_new, counts
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_fit_1d(args, km, wl, p, x, w, C):
@@ -373,6 +423,7 @@ def cpu_baseline_emeans(p, target_s: float):
         "value": 1.0 / per_epoch,
         "unit": "epochs/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"the first {n} of {wl.N} points as one e-means step against all K={wl.K} centroids "
                    f"(assignment, moving average, splits), {t:.2f} s, extrapolated linearly to one epoch"),
@@ -514,6 +565,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--chunk", type=int, default=1 << 22, help="points per host-to-device copy (host workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-zipf-update", action="store_true",
+                    help="skip the 33M-point update measurement that the headline line carries")
+    ap.add_argument("--points", type=int, default=0,
+                    help="run the workload with this many points per problem instead (profiling runs whose "
+                         "counters must stay below 2^31 per dispatch); the line then names the reduced size")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -539,6 +595,8 @@ def main():
     km.load()  # raises if the HIP library is missing
     name = args.workload or workloads.HEADLINE
     wl = workloads.WORKLOADS[name]
+    if args.points:
+        wl = wl.replace(name=f"{wl.name}@N={args.points}", N=args.points)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     if wl.host:
@@ -553,45 +611,50 @@ def main():
     ws = km.workspace(B, N, d, K, x.dtype, dev)
     labels = torch.empty((B, N), dtype=torch.int32, device=dev)
     counts = torch.empty((B, K), dtype=torch.int32, device=dev)
-    obj = torch.empty((max(args.steps, args.warmup, 1), B), dtype=torch.float64, device=dev)
+    obj = torch.empty((B, max(args.warmup, 1)), dtype=torch.float64, device=dev)
 
     if d == 1:
         return bench_fit_1d(args, km, wl, p, x, w, C)
 
-    def step(k):
-        km.kmeans_assign(x, C, weights=w, labels=labels, objective=obj[k], ws=ws)
-
-    for k in range(args.warmup):
-        step(k)
-        km.kmeans_update(x, labels, C, weights=w, c_new=C, counts=counts, ws=ws)
+    # warmup: W iterations of the fit, continued by the timed fit from where
+    # they left the centroids
+    if args.warmup > 0:
+        km.kmeans_fit(x, C, args.warmup, weights=w, centroids=C, labels=labels, counts=counts,
+                      objective=obj[:, :args.warmup].contiguous(), ws=ws)
     torch.cuda.synchronize()
 
+    # The timed region is ONE kmeans_fit call of exactly K iterations: each
+    # iteration is prep (fused into the previous divide), the assignment with
+    # the objective, the argsort, the segmented reduction and the divide.
+    # The library records a pair of events around every iteration's
+    # assignment kernel on the launch stream.
     K_steps = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K_steps)]
+    for e in events:
+        e.record()  # creates the events; the fit re-records them in place
+    e_end = torch.cuda.Event(enable_timing=True)
+    objK = torch.empty((B, K_steps), dtype=torch.float64, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(K_steps):
-        ev[k][0].record()
-        step(k)
-        ev[k][1].record()
-        km.kmeans_update(x, labels, C, weights=w, c_new=C, counts=counts, ws=ws)
-        ev[k][2].record()
+    km.kmeans_fit(x, C, K_steps, weights=w, centroids=C, labels=labels, counts=counts, objective=objK, ws=ws,
+                  assign_events=events)
+    e_end.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     elapsed = t1 - t0
-    assign_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K_steps
-    update_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K_steps
-    if d == 1:
-        bound, unit = "hbm", "GB/s"
-        algo = assign_bytes(wl)
-        achieved = algo / (assign_ms * 1e-3) / 1e9
-        peak = PEAK_HBM_GBS
-    else:
-        bound, unit = "mfma", "TFLOP/s"
-        algo = 2.0 * B * N * K * d
-        achieved = algo / (assign_ms * 1e-3) / 1e12
-        peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    assign_each = [events[2 * k].elapsed_time(events[2 * k + 1]) for k in range(K_steps)]
+    # the rest of an iteration: from the end of its assignment to the start of
+    # the next one (objective reduction, argsort, segmented reduction, divide
+    # fused with the next prep); the last iteration ends with the call
+    rest_each = [events[2 * k + 1].elapsed_time(events[2 * k + 2]) for k in range(K_steps - 1)]
+    rest_each.append(events[2 * K_steps - 1].elapsed_time(e_end))
+    assign_ms = sum(assign_each) / K_steps
+    update_ms = sum(rest_each) / K_steps
+    bound, unit = "mfma", "TFLOP/s"
+    algo = 2.0 * B * N * K * d
+    achieved = algo / (assign_ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
     ub = update_bytes(wl)
     out = {
         "metric": METRIC,
@@ -607,15 +670,22 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "N": N, "d": d, "K": K, "point_dtype": wl.dtype,
-                   "weighted": wl.weighted, "init": wl.init},
+                   "weighted": wl.weighted, "init": wl.init, "step": "one kmeans_fit call of `steps` iterations"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": _traffic(wl),
-                     "kernel": "k_assign_1d" if d == 1 else "k_assign_mfma",
-                     "algorithmic_per_launch": algo, "avg_launch_ms": assign_ms},
+                     "kernel": "k_assign_mfma",
+                     "algorithmic_per_launch": algo, "avg_launch_ms": assign_ms,
+                     "timing": "HIP events recorded by the library around each assignment kernel in the timed fit"},
         "update": {"avg_ms": update_ms, "algorithmic_bytes": ub, "GB/s": ub / (update_ms * 1e-3) / 1e9,
-                   "frac_hbm": ub / (update_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                   "frac_hbm": ub / (update_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "timing": "events: end of one assignment to the start of the next (objective reduction, "
+                             "argsort, segmented reduction, divide + next prep)"},
         "cpu_baseline": None,
     }
+    del x, w, ws, labels, counts
+    torch.cuda.empty_cache()
+    if not args.no_zipf_update and wl.name == workloads.HEADLINE and not args.points:
+        out["update_zipf"] = bench_update(km, workloads.WORKLOADS["zipf-n32m-k4096-d128-bf16"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -10,7 +10,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkmeans_mi355x.so")
+# KM_LIBRARY may name another build of the same sources (the sanitized host
+# build of the CPU test tier); by default the library next to this file.
+LIB_PATH = os.environ.get("KM_LIBRARY") or os.path.join(HERE, "libkmeans_mi355x.so")
 
 KM_F32, KM_F16, KM_BF16 = 0, 1, 2
 STATUS = {0: "KM_OK", 1: "KM_EINVAL", 2: "KM_EUNSUPPORTED", 3: "KM_EWORKSPACE", 4: "KM_EHIP"}
@@ -23,6 +25,8 @@ SIGNATURES = {
     "kmeans_sort_labels": (C.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "kmeans_update": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p, _sz, _p]),
     "kmeans_fit": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "kmeans_fit_timed": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p, _p, _sz,
+                                   _p]),
     "kmeans_stream_workspace_bytes": (_sz, [_i64, _i64, _i64, C.c_int, _i64]),
     "kmeans_fit_stream": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p, _sz,
                                     _p]),

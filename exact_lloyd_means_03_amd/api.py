@@ -6,6 +6,8 @@ computation runs in the HIP kernels of libkmeans_mi355x.so.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -133,9 +135,12 @@ def kmeans_update(x, labels, c_old, weights=None, c_new=None, counts=None, ws=No
 
 
 def kmeans_fit(x, init, n_iter: int, weights=None, centroids=None, labels=None, counts=None,
-               objective=None, ws=None):
+               objective=None, ws=None, assign_events=None):
     """n_iter Lloyd iterations from init.  Returns (centroids, labels, counts,
-    objective [B, n_iter] float64)."""
+    objective [B, n_iter] float64).  assign_events: None, or 2 * n_iter
+    recorded torch.cuda.Event objects (enable_timing=True) of the tensors'
+    device; event 2t is re-recorded right before iteration t's assignment
+    kernels and event 2t + 1 right after them (kmeans_fit_timed)."""
     B, N, d = _points(x)
     _dev_tensor(init, "init", torch.float32)
     if init.dim() != 3 or init.shape[0] != B or init.shape[2] != d:
@@ -153,10 +158,25 @@ def kmeans_fit(x, init, n_iter: int, weights=None, centroids=None, labels=None, 
     objective = torch.empty((B, max(n_iter, 0)), dtype=torch.float64, device=dev) if objective is None else \
         _dev_tensor(objective, "objective", torch.float64, (B, n_iter))
     ws = _ws(ws, B, N, d, K, x.dtype, dev)
-    st = _lib.load().kmeans_fit(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, d, K, _ptr(init), int(n_iter),
-                                _ptr(centroids), _ptr(labels), _ptr(counts), _ptr(objective), _ptr(ws),
-                                ws.numel(), _stream(dev))
-    _lib.check(st, "kmeans_fit")
+    if assign_events is None:
+        st = _lib.load().kmeans_fit(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, d, K, _ptr(init), int(n_iter),
+                                    _ptr(centroids), _ptr(labels), _ptr(counts), _ptr(objective), _ptr(ws),
+                                    ws.numel(), _stream(dev))
+        _lib.check(st, "kmeans_fit")
+        return centroids, labels, counts, objective
+    if len(assign_events) != 2 * n_iter:
+        raise ValueError(f"assign_events must hold 2 * n_iter = {2 * n_iter} events")
+    handles = []
+    for e in assign_events:
+        h = getattr(e, "cuda_event", 0)
+        if not h:
+            raise ValueError("assign_events must be torch.cuda.Event objects recorded once (so that they exist)")
+        handles.append(h)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    st = _lib.load().kmeans_fit_timed(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, d, K, _ptr(init), int(n_iter),
+                                      _ptr(centroids), _ptr(labels), _ptr(counts), _ptr(objective), arr, _ptr(ws),
+                                      ws.numel(), _stream(dev))
+    _lib.check(st, "kmeans_fit_timed")
     return centroids, labels, counts, objective
 
 

@@ -11,10 +11,18 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-BUILD = os.path.join(HERE, "_build")
-LIB = os.path.join(HERE, "libkmeans_mi355x.so")
 ARCH = os.environ.get("KM_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# KM_SANITIZE=1: the host code (argument checks, workspace plans, launch
+# sequences) is built with AddressSanitizer and UndefinedBehaviorSanitizer,
+# into _build_san/ next to this file (never over the product library); the
+# tests load it when KM_LIBRARY names it (tests/run_sanitized.py does both).
+# Device code is built as usual.
+SANITIZE = os.environ.get("KM_SANITIZE", "") == "1"
+BUILD = os.path.join(HERE, "_build_san" if SANITIZE else "_build")
+LIB = os.path.join(BUILD, "libkmeans_mi355x.so") if SANITIZE else os.path.join(HERE, "libkmeans_mi355x.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
 SOURCES = ["small.hip", "assign_mfma.hip", "assign_1d.hip", "fit_1d.hip", "optimal_1d.hip", "emeans.hip",
            "sort.hip", "update.hip", "api.hip"]
@@ -36,7 +44,8 @@ EXTRA = {"assign_mfma.hip": ["-fno-honor-nans"]}
 
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), *(SAN_FLAGS if SANITIZE else []), "-c", os.path.join(CSRC, src),
+           "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,7 +63,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *(SAN_FLAGS if SANITIZE else []), *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -71,6 +71,12 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
     w.piece_seg = take(Bz * np * sizeof(int32_t));
     w.slot = take(Bz * np * d * sizeof(float));
     w.wslot = take(Bz * np * sizeof(float));
+    const size_t ng = (size_t)fold_groups((int64_t)np);
+    w.gslot = take(Bz * ng * d * sizeof(float));
+    w.gwslot = take(Bz * ng * sizeof(float));
+    const size_t nch = (size_t)sort_chunks(B, N, K);
+    w.hist = take(Bz * nch * K * sizeof(int32_t));
+    w.prefix = take(Bz * nch * K * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -80,6 +86,17 @@ Workspace plan_workspace(int64_t B, int64_t N, int64_t d, int64_t K, DType xt) {
 using namespace km;
 
 namespace {
+
+// The code of an enum argument as the caller passed it: a C caller may pass
+// any int, and reading a value outside the enumerators through the enum type
+// is undefined, so the bytes are read as an int.
+template <typename E>
+int enum_code(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "enums of the ABI are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
 
 constexpr int64_t kMaxD = 512;     // 16-bit points
 constexpr int64_t kMaxDF32 = 256;  // float32 points
@@ -147,15 +164,21 @@ P* at(void* ws, size_t off) {
 // Assignment of all B*N points against C; optional per-block objective
 // partials reduced into obj_out[b * obj_stride].  prep = false: the tile
 // blob already holds C (written by the previous update's fused divide).
+// ev_begin / ev_end (may be NULL): recorded on s right before and right after
+// the assignment kernel launches (after the prep, before the objective
+// reduction).
 km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, const float* C, int64_t K,
                      const float* w, int32_t* labels, float* min_dist, double* obj_out, int64_t obj_stride,
-                     const Workspace& W, void* ws, hipStream_t s, bool prep = true) {
+                     const Workspace& W, void* ws, hipStream_t s, bool prep = true, hipEvent_t ev_begin = nullptr,
+                     hipEvent_t ev_end = nullptr, int32_t* hist = nullptr) {
     double* part = obj_out ? at<double>(ws, W.obj_part) : nullptr;
     if (use_assign_1d(d, K)) {
+        if (ev_begin) KM_HIP(hipEventRecord(ev_begin, s), "event");
         if (obj_out && N > 0 && W.nblk_assign == 1) {
             // one partial per row: it is the row's objective, written in place
             KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, obj_out, obj_stride, 1, s),
                    "assign_1d");
+            if (ev_end) KM_HIP(hipEventRecord(ev_end, s), "event");
             return KM_OK;
         }
         KM_HIP(launch_assign_1d(xt, x, B, N, C, K, w, labels, min_dist, part, W.nblk_assign, W.nblk_assign, s),
@@ -163,10 +186,12 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
     } else {
         void* blob = at<void>(ws, W.chat);
         if (prep) KM_HIP(launch_prep(xt, C, B, K, (int)d, W.DP, W.Kp, blob, s), "prep");
+        if (ev_begin) KM_HIP(hipEventRecord(ev_begin, s), "event");
         KM_HIP(launch_assign_mfma(xt, x, B, N, (int)d, W.DP, blob, W.Kp, w, labels, min_dist, part,
-                                  W.nblk_assign, at<void>(ws, W.split), s),
+                                  W.nblk_assign, at<void>(ws, W.split), s, nullptr, K, hist),
                "assign_mfma");
     }
+    if (ev_end) KM_HIP(hipEventRecord(ev_end, s), "event");
     if (obj_out) {
         if (N == 0) {
             KM_HIP(launch_zero(part, (size_t)B * W.nblk_assign * sizeof(double), s), "zero");
@@ -176,15 +201,18 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
     return KM_OK;
 }
 
+// The stable argsort of the labels (histogram rows in W.hist / W.prefix).
 // piece_seg (may be NULL): also record the first segment of every reduction
 // piece; short_flag (may be NULL): also flag the problems whose clusters are
-// all short enough for the one-segment-per-row-group reduction.
+// all short enough for the one-segment-per-row-group reduction.  counted:
+// the assignment already built the histogram rows.
 km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts, int32_t* offsets,
                    int32_t* perm, int32_t* piece_seg, int32_t* short_flag, const Workspace& W, void* ws,
-                   hipStream_t s) {
-    KM_HIP(launch_zero(counts, (size_t)B * K * sizeof(int32_t), s), "zero");
-    KM_HIP(launch_sort(labels, B, N, K, counts, offsets, at<int32_t>(ws, W.cursor), perm, segreduce_tw(B, N),
-                       segreduce_pieces(B, N), piece_seg, short_flag, s),
+                   hipStream_t s, bool counted = false) {
+    SortBufs o{counts, offsets, perm, at<int32_t>(ws, W.hist), at<int32_t>(ws, W.prefix), nullptr, piece_seg,
+               short_flag};
+    KM_HIP(launch_sort(labels, B, N, K, o, segreduce_tw(B, N), segreduce_pieces(B, N), s,
+                       counted ? SortMode::StableCounted : SortMode::Stable),
            "sort");
     return KM_OK;
 }
@@ -193,30 +221,33 @@ km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32
 // (the divide fused with the prep; matrix-core path only).
 km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t N, int64_t d,
                      const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
-                     const Workspace& W, void* ws, hipStream_t s, bool prep_next = false) {
+                     const Workspace& W, void* ws, hipStream_t s, bool prep_next = false, bool counted = false) {
     int32_t* cnt = counts ? counts : at<int32_t>(ws, W.counts);
     if (use_update_1d(xt, x, w, labels, d, N, K)) {
         KM_HIP(launch_update_1d_row(xt, x, w, B, N, labels, K, c_old, c_new, cnt, s), "update_1d_row");
         return KM_OK;
     }
+    // no clearing: every non-empty cluster's sum is stored once before the
+    // fold adds its slots, and empty clusters' sums are never read
     float* sums = at<float>(ws, W.sums);
-    float* wsum = at<float>(ws, W.wsum);
-    // sums and wsum are adjacent in the plan: clear both with one fill
-    KM_HIP(launch_zero(sums, W.offsets - W.sums, s), "zero");
+    float* wsum = w ? at<float>(ws, W.wsum) : nullptr;
     int32_t* offsets = at<int32_t>(ws, W.offsets);
     int32_t* perm = at<int32_t>(ws, W.perm);
     int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
     int32_t* short_flag = at<int32_t>(ws, W.seg_short);
-    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, short_flag, W, ws, s));
-    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, w ? wsum : nullptr, piece_seg,
-                            at<float>(ws, W.slot), at<float>(ws, W.wslot), short_flag, s),
+    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, short_flag, W, ws, s, counted));
+    float* slot = at<float>(ws, W.slot);
+    float* wslot = w ? at<float>(ws, W.wslot) : nullptr;
+    float* gslot = at<float>(ws, W.gslot);
+    float* gwslot = w ? at<float>(ws, W.gwslot) : nullptr;
+    KM_HIP(launch_segreduce(xt, x, w, B, N, (int)d, perm, offsets, K, sums, wsum, piece_seg, slot, wslot, gslot,
+                            gwslot, short_flag, s),
            "segreduce");
-    if (prep_next && !use_assign_1d(d, K))
-        KM_HIP(launch_divide_prep(xt, sums, w ? wsum : nullptr, cnt, B, K, (int)d, W.DP, W.Kp, c_old, c_new,
-                                  at<void>(ws, W.chat), s),
-               "divide");
-    else
-        KM_HIP(launch_divide(sums, w ? wsum : nullptr, cnt, B, K, (int)d, c_old, c_new, s), "divide");
+    void* blob = (prep_next && !use_assign_1d(d, K)) ? at<void>(ws, W.chat) : nullptr;
+    KM_HIP(launch_fold_divide(xt, sums, wsum, slot, wslot, gslot, gwslot, offsets, cnt,
+                              N <= kShortSegMean * K ? short_flag : nullptr, segreduce_pieces(B, N),
+                              segreduce_tw(B, N), B, K, (int)d, W.DP, W.Kp, c_old, c_new, blob, s),
+           "fold_divide");
     return KM_OK;
 }
 
@@ -357,26 +388,42 @@ double emeans_step_size(double alpha0, double floor_frac, int64_t t, int64_t T) 
            alpha0 * (1.0 - floor_frac) * 0.5 * (1.0 + cos(acos(-1.0) * (double)t / (double)(T - 1)));
 }
 
+km_status check_fit_args(const void* x, int xt, int64_t B, int64_t N, int64_t d, int64_t K, const float* init,
+                         int32_t n_iter, const float* centroids) {
+    KM_TRY(check_shape(B, N, d, K, enum_code(xt)));
+    if (n_iter < 0) return fail(KM_EINVAL, "n_iter=%d < 0", n_iter);
+    KM_TRY(check_scalar_k(d, K));
+    KM_TRY(need(x, B * N, "x"));
+    KM_TRY(need(init, B, "init"));
+    KM_TRY(need(centroids, B, "centroids"));
+    return KM_OK;
+}
+
+km_status run_fit(const void* x, int xt, const float* weights, int64_t B, int64_t N, int64_t d, int64_t K,
+                  const float* init, int32_t n_iter, float* centroids, int32_t* labels, int32_t* counts,
+                  double* objective, const Workspace& W, void* workspace, hipStream_t s,
+                  void* const* assign_events = nullptr);
+
 }  // namespace
 
 extern "C" {
 
 size_t kmeans_workspace_bytes(int64_t B, int64_t N, int64_t d, int64_t K, km_dtype xt) {
-    if (check_shape(B, N, d, K, (int)xt) != KM_OK) return 0;
-    return plan_workspace(B, N, d, K, (DType)xt).total;
+    if (check_shape(B, N, d, K, enum_code(xt)) != KM_OK) return 0;
+    return plan_workspace(B, N, d, K, (DType)enum_code(xt)).total;
 }
 
 km_status kmeans_assign(const void* x, km_dtype xt, int64_t B, int64_t N, int64_t d, const float* centroids,
                         int64_t K, const float* weights, int32_t* labels, float* min_dist, double* objective,
                         void* workspace, size_t workspace_bytes, km_stream stream) {
-    KM_TRY(check_shape(B, N, d, K, (int)xt));
+    KM_TRY(check_shape(B, N, d, K, enum_code(xt)));
     KM_TRY(check_scalar_k(d, K));
     KM_TRY(need(x, B * N, "x"));
     KM_TRY(need(centroids, B, "centroids"));
     KM_TRY(need(labels, B * N, "labels"));
-    const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
+    const Workspace W = plan_workspace(B, N, d, K, (DType)enum_code(xt));
     KM_TRY(check_ws(W, workspace, workspace_bytes));
-    return run_assign(x, (DType)xt, B, N, d, centroids, K, weights, labels, min_dist, objective, 1, W,
+    return run_assign(x, (DType)enum_code(xt), B, N, d, centroids, K, weights, labels, min_dist, objective, 1, W,
                       workspace, (hipStream_t)stream);
 }
 
@@ -385,12 +432,16 @@ km_status kmeans_sort_labels(const int32_t* labels, int64_t B, int64_t N, int64_
                              km_stream stream) {
     KM_TRY(check_shape(B, N, 2, K, KM_F32));
     KM_TRY(need(labels, B * N, "labels"));
-    // cursors, then whichever outputs the caller left to the workspace; this
-    // never exceeds kmeans_workspace_bytes() of the same B, N, K for any d
+    // histogram rows and their prefix, then whichever outputs the caller left
+    // to the workspace; this never exceeds kmeans_workspace_bytes() of the
+    // same B, N, K for any d
     Workspace W{};
     size_t off = 0;
-    W.cursor = off;
-    off += align_up((size_t)B * K * sizeof(int32_t));
+    const size_t rows = (size_t)B * sort_chunks(B, N, K) * K * sizeof(int32_t);
+    W.hist = off;
+    off += align_up(rows);
+    W.prefix = off;
+    off += align_up(rows);
     if (!counts) { W.counts = off; off += align_up((size_t)B * K * sizeof(int32_t)); }
     if (!offsets) { W.offsets = off; off += align_up((size_t)B * (K + 1) * sizeof(int32_t)); }
     if (!perm) { W.perm = off; off += align_up((size_t)B * N * sizeof(int32_t)); }
@@ -405,51 +456,86 @@ km_status kmeans_sort_labels(const int32_t* labels, int64_t B, int64_t N, int64_
 km_status kmeans_update(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d,
                         const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
                         void* workspace, size_t workspace_bytes, km_stream stream) {
-    KM_TRY(check_shape(B, N, d, K, (int)xt));
+    KM_TRY(check_shape(B, N, d, K, enum_code(xt)));
     KM_TRY(need(x, B * N, "x"));
     KM_TRY(need(labels, B * N, "labels"));
     KM_TRY(need(c_old, B, "c_old"));
     KM_TRY(need(c_new, B, "c_new"));
-    const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
+    const Workspace W = plan_workspace(B, N, d, K, (DType)enum_code(xt));
     KM_TRY(check_ws(W, workspace, workspace_bytes));
-    return run_update(x, (DType)xt, weights, B, N, d, labels, K, c_old, c_new, counts, W, workspace,
+    return run_update(x, (DType)enum_code(xt), weights, B, N, d, labels, K, c_old, c_new, counts, W, workspace,
                       (hipStream_t)stream);
 }
 
 km_status kmeans_fit(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d, int64_t K,
                      const float* init, int32_t n_iter, float* centroids, int32_t* labels, int32_t* counts,
                      double* objective, void* workspace, size_t workspace_bytes, km_stream stream) {
-    KM_TRY(check_shape(B, N, d, K, (int)xt));
-    if (n_iter < 0) return fail(KM_EINVAL, "n_iter=%d < 0", n_iter);
-    KM_TRY(check_scalar_k(d, K));
-    KM_TRY(need(x, B * N, "x"));
-    KM_TRY(need(init, B, "init"));
-    KM_TRY(need(centroids, B, "centroids"));
-    const Workspace W = plan_workspace(B, N, d, K, (DType)xt);
+    KM_TRY(check_fit_args(x, enum_code(xt), B, N, d, K, init, n_iter, centroids));
+    const Workspace W = plan_workspace(B, N, d, K, (DType)enum_code(xt));
     KM_TRY(check_ws(W, workspace, workspace_bytes));
-    hipStream_t s = (hipStream_t)stream;
+    return run_fit(x, enum_code(xt), weights, B, N, d, K, init, n_iter, centroids, labels, counts, objective, W,
+                   workspace, (hipStream_t)stream);
+}
+
+km_status kmeans_fit_timed(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d,
+                           int64_t K, const float* init, int32_t n_iter, float* centroids, int32_t* labels,
+                           int32_t* counts, double* objective, void* const* assign_events, void* workspace,
+                           size_t workspace_bytes, km_stream stream) {
+    KM_TRY(check_fit_args(x, enum_code(xt), B, N, d, K, init, n_iter, centroids));
+    KM_TRY(need(assign_events, n_iter, "assign_events"));
+    for (int32_t i = 0; i < 2 * n_iter; ++i)
+        if (assign_events[i] == nullptr) return fail(KM_EINVAL, "assign_events[%d] is NULL", i);
+    const Workspace W = plan_workspace(B, N, d, K, (DType)enum_code(xt));
+    KM_TRY(check_ws(W, workspace, workspace_bytes));
+    return run_fit(x, enum_code(xt), weights, B, N, d, K, init, n_iter, centroids, labels, counts, objective, W,
+                   workspace, (hipStream_t)stream, assign_events);
+}
+
+}  // extern "C"
+
+namespace {
+
+km_status run_fit(const void* x, int xt, const float* weights, int64_t B, int64_t N, int64_t d, int64_t K,
+                  const float* init, int32_t n_iter, float* centroids, int32_t* labels, int32_t* counts,
+                  double* objective, const Workspace& W, void* workspace, hipStream_t s,
+                  void* const* assign_events) {
+    auto ev = [&](int64_t i) { return assign_events ? (hipEvent_t)assign_events[i] : nullptr; };
     if (d == 1 && n_iter > 0 && fit_1d_rows_fits(N, K)) {
         // scalar rows that fit on chip: every iteration in one launch
-        KM_HIP(launch_fit_1d_rows((DType)xt, x, weights, B, N, init, K, n_iter, centroids, labels, counts,
+        for (int32_t t = 0; t < n_iter && assign_events; ++t) KM_HIP(hipEventRecord(ev(2 * t), s), "event");
+        KM_HIP(launch_fit_1d_rows((DType)enum_code(xt), x, weights, B, N, init, K, n_iter, centroids, labels, counts,
                                   objective, s),
                "fit_1d_rows");
+        for (int32_t t = 0; t < n_iter && assign_events; ++t) KM_HIP(hipEventRecord(ev(2 * t + 1), s), "event");
         return KM_OK;
     }
     if (init != centroids && B > 0)
         KM_HIP(hipMemcpyAsync(centroids, init, (size_t)B * K * d * sizeof(float), hipMemcpyDeviceToDevice, s),
                "copy init");
     int32_t* lab = labels ? labels : at<int32_t>(workspace, W.labels);
+    // the matrix-core assignment adds its labels to the sort's histogram rows
+    // (cleared here once; every sort clears them again after use), so the
+    // update needs no separate pass over the labels
+    const bool counted = n_iter > 0 && N > 0 && B > 0 && !use_assign_1d(d, K) &&
+                         !assign_mfma_merges(B, N, W.DP, (DType)enum_code(xt), W.Kp);
+    int32_t* hist = counted ? at<int32_t>(workspace, W.hist) : nullptr;
+    if (counted) KM_HIP(launch_zero(hist, W.prefix - W.hist, s), "zero");
     for (int32_t t = 0; t < n_iter; ++t) {
         // from the second iteration on, the previous update's divide wrote the
         // centroid tiles, unless the update took the scalar-row path
-        const bool fused = t > 0 && !use_update_1d((DType)xt, x, weights, lab, d, N, K);
-        KM_TRY(run_assign(x, (DType)xt, B, N, d, centroids, K, weights, lab, nullptr,
-                          objective ? objective + t : nullptr, n_iter, W, workspace, s, !fused));
-        KM_TRY(run_update(x, (DType)xt, weights, B, N, d, lab, K, centroids, centroids, counts, W, workspace, s,
-                          t + 1 < n_iter));
+        const bool fused = t > 0 && !use_update_1d((DType)enum_code(xt), x, weights, lab, d, N, K);
+        KM_TRY(run_assign(x, (DType)enum_code(xt), B, N, d, centroids, K, weights, lab, nullptr,
+                          objective ? objective + t : nullptr, n_iter, W, workspace, s, !fused, ev(2 * t),
+                          ev(2 * t + 1), hist));
+        KM_TRY(run_update(x, (DType)enum_code(xt), weights, B, N, d, lab, K, centroids, centroids, counts, W, workspace, s,
+                          t + 1 < n_iter, counted));
     }
     return KM_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t kmeans_optimal_1d_workspace_bytes(int64_t B, int64_t N, int64_t K) {
     if (B < 0 || !optimal_1d_supports(N, K)) return 0;
@@ -462,7 +548,8 @@ km_status kmeans_optimal_1d(const void* x, km_dtype xt, const float* weights, in
                             float* centroids, int32_t* labels, int32_t* counts, double* objective,
                             void* workspace, size_t workspace_bytes, km_stream stream) {
     if (B < 0 || N < 0) return fail(KM_EINVAL, "negative size: B=%lld N=%lld", (long long)B, (long long)N);
-    if (xt != KM_F32 && xt != KM_F16 && xt != KM_BF16) return fail(KM_EUNSUPPORTED, "unknown dtype %d", xt);
+    const int xc = enum_code(xt);
+    if (xc != KM_F32 && xc != KM_F16 && xc != KM_BF16) return fail(KM_EUNSUPPORTED, "unknown dtype %d", xc);
     if (K < 1 || K > N)
         return fail(KM_EINVAL, "the optimum needs 1 <= K <= N (K=%lld, N=%lld)", (long long)K, (long long)N);
     if (N > kOpt1DMaxN)
@@ -478,29 +565,29 @@ km_status kmeans_optimal_1d(const void* x, km_dtype xt, const float* weights, in
     Workspace W{};
     W.total = total;
     KM_TRY(check_ws(W, workspace, workspace_bytes));
-    KM_HIP(launch_optimal_1d((DType)xt, x, weights, B, N, K, centroids, labels, counts, objective, workspace,
-                             (hipStream_t)stream),
+    KM_HIP(launch_optimal_1d((DType)enum_code(xt), x, weights, B, N, K, centroids, labels, counts, objective,
+                             workspace, (hipStream_t)stream),
            "optimal_1d");
     return KM_OK;
 }
 
 size_t kmeans_stream_workspace_bytes(int64_t N, int64_t d, int64_t K, km_dtype xt, int64_t chunk) {
-    if (check_shape(1, N, d, K, (int)xt) != KM_OK || d < 2 || chunk < 1) return 0;
-    return plan_stream(N, d, K, (DType)xt, chunk).total;
+    if (check_shape(1, N, d, K, enum_code(xt)) != KM_OK || d < 2 || chunk < 1) return 0;
+    return plan_stream(N, d, K, (DType)enum_code(xt), chunk).total;
 }
 
 km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host, int64_t N, int64_t d, int64_t K,
                             const float* init, int32_t n_iter, float* centroids, int32_t* labels, int32_t* counts,
                             double* objective, int64_t chunk, void* workspace, size_t workspace_bytes,
                             km_stream stream) {
-    KM_TRY(check_shape(1, N, d, K, (int)xt));
+    KM_TRY(check_shape(1, N, d, K, enum_code(xt)));
     if (d < 2) return fail(KM_EUNSUPPORTED, "streamed fits need d >= 2 (d=%lld)", (long long)d);
     if (n_iter < 0) return fail(KM_EINVAL, "n_iter=%d < 0", n_iter);
     if (chunk < 1) return fail(KM_EINVAL, "chunk=%lld < 1", (long long)chunk);
     KM_TRY(need(x_host, N, "x_host"));
     KM_TRY(need(init, 1, "init"));
     KM_TRY(need(centroids, 1, "centroids"));
-    const DType t = (DType)xt;
+    const DType t = (DType)enum_code(xt);
     const StreamPlan P = plan_stream(N, d, K, t, chunk);
     {
         Workspace W{};
@@ -562,15 +649,16 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
             int32_t* offsets = at<int32_t>(ws, W.offsets);
             int32_t* perm = at<int32_t>(ws, W.perm);
             int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
-            KM_HIP(launch_zero(cnt, (size_t)K * sizeof(int32_t), s), "zero");
             // every chunk uses the piece width of a full chunk, so a shorter
-            // last chunk never has more pieces than the plan holds
+            // last chunk never has more pieces than the plan holds (nor more
+            // histogram rows: a shorter chunk has at most as many)
             const int TW = segreduce_tw(1, c);
-            KM_HIP(launch_sort(lab, 1, nc, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (nc + TW - 1) / TW,
-                               piece_seg, nullptr, s),
-                   "sort");
+            SortBufs o{cnt, offsets, perm, at<int32_t>(ws, W.hist), at<int32_t>(ws, W.prefix), nullptr, piece_seg,
+                       nullptr};
+            KM_HIP(launch_sort(lab, 1, nc, K, o, TW, (nc + TW - 1) / TW, s, SortMode::Stable), "sort");
             KM_HIP(launch_segreduce_tw(t, xb, wb, 1, nc, (int)d, perm, offsets, K, sums, wsum, piece_seg,
-                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, true, nullptr, s),
+                                       at<float>(ws, W.slot), at<float>(ws, W.wslot), nullptr, nullptr, TW, true,
+                                       nullptr, s),
                    "segreduce");
             KM_HIP(launch_add_i32(ctot, cnt, K, s), "add counts");
             KM_HIP(hipEventRecord(R->consumed[buf], s), "event");
@@ -588,16 +676,16 @@ km_status kmeans_fit_stream(const void* x_host, km_dtype xt, const float* w_host
 }
 
 size_t kmeans_emeans_workspace_bytes(int64_t N, int64_t d, int64_t K, km_dtype xt, int64_t batch) {
-    if (check_shape(1, N, d, K, (int)xt) != KM_OK || batch < 1 || !emeans_split_supports(K)) return 0;
+    if (check_shape(1, N, d, K, enum_code(xt)) != KM_OK || batch < 1 || !emeans_split_supports(K)) return 0;
     if (d == 1 && !assign_1d_supports(K)) return 0;
-    return plan_emeans(N, d, K, (DType)xt, batch, 1).total;
+    return plan_emeans(N, d, K, (DType)enum_code(xt), batch, 1).total;
 }
 
 km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_t K, const float* init,
                         int64_t batch, int32_t epochs, double alpha0, double floor_frac, double dead_frac,
                         double eps, const float* uniforms, float* centroids, int32_t* labels, int32_t* counts,
                         double* objective, void* workspace, size_t workspace_bytes, km_stream stream) {
-    KM_TRY(check_shape(1, N, d, K, (int)xt));
+    KM_TRY(check_shape(1, N, d, K, enum_code(xt)));
     KM_TRY(check_scalar_k(d, K));
     if (!emeans_split_supports(K))
         return fail(KM_EUNSUPPORTED, "e-means supports K <= %lld (K=%lld)", (long long)kEmeansMaxK, (long long)K);
@@ -612,7 +700,7 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
     KM_TRY(need(init, 1, "init"));
     KM_TRY(need(centroids, 1, "centroids"));
     if (dead_frac > 0.0) KM_TRY(need(uniforms, N, "uniforms"));
-    const DType t = (DType)xt;
+    const DType t = (DType)enum_code(xt);
     const EmeansPlan P = plan_emeans(N, d, K, t, batch, epochs);
     {
         Workspace W{};
@@ -673,11 +761,14 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
                    "assign_mfma");
         }
         // the batch's objective partials are summed by the moving-average kernel below
-        KM_HIP(launch_sort(lab, 1, m, K, cnt, offsets, at<int32_t>(ws, W.cursor), perm, TW, (m + TW - 1) / TW,
-                           piece_seg, at<int32_t>(ws, W.seg_short), s, counted),
+        SortBufs o{cnt, offsets, perm, nullptr, nullptr, at<int32_t>(ws, W.cursor), piece_seg,
+                   at<int32_t>(ws, W.seg_short)};
+        KM_HIP(launch_sort(lab, 1, m, K, o, TW, (m + TW - 1) / TW, s,
+                           counted ? SortMode::DirectCounted : SortMode::Direct),
                "sort");
+        // the atomic fold completes the sums (the moving average reads them)
         KM_HIP(launch_segreduce_tw(t, xb, nullptr, 1, m, (int)d, perm, offsets, K, sums, nullptr, piece_seg,
-                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), TW, false,
+                                   at<float>(ws, W.slot), at<float>(ws, W.wslot), nullptr, nullptr, TW, false,
                                    at<int32_t>(ws, W.seg_short), s),
                "segreduce");
         const double a = emeans_step_size(alpha0, floor_frac, st, P.steps);
@@ -694,14 +785,14 @@ km_status kmeans_emeans(const void* x, km_dtype xt, int64_t N, int64_t d, int64_
 }
 
 const char* kmeans_status_str(km_status st) {
-    switch (st) {
+    switch (enum_code(st)) {
         case KM_OK: return "ok";
         case KM_EINVAL: return "invalid argument";
         case KM_EUNSUPPORTED: return "unsupported shape or dtype";
         case KM_EWORKSPACE: return "workspace too small";
         case KM_EHIP: return "HIP runtime error";
+        default: return "unknown status";
     }
-    return "unknown status";
 }
 
 const char* kmeans_last_error(void) { return g_last_error.c_str(); }

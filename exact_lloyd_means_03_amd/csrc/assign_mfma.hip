@@ -230,7 +230,8 @@ template <typename T, int DP, bool VEC, int NCBT, int WAVEST>
 __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
     const T* __restrict__ X, int64_t N, int d, const char* __restrict__ blob, int ntiles, int tps,
     const float* __restrict__ w, int32_t* __restrict__ labels, float* __restrict__ min_dist,
-    double* __restrict__ obj_part, int64_t gpb, int64_t bgroups, int64_t ngroups, float* __restrict__ split) {
+    double* __restrict__ obj_part, int64_t gpb, int64_t bgroups, int64_t ngroups, float* __restrict__ split,
+    int32_t* __restrict__ hist, int64_t hist_ch, int64_t hist_nch, int K, int nbits) {
     typedef AssignCfg<T, DP, NCBT, WAVEST> Cfg;
     typedef Mf<T> M;
     typedef typename M::frag F;
@@ -511,6 +512,19 @@ __global__ __launch_bounds__(64 * WAVEST) void k_assign_mfma(
                     obj += (double)(w ? w[b * N + p] : 1.f) * (double)dist;
                 }
             }
+            if (hist) {
+                // the histogram row of the sort chunk that holds this group
+                // (a chunk is a whole number of groups): lanes with the same
+                // label add together, through their lowest lane
+                int32_t* row = hist + (b * hist_nch + (pg * Cfg::PTS) / hist_ch) * (int64_t)K;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const int64_t p = pg * Cfg::PTS + (wave * NCB + cb) * 32 + col;
+                    const bool act = half == 0 && p < N;
+                    const uint64_t m = lanes_matching(bidx[cb], nbits, act);
+                    if (act && lanes_below(m) == 0) atomicAdd(&row[bidx[cb]], (int32_t)__popcll(m));
+                }
+            }
         }
         if (obj_part) {
 #pragma unroll
@@ -673,7 +687,7 @@ template <typename T, int DP, int NCBT, int WV>
 static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const void* blob, int64_t ntiles,
                            const GroupShape& gs, const float* w, int32_t* labels, float* min_dist,
                            double* obj_part, int64_t nblk, void* scratch, int32_t* counts, int64_t K,
-                           hipStream_t s) {
+                           int32_t* hist, hipStream_t s) {
     const int64_t bgroups = B * nblk, ngroups = bgroups * gs.nslice;
     const bool vec = (d == DP) && ((uintptr_t)x % 16 == 0);
     const int64_t P = vec ? resident_blocks<T, DP, true, NCBT, WV>() : resident_blocks<T, DP, false, NCBT, WV>();
@@ -684,14 +698,17 @@ static hipError_t launch_n(const void* x, int64_t B, int64_t N, int d, const voi
     const int32_t* si = split ? (const int32_t*)scratch + gs.nslice * BN : nullptr;
     const float* sxx = split ? (const float*)scratch + 2 * gs.nslice * BN : nullptr;
     double* part = split ? nullptr : obj_part;
+    int32_t* hrow = split ? nullptr : hist;  // (the merge path does not build rows)
+    const int64_t hch = hrow ? sort_chunk(B, N, K) : 1, hnch = hrow ? sort_chunks(B, N, K) : 1;
+    const int nbits = label_bits(K);
     if (vec)
         hipLaunchKernelGGL((k_assign_mfma<T, DP, true, NCBT, WV>), grid, dim3(64 * WV), 0, s, (const T*)x, N, d,
                            (const char*)blob, (int)ntiles, (int)gs.tps, w, labels, min_dist, part, nblk, bgroups,
-                           ngroups, sv);
+                           ngroups, sv, hrow, hch, hnch, (int)K, nbits);
     else
         hipLaunchKernelGGL((k_assign_mfma<T, DP, false, NCBT, WV>), grid, dim3(64 * WV), 0, s, (const T*)x, N, d,
                            (const char*)blob, (int)ntiles, (int)gs.tps, w, labels, min_dist, part, nblk, bgroups,
-                           ngroups, sv);
+                           ngroups, sv, hrow, hch, hnch, (int)K, nbits);
     if (!split) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -707,7 +724,7 @@ template <typename T, int DP>
 static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const void* blob,
                            int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
                            double* obj_part, int64_t nblk, void* scratch, int32_t* counts, int64_t K,
-                           hipStream_t s) {
+                           int32_t* hist, hipStream_t s) {
     const GroupShape g = group_shape<T>(B, N, DP, ntiles);
     if (nblk != groups_per_problem(g, N)) return hipErrorInvalidValue;
     if (g.nslice > 1 && scratch == nullptr) return hipErrorInvalidValue;
@@ -715,19 +732,19 @@ static hipError_t launch_t(const void* x, int64_t B, int64_t N, int d, const voi
     if constexpr (DEF == 2) {
         if (g.ncb == 1)
             return launch_n<T, DP, 1, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk,
-                                          scratch, counts, K, s);
+                                          scratch, counts, K, hist, s);
     }
     return launch_n<T, DP, DEF, WV>(x, B, N, d, blob, ntiles, g, w, labels, min_dist, obj_part, nblk, scratch,
-                                    counts, K, s);
+                                    counts, K, hist, s);
 }
 
 template <typename T>
 static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, const void* blob,
                             int64_t ntiles, const float* w, int32_t* labels, float* min_dist,
                             double* obj_part, int64_t nblk, void* scratch, int32_t* counts, int64_t K,
-                            hipStream_t s) {
+                            int32_t* hist, hipStream_t s) {
 #define KM_LT(DPV) \
-    launch_t<T, DPV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, counts, K, s)
+    launch_t<T, DPV>(x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, counts, K, hist, s)
     switch (DP) {
         case 16: return KM_LT(16);
         case 32: return KM_LT(32);
@@ -748,17 +765,17 @@ static hipError_t launch_dp(int DP, const void* x, int64_t B, int64_t N, int d, 
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
                               float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s,
-                              int32_t* counts, int64_t K) {
+                              int32_t* counts, int64_t K, int32_t* hist) {
     if (B == 0 || N == 0) return hipSuccess;
     const int64_t ntiles = Kp / tile_rows(DP, dtype_bytes(xt));
     if (xt == DType::F32)
         return launch_dp<float>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch,
-                                counts, K, s);
+                                counts, K, hist, s);
     if (xt == DType::F16)
         return launch_dp<_Float16>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch,
-                                   counts, K, s);
+                                   counts, K, hist, s);
     return launch_dp<bf16_t>(DP, x, B, N, d, blob, ntiles, w, labels, min_dist, obj_part, nblk, scratch, counts,
-                             K, s);
+                             K, hist, s);
 }
 
 }  // namespace km

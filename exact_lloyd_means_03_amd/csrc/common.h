@@ -65,6 +65,30 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Lanes of the wave whose v equals this lane's (among the lanes where
+// `active` holds): one ballot per bit of the values (0 <= v < 2^nbits).
+__device__ __forceinline__ uint64_t lanes_matching(int32_t v, int nbits, bool active) {
+    uint64_t m = __ballot(active);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (v >> bit) & 1;
+        const uint64_t s = __ballot(active && set);
+        m &= set ? s : ~s;
+    }
+    return m;
+}
+
+// Set lanes of m below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Bits of the largest label K - 1 (0 for K == 1).
+inline int label_bits(int64_t K) {
+    int n = 0;
+    while ((int64_t(1) << n) < K) ++n;
+    return n;
+}
+
 // Workspace layout ----------------------------------------------------------
 // One layout serves every entry point; all regions are 256-byte aligned.
 struct Workspace {
@@ -82,6 +106,10 @@ struct Workspace {
     size_t piece_seg;  // [B][npieces] int32: first segment of each reduction piece
     size_t slot;       // [B][npieces][d] float: each piece's sum over its first segment
     size_t wslot;      // [B][npieces] float: its weight sum (weighted update)
+    size_t gslot;      // [B][fold groups][d] float: group slots of the deterministic fold
+    size_t gwslot;     // [B][fold groups] float
+    size_t hist;       // [B][sort chunks][K] int32: histogram rows of the label chunks
+    size_t prefix;     // [B][sort chunks][K] int32: their column prefix
     size_t total;
     int DP;
     int64_t Kp;
@@ -100,10 +128,13 @@ hipError_t launch_prep(DType xt, const float* C, int64_t B, int64_t K, int d, in
 // bytes (zero unless the launch cuts the centroids into slices).  counts
 // (may be NULL, [B][K], zero on entry): where assign_mfma_merges(...), the
 // merge also counts the labels; elsewhere it is ignored.
+// hist (may be NULL, unless merging): also add every label to the
+// histogram row of its sort chunk, hist[b][i / sort_chunk(B, N, K)][label]
+// (rows zero on entry), as the stable sort's StableCounted mode expects.
 hipError_t launch_assign_mfma(DType xt, const void* x, int64_t B, int64_t N, int d, int DP,
                               const void* blob, int64_t Kp, const float* w, int32_t* labels,
                               float* min_dist, double* obj_part, int64_t nblk, void* scratch, hipStream_t s,
-                              int32_t* counts = nullptr, int64_t K = 0);
+                              int32_t* counts = nullptr, int64_t K = 0, int32_t* hist = nullptr);
 int64_t assign_mfma_blocks(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
 bool assign_mfma_merges(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
 size_t assign_mfma_scratch_bytes(int64_t B, int64_t N, int DP, DType xt, int64_t Kp);
@@ -128,30 +159,67 @@ hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream
 constexpr int kShortSegMax = 64;
 constexpr int64_t kShortSegMean = 16;
 
-// piece_seg may be NULL (then TW and npieces are ignored).  short_flag (may
-// be NULL): per problem, 1 when no cluster has more than kShortSegMax points.
-// counted: counts already hold the labels' histogram (the count pass is skipped).
-hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K,
-                       int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* perm,
-                       int TW, int64_t npieces, int32_t* piece_seg, int32_t* short_flag, hipStream_t s,
-                       bool counted = false);
+// The argsort.  Stable: labels[perm] ascending, indices ascending within a
+// segment, deterministic.  Modes:
+//   Stable        -- histogram the labels into hist (rows of K per chunk of
+//                    sort_chunk() points), then as StableCounted;
+//   StableCounted -- hist already holds the histogram rows (the assignment
+//                    built them); they are cleared after use;
+//   Direct        -- unordered within a segment: one global atomic per label
+//                    (counts must be zero on entry; cursor needed);
+//   DirectCounted -- the same with counts already holding the histogram.
+enum class SortMode { Stable, StableCounted, Direct, DirectCounted };
+struct SortBufs {
+    int32_t* counts;      // [B][K]
+    int32_t* offsets;     // [B][K+1]
+    int32_t* perm;        // [B][N]
+    int32_t* hist;        // [B][nch][K] (stable modes)
+    int32_t* prefix;      // [B][nch][K] (stable modes)
+    int32_t* cursor;      // [B][K] (direct modes)
+    int32_t* piece_seg;   // [B][npieces] or NULL: first segment of every reduction piece
+    int32_t* short_flag;  // [B] or NULL: 1 when no cluster has more than kShortSegMax points
+};
+int64_t sort_chunk(int64_t B, int64_t N, int64_t K);
+int64_t sort_chunks(int64_t B, int64_t N, int64_t K);
+hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, const SortBufs& bufs, int TW,
+                       int64_t npieces, hipStream_t s, SortMode mode);
 
-// Segment sums of the sorted points (sums / wsum must be zero on entry).
-// short_flag (may be NULL): the sort's flags; with them, problems whose
-// clusters are all short are reduced one segment per row group instead.
+// Segment sums of the sorted points.  Each non-empty segment is stored once,
+// by the piece of TW sorted rows where it begins; the parts of a segment in
+// later pieces go to those pieces' slots.  Then either
+//   gslot == NULL: the slots are added into sums / wsum with atomics (sums
+//                  complete afterwards; order of the adds varies), or
+//   gslot != NULL: group slots are formed deterministically and
+//                  launch_fold_divide() adds them in a fixed order.
+// Empty clusters get nothing (their sums are not read).  short_flag (may be
+// NULL): the sort's flags; problems whose clusters are all short are reduced
+// one segment per row group instead (every cluster stored, empty ones 0).
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K,
                             float* sums, float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
-                            const int32_t* short_flag, hipStream_t s);
+                            float* gslot, float* gwslot, const int32_t* short_flag, hipStream_t s);
 // The same with a given piece width TW (the sort must have used the same).
-// accumulate: add into sums / wsum that hold earlier contributions (else
-// they must be zero on entry, and complete segments are stored).
+// accumulate: add every segment into sums / wsum, which hold earlier
+// contributions (the atomic fold; gslot is ignored).
 hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                                const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
-                               float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
-                               bool accumulate, const int32_t* short_flag, hipStream_t s);
+                               float* wsum, const int32_t* piece_seg, float* slot, float* wslot, float* gslot,
+                               float* gwslot, int TW, bool accumulate, const int32_t* short_flag, hipStream_t s);
 int64_t segreduce_pieces(int64_t B, int64_t N);
 int segreduce_tw(int64_t B, int64_t N);
+constexpr int kFoldG = 16;  // pieces per group slot
+int64_t fold_groups(int64_t npieces);
+
+// The deterministic fold fused with the divide: per cluster, the stored sum,
+// then its piece slots, then its group slots, added in that fixed order;
+// then c_new = S / W (or c_old for an empty cluster).  blob (may be NULL):
+// also write c_new in the tile layout of launch_prep for the next
+// assignment (xt, DP, Kp describe it).
+hipError_t launch_fold_divide(DType xt, const float* sums, const float* wsum, const float* slot, const float* wslot,
+                              const float* gslot, const float* gwslot, const int32_t* offsets,
+                              const int32_t* counts, const int32_t* short_flag, int64_t npieces, int TW, int64_t B,
+                              int64_t K, int d, int DP, int64_t Kp, const float* c_old, float* c_new, void* blob,
+                              hipStream_t s);
 
 hipError_t launch_divide(const float* sums, const float* wsum, const int32_t* counts,
                          int64_t B, int64_t K, int d, const float* c_old, float* c_new,

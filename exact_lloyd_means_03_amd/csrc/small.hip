@@ -107,6 +107,129 @@ __global__ __launch_bounds__(256) void k_divide_prep(const float* __restrict__ s
     if (lane == 0) *hn = real ? -0.5f * ss : -INFINITY;
 }
 
+// The deterministic fold of a Lloyd update fused with its divide (and, with
+// PREP, with the prep of the next assignment).  One wave per padded centroid
+// row (b, j); lane l holds coordinates l + 64 t.  For a cluster with points,
+// its sum is the value its first piece stored, then the slots of the pieces
+// after it that hold parts of it (the ones up to the end of the first piece's
+// group of kFoldG pieces), then the group slots of the following groups,
+// added in that order; the divide follows (IEEE float32, c_old for an empty
+// cluster).  Problems reduced one segment per row group (skip set) have
+// complete sums and no slots.
+template <typename T, bool WEIGHTED, bool PREP>
+__global__ __launch_bounds__(256) void k_fold_divide(
+    const float* __restrict__ sums, const float* __restrict__ wsum, const float* __restrict__ slot,
+    const float* __restrict__ wslot, const float* __restrict__ gslot, const float* __restrict__ gwslot,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts, const int32_t* __restrict__ skip,
+    int64_t npieces, int64_t ngroups, int TW, int64_t BKp, int64_t K, int64_t Kp, int d, int DP,
+    const float* c_old, float* c_new, char* __restrict__ blob) {
+    constexpr int U = 4;  // slots in flight
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= BKp) return;
+    const int64_t b = row / Kp, j = row - b * Kp;
+    const bool real = j < K;
+    const int64_t bj = b * K + j;
+    const int32_t n = real ? counts[bj] : 0;
+    float acc[8];
+    float wacc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int k = lane + 64 * t;
+        acc[t] = (n > 0 && k < d) ? sums[bj * d + k] : 0.f;
+    }
+    if (WEIGHTED && n > 0) wacc = wsum[bj];
+    if (n > 0 && !(skip && skip[b])) {
+        const int32_t o0 = offsets[b * (K + 1) + j], o1 = offsets[b * (K + 1) + j + 1];
+        const int64_t p_lo = o0 / TW + 1, p_hi = (o1 - 1) / TW;  // pieces holding a slot of this cluster
+        const int64_t g_lo = p_lo / kFoldG, g_hi = p_hi / kFoldG;
+        const int64_t ph = p_hi < (g_lo + 1) * kFoldG - 1 ? p_hi : (g_lo + 1) * kFoldG - 1;
+        // piece slots up to the end of the first group, then one group slot per group
+        auto add_run = [&](const float* base, const float* wbase, int64_t q0, int64_t q1) {
+            for (int64_t q = q0; q <= q1; q += U) {
+                float v[U][8], wv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool ok = q + u <= q1;
+                    const float* sp = base + (ok ? q + u : q0) * (int64_t)d;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int k = lane + 64 * t;
+                        v[u][t] = (ok && k < d) ? sp[k] : 0.f;
+                    }
+                    wv[u] = (WEIGHTED && ok) ? wbase[ok ? q + u : q0] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (q + u <= q1) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) acc[t] += v[u][t];
+                        if constexpr (WEIGHTED) wacc += wv[u];
+                    }
+                }
+            }
+        };
+        if (p_lo <= p_hi) {
+            add_run(slot + b * npieces * (int64_t)d, WEIGHTED ? wslot + b * npieces : nullptr, p_lo, ph);
+            if (g_hi > g_lo)
+                add_run(gslot + b * ngroups * (int64_t)d, WEIGHTED ? gwslot + b * ngroups : nullptr, g_lo + 1, g_hi);
+        }
+    }
+    const float W = n > 0 ? (WEIGHTED ? wacc : (float)n) : 1.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int k = lane + 64 * t;
+        float v = 0.f;
+        if (real && k < d) {
+            const int64_t i = bj * d + k;
+            v = n > 0 ? acc[t] / W : c_old[i];
+            c_new[i] = v;
+        }
+        if constexpr (PREP) {
+            if (k < DP) {
+                T* out;
+                float* hn;
+                tile_row<T>(blob, row, DP, &out, &hn);
+                const float r = tile_elem<T>(v, out + k);
+                ss = fmaf(r, r, ss);
+            }
+        }
+    }
+    if constexpr (PREP) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (lane == 0) {
+            T* out;
+            float* hn;
+            tile_row<T>(blob, row, DP, &out, &hn);
+            *hn = real ? -0.5f * ss : -INFINITY;
+        }
+    }
+}
+
+hipError_t launch_fold_divide(DType xt, const float* sums, const float* wsum, const float* slot, const float* wslot,
+                              const float* gslot, const float* gwslot, const int32_t* offsets,
+                              const int32_t* counts, const int32_t* short_flag, int64_t npieces, int TW, int64_t B,
+                              int64_t K, int d, int DP, int64_t Kp, const float* c_old, float* c_new, void* blob,
+                              hipStream_t s) {
+    const bool prep = blob != nullptr;
+    const int64_t Kr = prep ? Kp : K;  // rows: padded ones only to write the tile padding
+    const int64_t rows = B * Kr;
+    if (rows == 0) return hipSuccess;
+    const int64_t ng = fold_groups(npieces);
+    dim3 grid((unsigned)((rows + 3) / 4));
+    char* p = (char*)blob;
+#define KM_FD(TT, WW, PP)                                                                                             hipLaunchKernelGGL((k_fold_divide<TT, WW, PP>), grid, dim3(256), 0, s, sums, wsum, slot, wslot, gslot, gwslot,                        offsets, counts, short_flag, npieces, ng, TW, rows, K, Kr, d, DP, c_old, c_new, p)
+#define KM_FD_T(TT)                              if (wsum) {                                      if (prep) KM_FD(TT, true, true);             else KM_FD(TT, true, false);             } else {                                         if (prep) KM_FD(TT, false, true);            else KM_FD(TT, false, false);            }
+    if (xt == DType::F32) { KM_FD_T(float) }
+    else if (xt == DType::F16) { KM_FD_T(_Float16) }
+    else { KM_FD_T(bf16_t) }
+#undef KM_FD_T
+#undef KM_FD
+    return hipGetLastError();
+}
+
 hipError_t launch_divide_prep(DType xt, const float* sums, const float* wsum, const int32_t* counts, int64_t B,
                               int64_t K, int d, int DP, int64_t Kp, const float* c_old, float* c_new, void* blob,
                               hipStream_t s) {

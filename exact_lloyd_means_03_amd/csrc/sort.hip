@@ -2,94 +2,149 @@
 // sort-inverse update (technologypulse.uk "Flash-KMeans" article,
 // bottleneck 2; wispaper.ai "Flash-KMeans" blog, "Sort-Inverse Update").
 // After it, the indices of the points of cluster j form the contiguous
-// segment perm[offsets[j] .. offsets[j+1]); the points themselves are never
-// moved.
+// segment perm[offsets[j] .. offsets[j+1]) in ascending order (a stable
+// sort); the points themselves are never moved.
 //
-// Labels are small integers (< K), so a counting sort replaces the general
-// argsort:
-//   1. k_count   -- each block histograms a chunk of labels in LDS and adds
-//                   its non-zero bins to counts[b][.] (one global atomic per
-//                   non-empty bin per chunk);
-//   2. k_scan    -- exclusive prefix of counts -> offsets, and scatter cursors
-//                   (and, if asked, whether every cluster is short enough for
-//                   the one-segment-per-row-group reduction);
-//   3. k_scatter -- each block re-histograms its chunk, reserves one
-//                   contiguous run per non-empty bin with a single global
-//                   atomic on that bin's cursor, then places its indices in
-//                   the run with LDS atomics.
-// Chunks are large (about one block per CU over the whole job): the global
-// atomics on the cursors of the most popular clusters are serialized by the
-// memory system, so their number, blocks x non-empty bins, is what limits
-// both passes on skewed label distributions.  The scattered 4-byte index
-// stores need no staging: successive stores into a run fill the same cache
-// lines, which are merged in L2 before they reach HBM.
-// Runs of different chunks land in a segment in arrival order, so the order
-// inside a segment is unspecified; the set of indices is exact.
+// Labels are small integers (< K <= 32768), so a counting sort replaces the
+// general argsort.  The labels of a problem are cut into chunks of CH
+// consecutive points (CH >= K, about 256 chunks over the job):
+//   1. k_hist     -- each block histograms one chunk in LDS and stores the
+//                    chunk's whole row H[c][0..K) (no atomics in device
+//                    memory).  Inside a Lloyd fit the assignment kernel
+//                    builds H itself while it writes the labels, and this
+//                    pass is skipped.
+//   2. k_colscan  -- per bin, the exclusive prefix of H over the chunks ->
+//                    P[c][j] (the points of bin j in chunks before c), and
+//                    the column totals -> counts; H is cleared for the next
+//                    assignment that builds it.
+//   3. k_scan     -- exclusive prefix of counts -> offsets (and the first
+//                    segment of every reduction piece, and whether every
+//                    cluster is short enough for the one-segment-per-group
+//                    reduction).
+//   4. k_scatter  -- chunk c places its points of bin j from
+//                    offsets[j] + P[c][j] on, in index order: each wave of
+//                    the block takes a consecutive part of the chunk with its
+//                    own cursor per bin in LDS (the wave's histogram gives
+//                    the bases of the waves after it), and walks its part 64
+//                    labels at a time; lanes holding the same label find each
+//                    other with one ballot per label bit, the lower lanes
+//                    going first, and the lowest lane of each label advances
+//                    the cursor.
+// Every step is a deterministic function of the labels, so the whole sort
+// is: run twice on the same labels, it produces the same permutation.
 //
-// Few labels per cluster (N <= 16 K, as in a mini-batch against many
-// clusters) would leave the chunked passes with a handful of blocks, each
-// walking all K bins with a chain of dependent atomics.  There every label
-// takes its own global atomic instead (k_count_direct, k_scatter_direct),
-// one thread per label over the whole grid.
+// Few labels per cluster (a mini-batch against many clusters) can take an
+// unordered variant instead, where every label takes one global atomic
+// (k_count_direct, k_scatter_direct); its segments hold the right indices in
+// arrival order.
 // Labels outside [0, K) are skipped by every pass.
 #include "common.h"
 
 namespace km {
 
-constexpr int kSortThreads = 512;
+constexpr int kHistThreads = 512;
 
-// Labels per block: at least 4096 and K, doubled until the whole job takes
-// about 256 blocks.
-static int64_t sort_chunk(int64_t B, int64_t N, int64_t K) {
+// Labels per chunk: a power of two, at least 4096 and K, doubled until the
+// whole job takes at most 256 chunks (or one chunk per problem).  A chunk is
+// a whole number of every assignment point group (those hold 128..512
+// points), so the assignment can add a group's labels to its chunk's row.
+int64_t sort_chunk(int64_t B, int64_t N, int64_t K) {
     int64_t ch = 4096;
     while (ch < K) ch *= 2;
     while (ch < N && B * ((N + ch - 1) / ch) > 256) ch *= 2;
     return ch;
 }
 
-__device__ __forceinline__ void lds_histogram(const int32_t* __restrict__ L, int64_t i0, int64_t i1,
-                                              int K, int32_t* s_h) {
+int64_t sort_chunks(int64_t B, int64_t N, int64_t K) {
+    const int64_t ch = sort_chunk(B, N, K);
+    return N > 0 ? (N + ch - 1) / ch : 1;
+}
+
+// One block per (chunk, problem): LDS histogram of the chunk's labels, then
+// the whole row of K bins stored to H.
+__global__ __launch_bounds__(kHistThreads) void k_hist(const int32_t* __restrict__ labels, int64_t N, int K,
+                                                       int64_t CH, int64_t nch, int32_t* __restrict__ H) {
+    extern __shared__ int32_t s_h[];
     const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y, c = blockIdx.x;
+    const int64_t i0 = c * CH;
+    const int64_t i1 = (i0 + CH < N) ? i0 + CH : N;
+    const int32_t* L = labels + b * N;
+    for (int j = tid; j < K; j += kHistThreads) s_h[j] = 0;
+    __syncthreads();
     int64_t i = i0 + tid;
-    for (; i + 3 * kSortThreads < i1; i += 4 * kSortThreads) {
-        const int32_t l0 = L[i], l1 = L[i + kSortThreads], l2 = L[i + 2 * kSortThreads],
-                      l3 = L[i + 3 * kSortThreads];
+    for (; i + 3 * kHistThreads < i1; i += 4 * kHistThreads) {
+        const int32_t l0 = L[i], l1 = L[i + kHistThreads], l2 = L[i + 2 * kHistThreads],
+                      l3 = L[i + 3 * kHistThreads];
         if ((uint32_t)l0 < (uint32_t)K) atomicAdd(&s_h[l0], 1);
         if ((uint32_t)l1 < (uint32_t)K) atomicAdd(&s_h[l1], 1);
         if ((uint32_t)l2 < (uint32_t)K) atomicAdd(&s_h[l2], 1);
         if ((uint32_t)l3 < (uint32_t)K) atomicAdd(&s_h[l3], 1);
     }
-    for (; i < i1; i += kSortThreads) {
+    for (; i < i1; i += kHistThreads) {
         const int32_t l = L[i];
         if ((uint32_t)l < (uint32_t)K) atomicAdd(&s_h[l], 1);
     }
+    __syncthreads();
+    int32_t* row = H + (b * nch + c) * (int64_t)K;
+    for (int j = tid; j < K; j += kHistThreads) row[j] = s_h[j];
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_count(const int32_t* __restrict__ labels, int64_t N,
-                                                        int K, int64_t CH, int32_t* __restrict__ counts) {
-    extern __shared__ int32_t s_h[];
-    const int tid = threadIdx.x;
+// Column prefix of H.  A block takes 64 consecutive bins of one problem; its
+// 16 lane groups split the chunks into 16 consecutive ranges (at most 16
+// chunks each: nch <= 256).  Each thread keeps its range's counts in
+// registers, the range totals are combined in LDS in chunk order, and every
+// entry gets the count of its bin in all earlier chunks.  clear: store zeros
+// back to H (the assignment of the next iteration adds into it).
+constexpr int kColBins = 64, kColQ = 16, kColMaxPer = 16;
+
+__global__ __launch_bounds__(kColBins* kColQ) void k_colscan(int32_t* __restrict__ H, int64_t nch, int K,
+                                                             int32_t* __restrict__ P, int32_t* __restrict__ counts,
+                                                             bool clear) {
+    __shared__ int32_t s_tot[kColQ][kColBins];
+    const int jl = threadIdx.x % kColBins, q = threadIdx.x / kColBins;
     const int64_t b = blockIdx.y;
-    const int64_t i0 = (int64_t)blockIdx.x * CH;
-    const int64_t i1 = (i0 + CH < N) ? i0 + CH : N;
-    for (int j = tid; j < K; j += kSortThreads) s_h[j] = 0;
-    __syncthreads();
-    lds_histogram(labels + b * N, i0, i1, K, s_h);
-    __syncthreads();
-    for (int j = tid; j < K; j += kSortThreads) {
-        const int32_t v = s_h[j];
-        if (v) atomicAdd(&counts[b * K + j], v);
+    const int j = blockIdx.x * kColBins + jl;
+    const int64_t per = (nch + kColQ - 1) / kColQ;  // <= kColMaxPer
+    const int64_t c0 = q * per;
+    int32_t v[kColMaxPer];
+    int32_t tot = 0;
+#pragma unroll
+    for (int u = 0; u < kColMaxPer; ++u) {
+        const int64_t c = c0 + u;
+        v[u] = (u < per && c < nch && j < K) ? H[(b * nch + c) * K + j] : 0;
+        tot += v[u];
     }
+    s_tot[q][jl] = tot;
+    __syncthreads();
+    int32_t run = 0, all = 0;
+#pragma unroll
+    for (int r = 0; r < kColQ; ++r) {
+        const int32_t t = s_tot[r][jl];
+        run += r < q ? t : 0;
+        all += t;
+    }
+    if (j >= K) return;
+#pragma unroll
+    for (int u = 0; u < kColMaxPer; ++u) {
+        const int64_t c = c0 + u;
+        if (u < per && c < nch) {
+            P[(b * nch + c) * K + j] = run;
+            if (clear) H[(b * nch + c) * K + j] = 0;
+            run += v[u];
+        }
+    }
+    if (q == 0) counts[b * K + j] = all;
 }
 
-// One block per batch: exclusive scan of K counts -> offsets and scatter
-// cursors.  The counts are staged in LDS with coalesced loads, eight in
-// flight per thread, and zero-padded to Kpad (a multiple of 4096).  Each
-// thread then scans a contiguous run of Kpad / 1024 bins with 16-byte LDS
-// accesses, and the run totals are scanned with wave shuffles and the 16
-// wave totals: one shuffle scan for the whole row.  When piece_seg is given
-// it also records, for every reduction piece of TW sorted rows, the segment
-// its first row falls in (binary search over the offsets in LDS).
+// One block per problem: exclusive scan of K counts -> offsets.  The counts
+// are staged in LDS with coalesced loads, eight in flight per thread, and
+// zero-padded to Kpad (a multiple of 4096).  Each thread then scans a
+// contiguous run of Kpad / 1024 bins with 16-byte LDS accesses, and the run
+// totals are scanned with wave shuffles and the 16 wave totals: one shuffle
+// scan for the whole row.  When piece_seg is given it also records, for
+// every reduction piece of TW sorted rows, the segment its first row falls
+// in (binary search over the offsets in LDS).
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 static int64_t scan_kpad(int64_t K) { return (K + 4095) / 4096 * 4096; }
@@ -170,7 +225,8 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
     if (tid == 0) s_off[K] = total;
     __syncthreads();
     for (int j = tid; j <= K; j += 1024) offsets[b * (K + 1) + j] = s_off[j];
-    for (int j = tid; j < K; j += 1024) cursor[b * K + j] = s_off[j];
+    if (cursor)
+        for (int j = tid; j < K; j += 1024) cursor[b * K + j] = s_off[j];
     if (!piece_seg) return;
     // first segment of each piece that holds rows: the last j with offsets[j] <= p * TW
     for (int64_t p = tid; p < npieces && p * TW < total; p += 1024) {
@@ -185,44 +241,81 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
     }
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_scatter(const int32_t* __restrict__ labels, int64_t N,
-                                                          int K, int64_t CH, int32_t* __restrict__ cursor,
-                                                          int32_t* __restrict__ perm) {
-    extern __shared__ int32_t s_h[];
-    const int tid = threadIdx.x;
-    const int64_t b = blockIdx.y;
-    const int64_t i0 = (int64_t)blockIdx.x * CH;
+// One block per (chunk, problem), WB waves; wave w takes the w-th of WB
+// consecutive parts of the chunk.  LDS: WB cursor tables of K bins.
+constexpr int kScatterU = 4;  // rounds of labels loaded ahead
+
+template <int WB>
+__global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__ labels, int64_t N, int K,
+                                                     int nbits, int64_t CH, int64_t nch,
+                                                     const int32_t* __restrict__ P,
+                                                     const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm) {
+    extern __shared__ int32_t s_tab[];  // [WB][K]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t b = blockIdx.y, c = blockIdx.x;
+    const int64_t i0 = c * CH;
     const int64_t i1 = (i0 + CH < N) ? i0 + CH : N;
+    const int64_t part = ((i1 - i0 + WB - 1) / WB + 63) / 64 * 64;  // whole rounds per wave
+    const int64_t w0 = i0 + w * part;
+    const int64_t w1 = (w0 + part < i1) ? w0 + part : i1;
     const int32_t* L = labels + b * N;
-    for (int j = tid; j < K; j += kSortThreads) s_h[j] = 0;
-    __syncthreads();
-    lds_histogram(L, i0, i1, K, s_h);
-    __syncthreads();
-    // reserve this chunk's run in every non-empty segment
-    for (int j = tid; j < K; j += kSortThreads) {
-        const int32_t v = s_h[j];
-        if (v) s_h[j] = atomicAdd(&cursor[b * K + j], v);
+    int32_t* tab = s_tab + w * K;
+    for (int j = lane; j < K; j += 64) tab[j] = 0;
+    __builtin_amdgcn_wave_barrier();
+    // this wave's histogram
+    for (int64_t i = w0 + lane; i < w1; i += 64) {
+        const int32_t l = L[i];
+        if ((uint32_t)l < (uint32_t)K) atomicAdd(&tab[l], 1);
     }
     __syncthreads();
-    int32_t* P = perm + b * N;
-    auto place = [&](int64_t i, int32_t l) {
-        if ((uint32_t)l < (uint32_t)K) P[atomicAdd(&s_h[l], 1)] = (int32_t)i;
-    };
-    int64_t i = i0 + tid;
-    for (; i + 3 * kSortThreads < i1; i += 4 * kSortThreads) {  // 4 labels in flight
-        const int32_t l0 = L[i], l1 = L[i + kSortThreads], l2 = L[i + 2 * kSortThreads],
-                      l3 = L[i + 3 * kSortThreads];
-        place(i, l0);
-        place(i + kSortThreads, l1);
-        place(i + 2 * kSortThreads, l2);
-        place(i + 3 * kSortThreads, l3);
+    // cursor of bin j for wave w: where the chunk's points of bin j start,
+    // plus those of the earlier waves
+    const int32_t* Pc = P + (b * nch + c) * (int64_t)K;
+    const int32_t* ob = offsets + b * (K + 1);
+    for (int j = tid; j < K; j += 64 * WB) {
+        int32_t base = ob[j] + Pc[j];
+#pragma unroll
+        for (int v = 0; v < WB; ++v) {
+            const int32_t t = s_tab[v * K + j];
+            s_tab[v * K + j] = base;
+            base += t;
+        }
     }
-    for (; i < i1; i += kSortThreads) place(i, L[i]);
+    __syncthreads();
+    int32_t* Pb = perm + b * N;
+    int32_t nxt[kScatterU];
+#pragma unroll
+    for (int u = 0; u < kScatterU; ++u) {
+        const int64_t i = w0 + u * 64 + lane;
+        nxt[u] = i < w1 ? L[i] : -1;
+    }
+    for (int64_t r0 = w0; r0 < w1; r0 += 64 * kScatterU) {
+        int32_t cur[kScatterU];
+#pragma unroll
+        for (int u = 0; u < kScatterU; ++u) {
+            cur[u] = nxt[u];
+            const int64_t i = r0 + (u + kScatterU) * 64 + lane;
+            nxt[u] = i < w1 ? L[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kScatterU; ++u) {
+            const int32_t l = cur[u];
+            const bool ok = (uint32_t)l < (uint32_t)K;
+            const uint64_t m = lanes_matching(l, nbits, ok);
+            if (ok) {
+                const int rank = lanes_below(m);
+                const int32_t base = tab[l];
+                Pb[base + rank] = (int32_t)(r0 + u * 64 + lane);
+                if (rank == 0) tab[l] = base + (int32_t)__popcll(m);
+            }
+        }
+    }
 }
 
+// Unordered variant: one global atomic per label (counts must be zero on
+// entry unless already counted).
 constexpr int kDirectThreads = 256;
-
-static bool sort_direct(int64_t N, int64_t K) { return N <= 16 * K; }
 
 __global__ __launch_bounds__(kDirectThreads) void k_count_direct(const int32_t* __restrict__ labels, int64_t N,
                                                                  int K, int32_t* __restrict__ counts) {
@@ -248,41 +341,83 @@ static hipError_t set_lds(const void* f, size_t bytes) {
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts,
-                       int32_t* offsets, int32_t* cursor, int32_t* perm, int TW, int64_t npieces,
-                       int32_t* piece_seg, int32_t* short_flag, hipStream_t s, bool counted) {
-    // counts must be zero on entry (the caller clears it with the other accumulators)
-    if (B == 0) return hipSuccess;
-    const size_t lds = (size_t)K * sizeof(int32_t);
+// Waves per scatter block: as many K-bin cursor tables as fit in 128 KB of LDS, up to 8.
+static int scatter_waves(int64_t K) {
+    int wb = 8;
+    while (wb > 1 && (int64_t)wb * K * 4 > 128 * 1024) wb /= 2;
+    return wb;
+}
+
+static hipError_t launch_scan(const int32_t* counts, int64_t B, int64_t K, int32_t* offsets, int32_t* cursor,
+                              int TW, int64_t npieces, int32_t* piece_seg, int32_t* short_flag, hipStream_t s) {
     hipError_t e;
-    const bool direct = sort_direct(N, K);
-    const dim3 dgrid((unsigned)((N + kDirectThreads - 1) / kDirectThreads), (unsigned)B);
-    if (N > 0 && direct && !counted) {
-        hipLaunchKernelGGL(k_count_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, counts);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else if (N > 0 && !counted) {
-        if ((e = set_lds((const void*)k_count, lds)) != hipSuccess) return e;
-        const int64_t CH = sort_chunk(B, N, K);
-        dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
-        hipLaunchKernelGGL(k_count, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, counts);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     const size_t scan_lds = (size_t)(scan_kpad(K) + 1) * sizeof(int32_t);
     if ((e = set_lds((const void*)k_scan, scan_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(1024), scan_lds, s, counts, (int)K, offsets, cursor, TW,
                        npieces, piece_seg, short_flag);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (N > 0 && direct) {
-        hipLaunchKernelGGL(k_scatter_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, cursor, perm);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else if (N > 0) {
-        if ((e = set_lds((const void*)k_scatter, lds)) != hipSuccess) return e;
-        const int64_t CH = sort_chunk(B, N, K);
-        dim3 grid((unsigned)((N + CH - 1) / CH), (unsigned)B);
-        hipLaunchKernelGGL(k_scatter, grid, dim3(kSortThreads), lds, s, labels, N, (int)K, CH, cursor, perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, const SortBufs& o, int TW,
+                       int64_t npieces, hipStream_t s, SortMode mode) {
+    if (B == 0) return hipSuccess;
+    hipError_t e;
+    if (mode == SortMode::Direct || mode == SortMode::DirectCounted) {
+        // counts must be zero on entry unless the labels were already counted
+        const dim3 dgrid((unsigned)((N + kDirectThreads - 1) / kDirectThreads), (unsigned)B);
+        if (N > 0 && mode == SortMode::Direct) {
+            hipLaunchKernelGGL(k_count_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, o.counts);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if ((e = launch_scan(o.counts, B, K, o.offsets, o.cursor, TW, npieces, o.piece_seg, o.short_flag, s)) !=
+            hipSuccess)
+            return e;
+        if (N > 0) {
+            hipLaunchKernelGGL(k_scatter_direct, dgrid, dim3(kDirectThreads), 0, s, labels, N, (int)K, o.cursor,
+                               o.perm);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const int64_t CH = sort_chunk(B, N, K), nch = sort_chunks(B, N, K);
+    if (mode == SortMode::Stable && N > 0) {
+        const size_t lds = (size_t)K * sizeof(int32_t);
+        if ((e = set_lds((const void*)k_hist, lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_hist, dim3((unsigned)nch, (unsigned)B), dim3(kHistThreads), lds, s, labels, N, (int)K,
+                           CH, nch, o.hist);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return hipSuccess;
+    // StableCounted with N == 0: the rows are zero already
+    if (N > 0) {
+        hipLaunchKernelGGL(k_colscan, dim3((unsigned)((K + kColBins - 1) / kColBins), (unsigned)B),
+                           dim3(kColBins * kColQ), 0, s, o.hist, nch, (int)K, o.prefix, o.counts,
+                           mode == SortMode::StableCounted);
+    } else {
+        e = launch_zero(o.counts, (size_t)B * K * sizeof(int32_t), s);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_scan(o.counts, B, K, o.offsets, nullptr, TW, npieces, o.piece_seg, o.short_flag, s)) !=
+        hipSuccess)
+        return e;
+    if (N == 0) return hipSuccess;
+    const int nbits = label_bits(K);
+    const int wb = scatter_waves(K);
+    const size_t lds = (size_t)wb * K * sizeof(int32_t);
+    const dim3 grid((unsigned)nch, (unsigned)B);
+#define KM_SCATTER(WBV)                                                                                       \
+    do {                                                                                                      \
+        if ((e = set_lds((const void*)k_scatter<WBV>, lds)) != hipSuccess) return e;                         \
+        hipLaunchKernelGGL(k_scatter<WBV>, grid, dim3(64 * WBV), lds, s, labels, N, (int)K, nbits, CH, nch,   \
+                           o.prefix, o.offsets, o.perm);                                                      \
+    } while (0)
+    switch (wb) {
+        case 8: KM_SCATTER(8); break;
+        case 4: KM_SCATTER(4); break;
+        case 2: KM_SCATTER(2); break;
+        default: KM_SCATTER(1); break;
+    }
+#undef KM_SCATTER
+    return hipGetLastError();
 }
 
 }  // namespace km

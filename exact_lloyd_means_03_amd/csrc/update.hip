@@ -125,6 +125,10 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
         j = wbase + l - 1;
         return __shfl(win, l, 64);
     };
+    // whether the piece's first segment began in an earlier piece (then its
+    // part here goes to the piece's slot); one that begins exactly at the
+    // piece's first row is stored directly, like any later segment
+    const bool cont = offb[piece_seg[b * npieces + piece]] < (int32_t)q0;
 
     float acc[EPL];
 #pragma unroll
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
             for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
             if constexpr (WEIGHTED) wacc += __shfl_xor(wacc, o, 64);
         }
-        if (first) {  // the piece's first segment goes to its private slot
+        if (first && cont) {  // a segment begun earlier: its part goes to the piece's slot
             float* sp = slot + (b * npieces + piece) * (int64_t)d;
             if (gl == 0 && active) {
 #pragma unroll
@@ -149,12 +153,11 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
             if constexpr (WEIGHTED) {
                 if (lane == 0) wslot[b * npieces + piece] = wacc;
             }
-            first = false;
         } else {
-            // a segment that starts inside this piece: no other piece writes
-            // it directly (later pieces hold its rest in their slots, which
-            // the fold adds after this launch), so a plain store suffices,
-            // unless the sums carry earlier launches' contributions
+            // a segment that starts in this piece: no other piece writes it
+            // directly (later pieces hold its rest in their slots, which the
+            // fold adds after this launch), so a plain store suffices, unless
+            // the sums carry earlier launches' contributions
             float* sj = sums + (b * K + j) * (int64_t)d;
             if (gl == 0 && active) {
 #pragma unroll
@@ -173,6 +176,7 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                 }
             }
         }
+        first = false;
 #pragma unroll
         for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
         wacc = 0.f;
@@ -252,8 +256,11 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
 // sorted order, so the pieces that share a first segment are consecutive;
 // each wave walks kFoldG of them and issues one atomic per coordinate per
 // segment change, so even a segment that spans thousands of pieces receives
-// only (its pieces / kFoldG) atomic flushes.
-constexpr int kFoldG = 16;
+// only (its pieces / kFoldG) atomic flushes.  The order of those atomics
+// varies from run to run; this fold serves the sums that accumulate over
+// several launches and the mini-batch steps, the Lloyd update folds
+// deterministically (k_fold_groups, then the divide).
+int64_t fold_groups(int64_t npieces) { return (npieces + kFoldG - 1) / kFoldG; }
 
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ slot, const float* __restrict__ wslot,
@@ -295,8 +302,12 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t p = pb + u;
-            const bool ok = p < p1;
-            sg[u] = ok ? ps[p] : -1;
+            bool ok = p < p1;
+            const int sgp = ok ? ps[p] : 0;
+            // a piece whose first segment starts at its first row stored it
+            // directly: no slot
+            ok = ok && offsets[b * (K + 1) + sgp] < (int32_t)(p * TW);
+            sg[u] = ok ? sgp : -1;
             const float* sp = slot + (b * npieces + (ok ? p : p0)) * (int64_t)d;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -319,6 +330,78 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
         }
     }
     flush();
+}
+
+// Deterministic fold (sums that do not accumulate over launches): instead of
+// atomics, the slots of a segment are added in piece order by the divide.  A
+// segment spanning many pieces would make that a long serial walk, so this
+// pass first adds, for every group of kFoldG consecutive pieces, the slots of
+// the group's first run (its first piece and the following ones that share
+// that piece's segment), in piece order, into the group's own slot.  The
+// divide then adds at most kFoldG piece slots and one group slot per further
+// group.  A group whose first piece starts a segment holds no slot there and
+// stores nothing (no segment reads it).
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void k_fold_groups(const float* __restrict__ slot, const float* __restrict__ wslot,
+                                                     const int32_t* __restrict__ piece_seg,
+                                                     const int32_t* __restrict__ offsets, int64_t npieces,
+                                                     int64_t ngroups, int K, int TW, int d,
+                                                     float* __restrict__ gslot, float* __restrict__ gwslot,
+                                                     const int32_t* __restrict__ skip) {
+    constexpr int U = 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t b = blockIdx.y;
+    if (g >= ngroups) return;
+    if (skip && skip[b]) return;  // reduced by k_segsum_short
+    const int32_t* offb = offsets + b * (K + 1);
+    const int32_t total = offb[K];
+    const int64_t np = ((int64_t)total + TW - 1) / TW;  // pieces that hold rows
+    const int64_t p0 = g * kFoldG;
+    if (p0 >= np) return;
+    const int32_t* ps = piece_seg + b * npieces;
+    const int s0 = ps[p0];
+    if (offb[s0] >= (int32_t)(p0 * TW)) return;  // the group's first piece starts a segment
+    const int64_t pe = (p0 + kFoldG < np) ? p0 + kFoldG : np;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // columns lane + 64 t (d <= 512)
+    float wacc = 0.f;
+    bool more = true;
+    for (int64_t pb = p0; pb < pe && more; pb += U) {
+        float v[U][8];
+        float wv[U];
+        bool in[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = pb + u;
+            in[u] = p < pe && ps[p < pe ? p : p0] == s0;
+            const float* sp = slot + (b * npieces + (in[u] ? p : p0)) * (int64_t)d;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int k = lane + 64 * t;
+                v[u][t] = (in[u] && k < d) ? sp[k] : 0.f;
+            }
+            wv[u] = (WEIGHTED && in[u]) ? wslot[b * npieces + p] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (in[u]) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[t] += v[u][t];
+                wacc += wv[u];
+            } else {
+                more = false;
+            }
+        }
+    }
+    float* gp = gslot + (b * ngroups + g) * (int64_t)d;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int k = lane + 64 * t;
+        if (k < d) gp[k] = acc[t];
+    }
+    if constexpr (WEIGHTED) {
+        if (lane == 0) gwslot[b * ngroups + g] = wacc;
+    }
 }
 
 // Rows per wave piece: enough pieces to fill the chip, and long pieces when
@@ -425,17 +508,18 @@ int segreduce_tw(int64_t B, int64_t N) {
 // piece_seg: the first segment of every piece, written by the scan of the sort.
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
-                            float* wsum, const int32_t* piece_seg, float* slot, float* wslot,
-                            const int32_t* short_flag, hipStream_t s) {
-    return launch_segreduce_tw(xt, x, w, B, N, d, perm, offsets, K, sums, wsum, piece_seg, slot, wslot,
-                               segreduce_tw(B, N), false, short_flag, s);
+                            float* wsum, const int32_t* piece_seg, float* slot, float* wslot, float* gslot,
+                            float* gwslot, const int32_t* short_flag, hipStream_t s) {
+    return launch_segreduce_tw(xt, x, w, B, N, d, perm, offsets, K, sums, wsum, piece_seg, slot, wslot, gslot,
+                               gwslot, segreduce_tw(B, N), false, short_flag, s);
 }
 
 hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                                const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
-                               float* wsum, const int32_t* piece_seg, float* slot, float* wslot, int TW,
-                               bool accumulate, const int32_t* short_flag, hipStream_t s) {
+                               float* wsum, const int32_t* piece_seg, float* slot, float* wslot, float* gslot,
+                               float* gwslot, int TW, bool accumulate, const int32_t* short_flag, hipStream_t s) {
     if (B == 0 || N == 0) return hipSuccess;
+    if (accumulate) gslot = nullptr;
     // short segments on average: try the one-segment-per-row-group kernel
     // (it runs where the sort found every cluster short; the piece kernels
     // run elsewhere)
@@ -489,6 +573,16 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 fgrid((unsigned)((npieces + 4 * kFoldG - 1) / (4 * kFoldG)), (unsigned)B);
+    if (gslot) {
+        const int64_t ng = fold_groups(npieces);
+        if (w)
+            hipLaunchKernelGGL(k_fold_groups<true>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
+                               ng, (int)K, TW, d, gslot, gwslot, skip);
+        else
+            hipLaunchKernelGGL(k_fold_groups<false>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets,
+                               npieces, ng, (int)K, TW, d, gslot, gwslot, skip);
+        return hipGetLastError();
+    }
     if (w)
         hipLaunchKernelGGL(k_fold_slots<true>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
                            (int)K, TW, d, sums, wsum, skip);

@@ -12,13 +12,15 @@
  *     memory (same article, "bottleneck 1"; wispaper.ai "Flash-KMeans" blog,
  *     "FlashAssign: Materialization-Free Assignment").  Scalar points (d = 1)
  *     take a binary search over the sorted centroids instead.
- *   - update: the label vector is argsorted by cluster id so that each cluster
- *     is a contiguous segment, and every segment is reduced on chip and
- *     stored once; only the pieces of a cluster that spans several reduction
- *     pieces are combined with a few atomic adds per coordinate, instead of
- *     one per point.  The point matrix is never permuted in memory
+ *   - update: the label vector is argsorted by cluster id (a stable
+ *     counting sort) so that each cluster is a contiguous segment, and every
+ *     segment is reduced on chip and stored once; the pieces of a cluster
+ *     that spans several reduction pieces are added in a fixed order by the
+ *     divide, instead of one scattered atomic per point and coordinate.
+ *     The point matrix is never permuted in memory
  *     (technologypulse.uk article, "bottleneck 2"; wispaper.ai blog,
- *     "Sort-Inverse Update").  The new centroid is the mean
+ *     "Sort-Inverse Update").  Inside a fit, the assignment also counts its
+ *     labels for the sort.  The new centroid is the mean
  *     of its points (daily.steinslab.io "e-means" article, "Breaking 70 Years
  *     of Full-Batch Inertia": centroid = S_j / N_j); a cluster with no points
  *     keeps its previous centroid.
@@ -104,8 +106,9 @@ KM_API km_status kmeans_assign(const void *x, km_dtype xt, int64_t B, int64_t N,
  *   offsets  out [B,K+1] int32: exclusive prefix of counts; offsets[b][K] is
  *            the number of labelled points.
  *   perm     out [B,N] int32: perm[b][offsets[b][j] .. offsets[b][j+1]) are
- *            the indices i of batch b with labels[b][i] == j, in an
- *            unspecified order; entries from offsets[b][K] on are not written.
+ *            the indices i of batch b with labels[b][i] == j, in ascending
+ *            order (a stable sort: the result is unique); entries from
+ *            offsets[b][K] on are not written.
  * May be NULL: none of counts / offsets / perm (they then live in the
  * workspace, which makes the call a no-op for the caller). */
 KM_API km_status kmeans_sort_labels(const int32_t *labels, int64_t B, int64_t N, int64_t K,
@@ -123,7 +126,10 @@ KM_API km_status kmeans_update(const void *x, km_dtype xt, const float *weights,
                         const float *c_old, float *c_new, int32_t *counts,
                         void *workspace, size_t workspace_bytes, km_stream stream);
 
-/* n_iter Lloyd iterations (assignment, then update) from init.
+/* n_iter Lloyd iterations (assignment, then update) from init.  For d >= 2
+ * the result is a deterministic function of the inputs: two calls on the
+ * same inputs give bit-identical outputs (no floating-point atomics on this
+ * path).
  *   init       [B,K,d] float32 (may alias centroids).
  *   centroids  out [B,K,d] float32: after the last update.
  *   labels     out [B,N] int32 or NULL: the last assignment.
@@ -137,6 +143,26 @@ KM_API km_status kmeans_fit(const void *x, km_dtype xt, const float *weights,
                      const float *init, int32_t n_iter,
                      float *centroids, int32_t *labels, int32_t *counts, double *objective,
                      void *workspace, size_t workspace_bytes, km_stream stream);
+
+/* kmeans_fit that also times the assignment stage of every iteration with
+ * the caller's events (the assignment stage dominates an iteration:
+ * technologypulse.uk "Flash-KMeans" article, "bottleneck 1").
+ *   assign_events  2 * n_iter hipEvent_t handles, created by the caller
+ *                  (with timing enabled to read durations): assign_events[2t]
+ *                  is recorded on `stream` right before the assignment
+ *                  kernels of iteration t are launched (after the centroid
+ *                  prep), assign_events[2t + 1] right after them (before the
+ *                  objective reduction and the update).  Where all
+ *                  iterations run in one launch (scalar rows that fit on
+ *                  chip), every even event is recorded before that launch
+ *                  and every odd one after it.
+ * The rest is kmeans_fit.  KM_EINVAL if any handle is NULL. */
+KM_API km_status kmeans_fit_timed(const void *x, km_dtype xt, const float *weights,
+                           int64_t B, int64_t N, int64_t d, int64_t K,
+                           const float *init, int32_t n_iter,
+                           float *centroids, int32_t *labels, int32_t *counts, double *objective,
+                           void *const *assign_events,
+                           void *workspace, size_t workspace_bytes, km_stream stream);
 
 /* Lloyd fit of one problem whose points stay in host memory
  * (technologypulse.uk "Flash-KMeans" article, performance section:

@@ -8,14 +8,25 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "lloyd_oracle.c")
-LIB = os.path.join(HERE, "liblloyd_oracle.so")
+# KM_SANITIZE=1: built with clang's AddressSanitizer and
+# UndefinedBehaviorSanitizer (the runtime the sanitized HIP host code uses)
+# into _build_san/; the tests load it when KM_ORACLE_LIBRARY names it.
+SANITIZE = os.environ.get("KM_SANITIZE", "") == "1"
+LIB = os.path.join(HERE, "_build_san", "liblloyd_oracle.so") if SANITIZE else os.path.join(HERE, "liblloyd_oracle.so")
+CLANG = "/opt/rocm/llvm/bin/clang"
 
 
 def compile_source(src: str, out: str, verbose: bool = False) -> str:
     """Compile an oracle C source into the shared library `out`."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
-           "-shared", "-fPIC", src, "-o", tmp, "-lm"]
+    if SANITIZE and out == LIB:
+        cmd = [CLANG, "-O1", "-g", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+               "-shared", "-fPIC", src, "-o", tmp, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+               "-shared", "-fPIC", src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

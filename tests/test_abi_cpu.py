@@ -186,3 +186,15 @@ def test_emeans_rejects(lib):
     assert call(xt=5) == 2
     assert call(ws_bytes=64) == 3
     assert call(ws=C.c_void_p(0x100010)) == 1
+
+
+def test_fit_timed_rejects(lib):
+    ws = C.c_void_p(0x100000)
+    ev = (C.c_void_p * 4)(0x10, 0x20, 0x30, 0x40)
+    call = lambda events, n_iter=2, ws_bytes=1 << 30: lib.kmeans_fit_timed(  # noqa: E731
+        FAKE, 1, None, 1, 10, 8, 4, FAKE, n_iter, FAKE, None, None, None, events, ws, ws_bytes, None)
+    assert call(None) == 1 and b"assign_events" in lib.kmeans_last_error()
+    bad = (C.c_void_p * 4)(0x10, 0x20, None, 0x40)
+    assert call(bad) == 1 and b"assign_events[2]" in lib.kmeans_last_error()
+    assert call(ev, n_iter=-1) == 1
+    assert call(ev, ws_bytes=16) == 3

@@ -63,6 +63,18 @@ def test_assign_parity(km, dtype, B, N, d, K):
     _assign_case(km, x, C, what=f"{dtype} B{B} N{N} d{d} K{K}")
 
 
+@pytest.mark.parametrize("dtype,B,N,d,K", [
+    ("f16", 1, 300001, 128, 700), ("bf16", 1, 262147, 96, 513), ("f32", 1, 300001, 128, 300),
+    ("f16", 3, 90001, 256, 257), ("bf16", 2, 150001, 64, 1030),
+])
+def test_assign_parity_persistent_walk(km, dtype, B, N, d, K):
+    """More point groups than the chip holds blocks at once: every block walks
+    several groups (next group's first tile and points loaded during the
+    current group's last tile and output write), checked on every point."""
+    x, C = _rand_problem(B, N, d, K, dtype, seed=N + d + K)
+    _assign_case(km, x, C, what=f"persistent {dtype} B{B} N{N} d{d} K{K}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("K", [1, 2, 8, 16, 100, 1024, 1500, 16384])
 def test_assign_1d_parity(km, dtype, K):
@@ -144,12 +156,29 @@ def test_misaligned_points(km):
 
 def test_sort_labels(km):
     rng = np.random.default_rng(0)
-    for (B, N, K) in [(1, 1, 1), (2, 5000, 7), (1, 70000, 3000), (3, 40000, 16), (1, 100, 5000)]:
+    for (B, N, K) in [(1, 1, 1), (2, 5000, 7), (1, 70000, 3000), (3, 40000, 16), (1, 100, 5000),
+                      # one to eight cursor tables per scatter block, many chunks, ragged tails
+                      (1, 300001, 32768), (2, 200003, 16384), (1, 1 << 20, 8192), (1, 2000003, 4096),
+                      (5, 77777, 1000), (1, 65536, 16384), (1, 4097, 2)]:
         lab = rng.integers(0, K, size=(B, N)).astype(np.int32)
         lab[:, ::97] = -1            # unlabeled points
         lab[:, 5::101] = K + 3       # out of range
         counts, offsets, perm = km.kmeans_sort_labels(torch.from_numpy(lab).cuda(), K)
         parity.check_perm(lab, K, counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy())
+
+
+def test_sort_labels_one_label_and_determinism(km):
+    # every point in one cluster (one segment across all chunks), then a
+    # repeat of a random sort: the same permutation bit for bit
+    for K in (1, 5, 8192):
+        lab = np.full((1, 500000), K - 1, np.int32)
+        counts, offsets, perm = km.kmeans_sort_labels(torch.from_numpy(lab).cuda(), K)
+        parity.check_perm(lab, K, counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy())
+    lab = torch.from_numpy(np.random.default_rng(5).integers(0, 3000, size=(2, 400000)).astype(np.int32)).cuda()
+    a = km.kmeans_sort_labels(lab, 3000)
+    b = km.kmeans_sort_labels(lab, 3000)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
 
 
 def test_sort_labels_skewed(km):
@@ -388,3 +417,29 @@ def test_fit_with_centroid_slices(km):
     X, Chat, lab_ref, d1, d2 = parity.oracle_assign(workloads.raw_bits(x), "bf16", c1.cpu().numpy())
     parity.check_labels(l2.cpu().numpy(), lab_ref, d1, d2, "fit slices it 2")
     parity.check_objective(J2.cpu().numpy()[:, 1], d1.sum(-1), "fit slices it 2")
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("gmm-n1m-k8192-d128-f16", dict(N=200003, K=2048, n_iter=3)),
+    ("zipf-n32m-k4096-d128-bf16", dict(N=1000003, K=512, n_iter=3)),
+    ("gmm-b32-n65536-k1024-d128-f16", dict(B=8, N=30001, K=700, n_iter=3)),
+    ("gmm-n8192-k256-d128-f32", dict(n_iter=4)),
+])
+def test_fit_is_deterministic(km, name, kw):
+    """Two fits of the same inputs give bit-identical centroids, labels,
+    counts and objectives: the label sort is stable, every segment and slot
+    is summed in a fixed order, and the fold adds the slots in piece order
+    (no float atomics on the Lloyd path)."""
+    wl = workloads.small(name, **kw)
+    p = workloads.generate(wl)
+    x, w, init = parity.to_device(p)
+    a = km.kmeans_fit(x, init, wl.n_iter, weights=w)
+    b = km.kmeans_fit(x, init, wl.n_iter, weights=w)
+    torch.cuda.synchronize()
+    for u, v, what in zip(a, b, ("centroids", "labels", "counts", "objective")):
+        assert torch.equal(u, v), f"{name}: {what} differ between two runs"
+    # and a separate update call on the final labels, twice
+    c1, n1 = km.kmeans_update(x, a[1], a[0], weights=w)
+    c2, n2 = km.kmeans_update(x, a[1], a[0], weights=w)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(n1, n2)
