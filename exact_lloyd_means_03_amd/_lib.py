@@ -27,6 +27,8 @@ SIGNATURES = {
     "kmeans_fit": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "kmeans_fit_timed": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p, _p, _sz,
                                    _p]),
+    "kmeans_fit_static_max_bytes": (_sz, []),
+    "kmeans_fit_static": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _p]),
     "kmeans_stream_workspace_bytes": (_sz, [_i64, _i64, _i64, C.c_int, _i64]),
     "kmeans_fit_stream": (C.c_int, [_p, C.c_int, _p, _i64, _i64, _i64, _p, _i32, _p, _p, _p, _p, _i64, _p, _sz,
                                     _p]),

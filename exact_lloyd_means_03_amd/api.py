@@ -180,6 +180,34 @@ def kmeans_fit(x, init, n_iter: int, weights=None, centroids=None, labels=None, 
     return centroids, labels, counts, objective
 
 
+def kmeans_fit_static(x, init, n_iter: int, weights=None, centroids=None, labels=None, counts=None,
+                      objective=None):
+    """kmeans_fit without a workspace: the library's static per-device scratch
+    (kmeans_fit_static_max_bytes() bytes) serves instead, so the call
+    allocates nothing itself (pass every output tensor to allocate nothing
+    here either).  Returns (centroids, labels, counts, objective)."""
+    B, N, d = _points(x)
+    _dev_tensor(init, "init", torch.float32)
+    if init.dim() != 3 or init.shape[0] != B or init.shape[2] != d:
+        raise ValueError("init must be [B, K, d] float32")
+    K = init.shape[1]
+    dev = x.device
+    if weights is not None:
+        _dev_tensor(weights, "weights", torch.float32, (B, N))
+    centroids = torch.empty_like(init) if centroids is None else \
+        _dev_tensor(centroids, "centroids", torch.float32, init.shape)
+    labels = torch.empty((B, N), dtype=torch.int32, device=dev) if labels is None else \
+        _dev_tensor(labels, "labels", torch.int32, (B, N))
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev) if counts is None else \
+        _dev_tensor(counts, "counts", torch.int32, (B, K))
+    objective = torch.empty((B, max(n_iter, 0)), dtype=torch.float64, device=dev) if objective is None else \
+        _dev_tensor(objective, "objective", torch.float64, (B, n_iter))
+    st = _lib.load().kmeans_fit_static(_ptr(x), _DT[x.dtype], _ptr(weights), B, N, d, K, _ptr(init), int(n_iter),
+                                       _ptr(centroids), _ptr(labels), _ptr(counts), _ptr(objective), _stream(dev))
+    _lib.check(st, "kmeans_fit_static")
+    return centroids, labels, counts, objective
+
+
 def kmeans_optimal_1d(x, K: int, weights=None, centroids=None, labels=None, counts=None, objective=None, ws=None):
     """Globally optimal weighted 1D k-means of every row of x [B, N] (or
     [B, N, 1]).  Returns (centroids [B, K] float32 ascending, labels [B, N]

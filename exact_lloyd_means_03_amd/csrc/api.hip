@@ -404,6 +404,36 @@ km_status run_fit(const void* x, int xt, const float* weights, int64_t B, int64_
                   double* objective, const Workspace& W, void* workspace, hipStream_t s,
                   void* const* assign_events = nullptr);
 
+// ---------------------------------------------------------------------------
+// Scratch of kmeans_fit_static: one array per device, in the code object's
+// device memory, so that the entry point needs no allocation.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in symbol): the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+km_status static_scratch(void** out) {
+    int dev = 0;
+    KM_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(KM_EUNSUPPORTED, "kmeans_fit_static: device %d >= %d", dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        KM_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (p == nullptr || (uintptr_t)p % 256 != 0)
+            return fail(KM_EHIP, "kmeans_fit_static: unexpected scratch address %p", p);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,6 +519,24 @@ km_status kmeans_fit_timed(const void* x, km_dtype xt, const float* weights, int
     KM_TRY(check_ws(W, workspace, workspace_bytes));
     return run_fit(x, enum_code(xt), weights, B, N, d, K, init, n_iter, centroids, labels, counts, objective, W,
                    workspace, (hipStream_t)stream, assign_events);
+}
+
+size_t kmeans_fit_static_max_bytes(void) { return kStaticScratchBytes; }
+
+km_status kmeans_fit_static(const void* x, km_dtype xt, const float* weights, int64_t B, int64_t N, int64_t d,
+                            int64_t K, const float* init, int32_t n_iter, float* centroids, int32_t* labels,
+                            int32_t* counts, double* objective, km_stream stream) {
+    KM_TRY(check_fit_args(x, enum_code(xt), B, N, d, K, init, n_iter, centroids));
+    const Workspace W = plan_workspace(B, N, d, K, (DType)enum_code(xt));
+    if (W.total > kStaticScratchBytes)
+        return fail(KM_EWORKSPACE,
+                    "kmeans_fit_static: these shapes need %zu bytes of scratch, more than the library's static "
+                    "%zu bytes (use kmeans_fit with a caller workspace)",
+                    W.total, kStaticScratchBytes);
+    void* ws = nullptr;
+    KM_TRY(static_scratch(&ws));
+    return run_fit(x, enum_code(xt), weights, B, N, d, K, init, n_iter, centroids, labels, counts, objective, W, ws,
+                   (hipStream_t)stream);
 }
 
 }  // extern "C"

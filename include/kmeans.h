@@ -164,6 +164,25 @@ KM_API km_status kmeans_fit_timed(const void *x, km_dtype xt, const float *weigh
                            void *const *assign_events,
                            void *workspace, size_t workspace_bytes, km_stream stream);
 
+/* kmeans_fit for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as kmeans_fit, without the workspace:
+ * the scratch lives in one static device array of
+ * kmeans_fit_static_max_bytes() bytes (64 MiB) per device, held from the
+ * first call on that device until the process ends.  The call allocates and
+ * frees nothing.  Shapes whose kmeans_workspace_bytes() exceeds that size
+ * return KM_EWORKSPACE before anything is enqueued.
+ * Every call on one device uses the same array, and each call clears what
+ * it needs at the start: calls that may overlap in time on one device (on
+ * different streams, or from different threads without ordering) race on
+ * it and must not be issued. */
+KM_API size_t kmeans_fit_static_max_bytes(void);
+KM_API km_status kmeans_fit_static(const void *x, km_dtype xt, const float *weights,
+                            int64_t B, int64_t N, int64_t d, int64_t K,
+                            const float *init, int32_t n_iter,
+                            float *centroids, int32_t *labels, int32_t *counts, double *objective,
+                            km_stream stream);
+
 /* Lloyd fit of one problem whose points stay in host memory
  * (technologypulse.uk "Flash-KMeans" article, performance section:
  * out-of-core runs in which a chunked stream overlap hides the PCIe

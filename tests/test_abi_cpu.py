@@ -188,6 +188,28 @@ def test_emeans_rejects(lib):
     assert call(ws=C.c_void_p(0x100010)) == 1
 
 
+def test_fit_static_rejects_before_any_hip_call(lib):
+    # the static scratch is 64 MiB per device; shapes that need more are
+    # refused on the host, as are invalid arguments
+    assert lib.kmeans_fit_static_max_bytes() == 64 << 20
+
+    def call(**kw):
+        a = dict(x=FAKE, xt=1, B=1, N=1 << 24, d=128, K=4096, init=FAKE, n_iter=2, C=FAKE)
+        a.update(kw)
+        return lib.kmeans_fit_static(a["x"], a["xt"], None, a["B"], a["N"], a["d"], a["K"], a["init"], a["n_iter"],
+                                     a["C"], None, None, None, None)
+
+    assert lib.kmeans_workspace_bytes(1, 1 << 24, 128, 4096, 1) > lib.kmeans_fit_static_max_bytes()
+    assert call() == 3 and b"static" in lib.kmeans_last_error()
+    assert call(x=None) == 1
+    assert call(init=None) == 1
+    assert call(C=None) == 1
+    assert call(n_iter=-1) == 1
+    assert call(K=0) == 1
+    assert call(xt=7) == 2
+    assert call(d=1, K=20000, xt=0) == 2
+
+
 def test_fit_timed_rejects(lib):
     ws = C.c_void_p(0x100000)
     ev = (C.c_void_p * 4)(0x10, 0x20, 0x30, 0x40)
