@@ -77,6 +77,21 @@ __device__ __forceinline__ uint64_t lanes_matching(int32_t v, int nbits, bool ac
     return m;
 }
 
+// The same with the number of bits fixed at compile time (unrolled); bits at
+// or above the values' width are zero in every active lane and change
+// nothing, so NB may exceed it.
+template <int NB>
+__device__ __forceinline__ uint64_t lanes_matching_n(int32_t v, bool active) {
+    uint64_t m = __ballot(active);
+#pragma unroll
+    for (int bit = 0; bit < NB; ++bit) {
+        const bool set = (v >> bit) & 1;
+        const uint64_t s = __ballot(active && set);
+        m &= set ? s : ~s;
+    }
+    return m;
+}
+
 // Set lanes of m below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

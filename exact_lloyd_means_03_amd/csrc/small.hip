@@ -116,14 +116,14 @@ __global__ __launch_bounds__(256) void k_divide_prep(const float* __restrict__ s
 // added in that order; the divide follows (IEEE float32, c_old for an empty
 // cluster).  Problems reduced one segment per row group (skip set) have
 // complete sums and no slots.
-template <typename T, bool WEIGHTED, bool PREP>
+template <typename T, bool WEIGHTED, bool PREP, int DT>
 __global__ __launch_bounds__(256) void k_fold_divide(
     const float* __restrict__ sums, const float* __restrict__ wsum, const float* __restrict__ slot,
     const float* __restrict__ wslot, const float* __restrict__ gslot, const float* __restrict__ gwslot,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts, const int32_t* __restrict__ skip,
     int64_t npieces, int64_t ngroups, int TW, int64_t BKp, int64_t K, int64_t Kp, int d, int DP,
     const float* c_old, float* c_new, char* __restrict__ blob) {
-    constexpr int U = 4;  // slots in flight
+    constexpr int U = 16;  // slots in flight (a cluster of millions of points has ~100 group slots)
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= BKp) return;
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(256) void k_fold_divide(
     const bool real = j < K;
     const int64_t bj = b * K + j;
     const int32_t n = real ? counts[bj] : 0;
-    float acc[8];
+    float acc[DT];  // coordinates lane + 64 t, t < DT (d <= 64 DT)
     float wacc = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < DT; ++t) {
         const int k = lane + 64 * t;
         acc[t] = (n > 0 && k < d) ? sums[bj * d + k] : 0.f;
     }
@@ -147,23 +147,23 @@ __global__ __launch_bounds__(256) void k_fold_divide(
         // piece slots up to the end of the first group, then one group slot per group
         auto add_run = [&](const float* base, const float* wbase, int64_t q0, int64_t q1) {
             for (int64_t q = q0; q <= q1; q += U) {
-                float v[U][8], wv[U];
+                float v[U][DT], wv[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const bool ok = q + u <= q1;
                     const float* sp = base + (ok ? q + u : q0) * (int64_t)d;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
+                    for (int t = 0; t < DT; ++t) {
                         const int k = lane + 64 * t;
                         v[u][t] = (ok && k < d) ? sp[k] : 0.f;
                     }
-                    wv[u] = (WEIGHTED && ok) ? wbase[ok ? q + u : q0] : 0.f;
+                    wv[u] = (WEIGHTED && ok) ? wbase[q + u] : 0.f;
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     if (q + u <= q1) {
 #pragma unroll
-                        for (int t = 0; t < 8; ++t) acc[t] += v[u][t];
+                        for (int t = 0; t < DT; ++t) acc[t] += v[u][t];
                         if constexpr (WEIGHTED) wacc += wv[u];
                     }
                 }
@@ -177,20 +177,20 @@ __global__ __launch_bounds__(256) void k_fold_divide(
     }
     const float W = n > 0 ? (WEIGHTED ? wacc : (float)n) : 1.f;
     float ss = 0.f;
+    T* out = nullptr;
+    float* hn = nullptr;
+    if constexpr (PREP) tile_row<T>(blob, row, DP, &out, &hn);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int k = lane + 64 * t;
         float v = 0.f;
-        if (real && k < d) {
+        if (t < DT && real && k < d) {
             const int64_t i = bj * d + k;
-            v = n > 0 ? acc[t] / W : c_old[i];
+            v = n > 0 ? acc[t < DT ? t : 0] / W : c_old[i];
             c_new[i] = v;
         }
         if constexpr (PREP) {
             if (k < DP) {
-                T* out;
-                float* hn;
-                tile_row<T>(blob, row, DP, &out, &hn);
                 const float r = tile_elem<T>(v, out + k);
                 ss = fmaf(r, r, ss);
             }
@@ -199,12 +199,7 @@ __global__ __launch_bounds__(256) void k_fold_divide(
     if constexpr (PREP) {
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-        if (lane == 0) {
-            T* out;
-            float* hn;
-            tile_row<T>(blob, row, DP, &out, &hn);
-            *hn = real ? -0.5f * ss : -INFINITY;
-        }
+        if (lane == 0) *hn = real ? -0.5f * ss : -INFINITY;
     }
 }
 
@@ -220,12 +215,25 @@ hipError_t launch_fold_divide(DType xt, const float* sums, const float* wsum, co
     const int64_t ng = fold_groups(npieces);
     dim3 grid((unsigned)((rows + 3) / 4));
     char* p = (char*)blob;
-#define KM_FD(TT, WW, PP)                                                                                             hipLaunchKernelGGL((k_fold_divide<TT, WW, PP>), grid, dim3(256), 0, s, sums, wsum, slot, wslot, gslot, gwslot,                        offsets, counts, short_flag, npieces, ng, TW, rows, K, Kr, d, DP, c_old, c_new, p)
-#define KM_FD_T(TT)                              if (wsum) {                                      if (prep) KM_FD(TT, true, true);             else KM_FD(TT, true, false);             } else {                                         if (prep) KM_FD(TT, false, true);            else KM_FD(TT, false, false);            }
+#define KM_FD(TT, WW, PP, DD)                                                                               \
+    hipLaunchKernelGGL((k_fold_divide<TT, WW, PP, DD>), grid, dim3(256), 0, s, sums, wsum, slot, wslot, gslot, \
+                       gwslot, offsets, counts, short_flag, npieces, ng, TW, rows, K, Kr, d, DP, c_old, c_new, p)
+#define KM_FD_D(TT, WW, PP)             \
+    if (d <= 128) KM_FD(TT, WW, PP, 2); \
+    else KM_FD(TT, WW, PP, 8);
+#define KM_FD_T(TT)                           \
+    if (wsum) {                               \
+        if (prep) { KM_FD_D(TT, true, true) } \
+        else { KM_FD_D(TT, true, false) }     \
+    } else {                                  \
+        if (prep) { KM_FD_D(TT, false, true) } \
+        else { KM_FD_D(TT, false, false) }    \
+    }
     if (xt == DType::F32) { KM_FD_T(float) }
     else if (xt == DType::F16) { KM_FD_T(_Float16) }
     else { KM_FD_T(bf16_t) }
 #undef KM_FD_T
+#undef KM_FD_D
 #undef KM_FD
     return hipGetLastError();
 }

@@ -242,15 +242,19 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
 }
 
 // One block per (chunk, problem), WB waves; wave w takes the w-th of WB
-// consecutive parts of the chunk.  LDS: WB cursor tables of K bins.
-constexpr int kScatterU = 4;  // rounds of labels loaded ahead
+// consecutive parts of the chunk.  LDS: WB cursor tables of K bins.  Labels
+// are read kScatterR rounds of 64 at a time, the next batch's loads issued
+// before the current batch is ranked, so the ranking (a chain of LDS reads
+// and writes per round) runs under the loads.
+constexpr int kScatterR = 16;
 
-template <int WB>
+template <int WB, int NB>
 __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__ labels, int64_t N, int K,
-                                                     int nbits, int64_t CH, int64_t nch,
+                                                     int64_t CH, int64_t nch,
                                                      const int32_t* __restrict__ P,
                                                      const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm) {
+    constexpr int R = kScatterR;
     extern __shared__ int32_t s_tab[];  // [WB][K]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t b = blockIdx.y, c = blockIdx.x;
@@ -261,54 +265,74 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     const int64_t w1 = (w0 + part < i1) ? w0 + part : i1;
     const int32_t* L = labels + b * N;
     int32_t* tab = s_tab + w * K;
+    auto load_batch = [&](int64_t r0, int32_t (&v)[R]) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int64_t i = r0 + u * 64 + lane;
+            v[u] = i < w1 ? L[i] : -1;
+        }
+    };
     for (int j = lane; j < K; j += 64) tab[j] = 0;
     __builtin_amdgcn_wave_barrier();
-    // this wave's histogram
-    for (int64_t i = w0 + lane; i < w1; i += 64) {
-        const int32_t l = L[i];
-        if ((uint32_t)l < (uint32_t)K) atomicAdd(&tab[l], 1);
+    // this wave's histogram, R labels in flight per lane
+    for (int64_t r0 = w0; r0 < w1; r0 += 64 * R) {
+        int32_t v[R];
+        load_batch(r0, v);
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+            if ((uint32_t)v[u] < (uint32_t)K) atomicAdd(&tab[v[u]], 1);
     }
     __syncthreads();
     // cursor of bin j for wave w: where the chunk's points of bin j start,
-    // plus those of the earlier waves
+    // plus those of the earlier waves (bins loaded 8 at a time per thread)
     const int32_t* Pc = P + (b * nch + c) * (int64_t)K;
     const int32_t* ob = offsets + b * (K + 1);
-    for (int j = tid; j < K; j += 64 * WB) {
-        int32_t base = ob[j] + Pc[j];
+    constexpr int BU = 8;
+    for (int j0 = tid; j0 < K; j0 += 64 * WB * BU) {
+        int32_t base[BU];
 #pragma unroll
-        for (int v = 0; v < WB; ++v) {
-            const int32_t t = s_tab[v * K + j];
-            s_tab[v * K + j] = base;
-            base += t;
+        for (int e = 0; e < BU; ++e) {
+            const int j = j0 + e * 64 * WB;
+            base[e] = j < K ? ob[j] + Pc[j] : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < BU; ++e) {
+            const int j = j0 + e * 64 * WB;
+            if (j < K) {
+#pragma unroll
+                for (int v = 0; v < WB; ++v) {
+                    const int32_t t = s_tab[v * K + j];
+                    s_tab[v * K + j] = base[e];
+                    base[e] += t;
+                }
+            }
         }
     }
     __syncthreads();
     int32_t* Pb = perm + b * N;
-    int32_t nxt[kScatterU];
+    int32_t nxt[R];
+    load_batch(w0, nxt);
+    for (int64_t r0 = w0; r0 < w1; r0 += 64 * R) {
+        int32_t cur[R];
 #pragma unroll
-    for (int u = 0; u < kScatterU; ++u) {
-        const int64_t i = w0 + u * 64 + lane;
-        nxt[u] = i < w1 ? L[i] : -1;
-    }
-    for (int64_t r0 = w0; r0 < w1; r0 += 64 * kScatterU) {
-        int32_t cur[kScatterU];
+        for (int u = 0; u < R; ++u) cur[u] = nxt[u];
+        load_batch(r0 + 64 * R, nxt);
+        // first every round's grouping (ballots only, no memory) ...
+        int rank[R], cnt[R];
 #pragma unroll
-        for (int u = 0; u < kScatterU; ++u) {
-            cur[u] = nxt[u];
-            const int64_t i = r0 + (u + kScatterU) * 64 + lane;
-            nxt[u] = i < w1 ? L[i] : -1;
+        for (int u = 0; u < R; ++u) {
+            const bool ok = (uint32_t)cur[u] < (uint32_t)K;
+            const uint64_t m = lanes_matching_n<NB>(cur[u], ok);
+            rank[u] = ok ? lanes_below(m) : -1;
+            cnt[u] = (int)__popcll(m);
         }
+        // ... then the chain of cursor reads and advances, round by round
 #pragma unroll
-        for (int u = 0; u < kScatterU; ++u) {
-            const int32_t l = cur[u];
-            const bool ok = (uint32_t)l < (uint32_t)K;
-            const uint64_t m = lanes_matching(l, nbits, ok);
-            if (ok) {
-                const int rank = lanes_below(m);
-                const int32_t base = tab[l];
-                Pb[base + rank] = (int32_t)(r0 + u * 64 + lane);
-                if (rank == 0) tab[l] = base + (int32_t)__popcll(m);
-            }
+        for (int u = 0; u < R; ++u) {
+            const int32_t l = rank[u] >= 0 ? cur[u] : 0;
+            const int32_t base = tab[l];
+            if (rank[u] >= 0) Pb[base + rank[u]] = (int32_t)(r0 + u * 64 + lane);
+            if (rank[u] == 0) tab[l] = base + cnt[u];
         }
     }
 }
@@ -339,13 +363,6 @@ __global__ __launch_bounds__(kDirectThreads) void k_scatter_direct(const int32_t
 static hipError_t set_lds(const void* f, size_t bytes) {
     if (bytes <= 64 * 1024) return hipSuccess;
     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
-// Waves per scatter block: as many K-bin cursor tables as fit in 128 KB of LDS, up to 8.
-static int scatter_waves(int64_t K) {
-    int wb = 8;
-    while (wb > 1 && (int64_t)wb * K * 4 > 128 * 1024) wb /= 2;
-    return wb;
 }
 
 static hipError_t launch_scan(const int32_t* counts, int64_t B, int64_t K, int32_t* offsets, int32_t* cursor,
@@ -401,21 +418,21 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
         return e;
     if (N == 0) return hipSuccess;
     const int nbits = label_bits(K);
-    const int wb = scatter_waves(K);
-    const size_t lds = (size_t)wb * K * sizeof(int32_t);
     const dim3 grid((unsigned)nch, (unsigned)B);
-#define KM_SCATTER(WBV)                                                                                       \
-    do {                                                                                                      \
-        if ((e = set_lds((const void*)k_scatter<WBV>, lds)) != hipSuccess) return e;                         \
-        hipLaunchKernelGGL(k_scatter<WBV>, grid, dim3(64 * WBV), lds, s, labels, N, (int)K, nbits, CH, nch,   \
-                           o.prefix, o.offsets, o.perm);                                                      \
+#define KM_SCATTER(WBV, NBV)                                                                                \
+    do {                                                                                                    \
+        const size_t lds = (size_t)(WBV) * K * sizeof(int32_t);                                             \
+        if ((e = set_lds((const void*)k_scatter<WBV, NBV>, lds)) != hipSuccess) return e;                  \
+        hipLaunchKernelGGL((k_scatter<WBV, NBV>), grid, dim3(64 * WBV), lds, s, labels, N, (int)K, CH, nch, \
+                           o.prefix, o.offsets, o.perm);                                                    \
     } while (0)
-    switch (wb) {
-        case 8: KM_SCATTER(8); break;
-        case 4: KM_SCATTER(4); break;
-        case 2: KM_SCATTER(2); break;
-        default: KM_SCATTER(1); break;
-    }
+    // waves per block: as many K-bin cursor tables as fit in 128 KB of LDS
+    // (K <= 4096: 8, 8192: 4, 16384: 2, 32768: 1); labels of nbits bits
+    if (nbits <= 8) KM_SCATTER(8, 8);
+    else if (nbits <= 12) KM_SCATTER(8, 12);
+    else if (nbits <= 13) KM_SCATTER(4, 13);
+    else if (nbits <= 14) KM_SCATTER(2, 14);
+    else KM_SCATTER(1, 15);
 #undef KM_SCATTER
     return hipGetLastError();
 }
