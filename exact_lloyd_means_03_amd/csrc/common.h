@@ -80,16 +80,20 @@ __device__ __forceinline__ uint64_t lanes_matching(int32_t v, int nbits, bool ac
 // The same with the number of bits fixed at compile time (unrolled); bits at
 // or above the values' width are zero in every active lane and change
 // nothing, so NB may exceed it.
+// Per bit: e = 0 or -1 by the lane's bit, s = the lanes whose bit is set, and
+// s ^ e the lanes whose bit differs from this lane's; the differing lanes of
+// all bits are removed from the active lanes at the end.
 template <int NB>
 __device__ __forceinline__ uint64_t lanes_matching_n(int32_t v, bool active) {
-    uint64_t m = __ballot(active);
+    uint32_t diff_lo = 0u, diff_hi = 0u;
 #pragma unroll
     for (int bit = 0; bit < NB; ++bit) {
-        const bool set = (v >> bit) & 1;
-        const uint64_t s = __ballot(active && set);
-        m &= set ? s : ~s;
+        const int32_t e = (int32_t)((uint32_t)v << (31 - bit)) >> 31;
+        const uint64_t s = __ballot(e != 0);
+        diff_lo |= (uint32_t)s ^ (uint32_t)e;
+        diff_hi |= (uint32_t)(s >> 32) ^ (uint32_t)e;
     }
-    return m;
+    return __ballot(active) & ~(((uint64_t)diff_hi << 32) | diff_lo);
 }
 
 // Set lanes of m below this lane.

@@ -40,6 +40,7 @@ namespace km {
 constexpr int kFit1DThreads = 256;
 constexpr int kFit1DMaxN = 8192;
 constexpr int kFit1DWaveMaxN = 64 * 64;  // rows a single wave keeps in registers
+constexpr int kRankBuckets = 256;         // buckets of the rank table (the values of a byte)
 
 bool fit_1d_rows_fits(int64_t N, int64_t K) { return N >= 1 && N <= kFit1DMaxN && K <= kFit1DMaxK; }
 
@@ -179,17 +180,44 @@ __global__ __launch_bounds__(kFit1DThreads) void k_fit_1d_rows(
 
 // One wave per row (rows of up to 64 * PPT points): the same iteration with
 // no block barriers, so the serial step of one row (the thresholds) overlaps
-// the point work of the other rows on the CU, and about ten rows share a CU.
-template <typename T, int PPT>
-__global__ __launch_bounds__(64) void k_fit_1d_wave(
+// the point work of the other rows on the CU.  KC: the most ranks a row can
+// have (K <= KC).
+//
+// A point's rank comes from a table instead of a compare per threshold:
+// kRankBuckets buckets of equal width between the first and the last
+// threshold, with bucket(x) monotone in x (float32 multiply-add, then a
+// saturating conversion to a byte).  A threshold in a lower bucket than x's is below x and one in a
+// higher bucket is above it.  So with c the count of thresholds in buckets
+// below x's, the rank of x is c plus one compare with threshold c (the one
+// in x's bucket if there is one, else a higher one, or +inf): an entry holds
+// threshold c and c.  The table is built from a mark per threshold in its
+// bucket and a count of the marks below each bucket (ballots).  An iteration
+// whose thresholds put two in one bucket counts compares instead.
+//
+// Each lane adds w*x and w of its points, in float64, into its own per-rank
+// bins ([rank][lane] doubles, so the 64 lanes of one add hit distinct banks
+// whatever the ranks).  The objective sum w (x - v)^2 of an assignment is
+// sum w x^2 (the same for every assignment) minus sum_r v_r (2 S_r - v_r W_r)
+// over the ranks, in float64.
+template <typename T, int PPT, int KC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_fit_1d_wave(
     const T* __restrict__ X, const float* __restrict__ w, int N, const float* __restrict__ init, int K,
     int n_iter, float* __restrict__ centroids, int32_t* __restrict__ labels, int32_t* __restrict__ counts,
     double* __restrict__ objective) {
+    static_assert(KC >= 2 && KC <= kFit1DMaxK && (KC & (KC - 1)) == 0, "KC: a power of two up to the rank limit");
+    static_assert(kRankBuckets == 4 * 64, "each lane builds four consecutive table entries");
+    constexpr int NT = KC - 1;                          // thresholds at most
+    constexpr int kRow = 64 * (int)sizeof(double);      // bytes of one rank's bins
     __shared__ float s_c[kFit1DMaxK];
     __shared__ float s_val[kFit1DMaxK];
     __shared__ int s_idx[kFit1DMaxK];
     __shared__ float s_thr[kFit1DMaxK];
-    __shared__ double2 s_bin[kFit1DMaxK][64 + 1];  // per-lane (sum w*x, sum w) per rank (rows padded)
+    // per-lane bins per rank, S_r = sum w x in s_bin[0] and W_r = sum w in
+    // s_bin[1]: a row is 64 doubles, so the bank of a bin depends on its lane
+    // alone and the lanes' adds never conflict
+    __shared__ double s_bin[2][KC][64];
+    __shared__ float2 s_tab[kRankBuckets];  // (threshold c, c as the byte offset of its bin row)
+    __shared__ uint32_t s_hit[kRankBuckets / 4];  // a byte per bucket: 1 where a threshold falls
     __shared__ int s_cnt[kFit1DMaxK];
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.x;
@@ -207,70 +235,150 @@ __global__ __launch_bounds__(64) void k_fit_1d_wave(
         ws[p] = i < N ? (w ? w[b * N + i] : 1.f) : 0.f;  // past the row end: weight 0, no effect
     }
     if (lane < K) s_c[lane] = init[b * K + lane];
-    if (lane < kFit1DMaxK) s_cnt[lane] = 0;
+    s_hit[lane] = 0u;
+#pragma unroll
+    for (int r = 0; r < KC; ++r) s_bin[0][r][lane] = s_bin[1][r][lane] = 0.0;
+    // sum w x^2 over the row
+    double qtot = 0.0;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) qtot += ((double)ws[p] * (double)xs[p]) * (double)xs[p];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) qtot += __shfl_xor(qtot, o, 64);
     wave_sync();
 
     int A = 0;
+    bool tab_ok = false;  // the table holds the last assignment's ranks
+    float scale = 0.f, bias = 0.f;
+    // monotone in x (any monotone map serves: the table is built with the
+    // same one): the float32 multiply-add, converted to an unsigned byte with
+    // rounding to nearest even and saturation (NaN to 0), so every result is
+    // an entry of the table
+    static_assert(kRankBuckets == 256, "bucket() yields a byte");
+    auto bucket = [&](float x) { return (int)__builtin_amdgcn_cvt_pk_u8_f32(fmaf(x, scale, bias), 0, 0); };
     for (int t = 0; t < n_iter; ++t) {
+        // the empty asm hides that the points do not change between
+        // iterations, so their float64 forms are not kept live across them
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) asm volatile("" : "+v"(xs[p]), "+v"(ws[p]));
         A = f1_thresholds<T>(s_c, K, lane, s_val, s_idx, s_thr);
-#pragma unroll
-        for (int r = 0; r < kFit1DMaxK; ++r) s_bin[r][lane] = make_double2(0.0, 0.0);
         wave_sync();
-        // the thresholds are the same in every lane: held in scalar registers,
-        // a point's rank is a branch-free count over them
-        float tr[kFit1DMaxK - 1];
+        // the thresholds are the same in every lane: held in scalar registers
+        float tr[NT];
         f1_scalar_thresholds(s_thr, tr);
-        float jpart = 0.f;
+        const int nt = A - 1;
+        const float lo = tr[0], hi = nt >= 1 ? s_thr[nt - 1] : lo;
+        scale = (nt >= 2 && hi > lo) ? (float)(kRankBuckets - 1) / (hi - lo) : 0.f;
+        bias = -lo * scale;
+        // lane a < nt: the bucket of threshold a, and whether threshold a - 1
+        // shares it
+        const int bt = lane < nt ? bucket(s_thr[lane]) : 0;
+        const bool coll = __ballot(lane >= 1 && lane < nt && bt == bucket(s_thr[lane - 1 < 0 ? 0 : lane - 1])) != 0;
+        tab_ok = !coll;
+        if (!coll) {
+            if (lane < nt) ((unsigned char*)s_hit)[bt] = 1;
+            wave_sync();
+            const uint32_t h = s_hit[lane];  // the marks of buckets 4 lane .. 4 lane + 3
+            s_hit[lane] = 0u;                // cleared for the next table
+            const uint64_t below_lanes = (1ull << lane) - 1ull;
+            int c = 0;  // marks in the buckets of lower lanes
 #pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            // the empty asm hides that x and w do not change between
-            // iterations, so their float64 forms are not kept live across them
-            float xv = xs[p], wv = ws[p];
-            asm volatile("" : "+v"(xv), "+v"(wv));
-            const int m = f1_rank_cmp(xv, tr);
-            const float tv = xv - s_val[m];
-            jpart = fmaf(wv, tv * tv, jpart);
-            // this lane's own bins, adds that return nothing: no point waits on another
-            atomicAdd(&s_bin[m][lane].x, (double)wv * (double)xv);
-            atomicAdd(&s_bin[m][lane].y, (double)wv);
-            if (p % 16 == 15) __builtin_amdgcn_sched_barrier(0);  // 16 points in flight at most
+            for (int j = 0; j < 4; ++j) c += __popcll(__ballot((h >> (8 * j)) & 1u) & below_lanes);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s_tab[4 * lane + j] = make_float2(s_thr[c], __int_as_float(c * kRow));  // c <= nt: s_thr[nt] is +inf
+                c += (h >> (8 * j)) & 1u;
+            }
         }
-        double jd = jpart;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) jd += __shfl_xor(jd, o, 64);
         wave_sync();
-        // per-rank sums: lane (r, part) adds the bins of rank r of lanes
-        // part*16 .. +16; two exchanges combine the four parts
-        const int r = lane & (kFit1DMaxK - 1), part = lane >> 4;
+        // off: the byte offset of this lane's bin of rank m, m kRow + 8 lane;
+        // this lane's own bins, adds that return nothing: no point waits on
+        // another
+        const int lane8 = lane * (int)sizeof(double);
+        auto add = [&](int off, float xv, float wv) {
+            const double wd = (double)wv;
+            double* bin = (double*)((char*)&s_bin[0][0][0] + off);
+            atomicAdd(bin, wd * (double)xv);
+            atomicAdd(bin + KC * 64, wd);
+        };
+        // groups of 16 points: their ranks first (the table reads overlap
+        // instead of each waiting in turn), then their adds
+        constexpr int G = 16;
+#pragma unroll
+        for (int p0 = 0; p0 < PPT; p0 += G) {
+            int off[G];
+            if (!coll) {
+                float2 e[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) e[j] = s_tab[bucket(xs[p0 + j])];
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    off[j] = __float_as_int(e[j].y) + (xs[p0 + j] >= e[j].x ? kRow : 0) + lane8;
+            } else {
+#pragma unroll
+                for (int j = 0; j < G; ++j) off[j] = f1_rank_cmp(xs[p0 + j], tr) * kRow + lane8;
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) add(off[j], xs[p0 + j], ws[p0 + j]);
+            __builtin_amdgcn_sched_barrier(0);  // one group of points in flight at a time
+        }
+        wave_sync();
+        // per-rank sums: lane (r, part) takes the bins of rank r of lanes
+        // part*KC .. +KC, clearing them for the next iteration in the same
+        // exchange, and shuffles combine the parts.  Lane r starts at column
+        // r of its part, so each exchange of the wave touches 64 distinct
+        // columns.
+        const int r = lane % KC, part = lane / KC;
         double S = 0.0, W = 0.0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const double2 v = s_bin[r][part * 16 + q];
-            S += v.x;
-            W += v.y;
+        for (int q = 0; q < KC; ++q) {
+            const int c = part * KC + ((q + r) & (KC - 1));
+            S += __longlong_as_double((long long)atomicExch((unsigned long long*)&s_bin[0][r][c], 0ull));
+            W += __longlong_as_double((long long)atomicExch((unsigned long long*)&s_bin[1][r][c], 0ull));
         }
-        S += __shfl_xor(S, 16, 64);
-        W += __shfl_xor(W, 16, 64);
-        S += __shfl_xor(S, 32, 64);
-        W += __shfl_xor(W, 32, 64);
+#pragma unroll
+        for (int o = KC; o < 64; o <<= 1) {
+            S += __shfl_xor(S, o, 64);
+            W += __shfl_xor(W, o, 64);
+        }
+        // the objective's share of rank r with value v: v (2 S - v W)
+        const double v = r < A ? (double)s_val[r] : 0.0;
+        double J = r < A ? v * (2.0 * S - v * W) : 0.0;
+#pragma unroll
+        for (int o = 1; o < KC; o <<= 1) J += __shfl_xor(J, o, 64);
         if (lane < A && W > 0.0) s_c[s_idx[lane]] = (float)(S / W);
-        if (lane == 0 && objective) objective[b * n_iter + t] = jd;
+        if (lane == 0 && objective) objective[b * n_iter + t] = qtot - J;
         wave_sync();
     }
-    // labels and counts of the last assignment: s_thr, s_val and s_idx still
-    // hold that iteration's values (only s_c has moved on)
+    // labels and counts of the last assignment: s_thr, s_val, s_idx, s_tab,
+    // scale and bias still hold that iteration's values (only s_c has moved
+    // on).  The bins are all zero again: per-lane counts go there.
     if (n_iter > 0) {
-        float tr[kFit1DMaxK - 1];
+        int* cbin = (int*)&s_bin[0][0][0];  // [rank][lane]
+        float tr[NT];
         f1_scalar_thresholds(s_thr, tr);
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int i = p * 64 + lane;
+            int m;
+            if (tab_ok) {
+                const float2 e = s_tab[bucket(xs[p])];
+                m = __float_as_int(e.y) / kRow + (xs[p] >= e.x ? 1 : 0);
+            } else {
+                m = f1_rank_cmp(xs[p], tr);
+            }
             if (i < N) {
-                const int m = f1_rank_cmp(xs[p], tr);
                 if (labels) labels[b * N + i] = s_idx[m];
-                atomicAdd(&s_cnt[m], 1);
+                atomicAdd(&cbin[m * 64 + lane], 1);
             }
         }
+        wave_sync();
+        const int r = lane % KC, part = lane / KC;
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < KC; ++q) c += cbin[r * 64 + part * KC + ((q + r) & (KC - 1))];
+#pragma unroll
+        for (int o = KC; o < 64; o <<= 1) c += __shfl_xor(c, o, 64);
+        if (lane < KC) s_cnt[lane] = c;
         wave_sync();
     }
     if (lane < K) {
@@ -299,9 +407,15 @@ hipError_t launch_fit_1d_rows(DType xt, const void* x, const float* w, int64_t B
     } else {                             \
         KM_F1(TT, 32);                   \
     }
-#define KM_FW(TT, PP)                                                                                 \
-    hipLaunchKernelGGL((k_fit_1d_wave<TT, PP>), grid, dim3(64), 0, s, (const TT*)x, w, (int)N, init,    \
-                       (int)K, n_iter, centroids, labels, counts, objective)
+#define KM_FW(TT, PP)                                                                                     \
+    do {                                                                                                      \
+        if (K <= 8)                                                                                           \
+            hipLaunchKernelGGL((k_fit_1d_wave<TT, PP, 8>), grid, dim3(64), 0, s, (const TT*)x, w, (int)N, init, \
+                               (int)K, n_iter, centroids, labels, counts, objective);                         \
+        else                                                                                                  \
+            hipLaunchKernelGGL((k_fit_1d_wave<TT, PP, 16>), grid, dim3(64), 0, s, (const TT*)x, w, (int)N,     \
+                               init, (int)K, n_iter, centroids, labels, counts, objective);                   \
+    } while (0)
 #define KM_FW_T(TT)                      \
     if (N <= 16 * 64) {                  \
         KM_FW(TT, 16);                   \

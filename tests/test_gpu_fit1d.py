@@ -2,9 +2,9 @@
 
 Rows of up to 8192 points with K <= 16 run every iteration in one launch;
 the cases below cover that path's edges (one centroid, duplicate centroids,
-unweighted and weighted rows, ragged row lengths, 16-bit points, rows of
-more than 4096 points, a single iteration, optional outputs) and the
-boundary to the per-iteration path (K = 17, N = 8193), which must agree.
+centroids a few floats apart, unweighted and weighted rows, ragged row
+lengths, 16-bit points, rows of more than 4096 points, a single iteration,
+optional outputs) and the boundary to the per-iteration path (K = 17, N = 8193), which must agree.
 """
 import numpy as np
 import pytest
@@ -110,6 +110,23 @@ def test_optional_outputs_and_no_iterations(km):
     c0, _, _, _ = km.kmeans_fit(xd, Cd, 0, weights=wd)
     torch.cuda.synchronize()
     assert torch.equal(c0, Cd)
+
+
+@pytest.mark.parametrize("n_iter", [1, 4])
+def test_close_thresholds_count_compares(km, n_iter):
+    """Four centroids a few floats apart put three thresholds within a span
+    far below the width of one table bucket, so two of them share a bucket:
+    that iteration ranks points by compares, and with one iteration so do
+    the labels and counts."""
+    x, w, C = _rows(12, 4096, 16, "f32", True, seed=29)
+    Cn = C.numpy()[..., 0].copy()
+    for b in range(Cn.shape[0]):
+        v = np.float32(np.median(x.numpy()[b, :, 0]))
+        for j in range(4):  # indices 3, 7, 11, 15 hold v and the next floats above it
+            Cn[b, 4 * j + 3] = v
+            v = np.nextafter(v, np.float32(np.inf))
+    C = torch.from_numpy(Cn).reshape(C.shape)
+    _compare(km, x, w, C, n_iter, f"close thresholds it{n_iter}")
 
 
 @pytest.mark.parametrize("N,K", [(4096, 17), (8193, 16)])
