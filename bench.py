@@ -34,7 +34,8 @@ PEAK_VALU_GOPS = 256 * 4 * 16 * 2.4
 OPS_1D_PER_POINT = 8
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_03_amd", "csrc", "assign_mfma.hip")
+# the sources of the assignment kernel: a traffic figure holds while they are unchanged
+ASSIGN_SRC = [os.path.join(ROOT, "exact_lloyd_means_03_amd", "csrc", f) for f in ("assign_mfma.hip", "common.h")]
 
 
 def update_bytes(wl) -> float:
@@ -52,8 +53,11 @@ def assign_bytes(wl) -> float:
     return B * N * (d * s + 4) + w + B * K * d * 4
 
 
-def _src_hash(path) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def _src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(wl):
@@ -603,10 +607,15 @@ def main():
         return bench_stream(args, km, wl)
     if wl.em_batch:
         return bench_emeans(args, km, wl)
-    p = workloads.generate(wl)
-    x = p.x.to(dev)
-    w = None if p.w is None else p.w.to(dev)
-    C = p.init.to(dev).clone()
+    if wl.device_gen:
+        p = None  # made on the GPU; no host copy for the CPU baseline
+        x, C = workloads.generate_device(wl)
+        w = None
+    else:
+        p = workloads.generate(wl)
+        x = p.x.to(dev)
+        w = None if p.w is None else p.w.to(dev)
+        C = p.init.to(dev).clone()
     B, N, d, K = wl.B, wl.N, wl.d, wl.K
     ws = km.workspace(B, N, d, K, x.dtype, dev)
     labels = torch.empty((B, N), dtype=torch.int32, device=dev)
@@ -686,7 +695,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_zipf_update and wl.name == workloads.HEADLINE and not args.points:
         out["update_zipf"] = bench_update(km, workloads.WORKLOADS["zipf-n32m-k4096-d128-bf16"])
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and p is not None:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -62,6 +62,7 @@ class Workload:
     w_lo: float = 0.1       # rows1d: sample weights ~ U(w_lo, w_hi)
     w_hi: float = 1.0
     host: bool = False      # the points stay in (pinned) host memory: generate_host()
+    device_gen: bool = False  # too large for the host generator: generate_device()
     em_batch: int = 0       # e-means: points per step (0: not an e-means workload)
     em_epochs: int = 0      # e-means: passes over the points
     em_alpha0: float = 0.5  # e-means: first step size
@@ -101,6 +102,15 @@ WORKLOADS = {
                  n_iter=30, seed=5, kind="rows1d", init="linspace"),
         Workload("stream-n64m-k32768-d128-f16", B=1, N=1 << 26, d=128, K=32768, dtype="f16",
                  n_iter=3, seed=6, sigma=0.15, init="random", host=True),
+        # the out-of-core size of the technologypulse.uk article's performance
+        # section, 4e8 points against 16384 centroids (d = 128, 102 GB in
+        # fp16): resident in device memory, and streamed from pinned host
+        # memory at 2.5e8 points (64 GB, the most one pinned allocation holds
+        # on the measuring host)
+        Workload("gmm-n400m-k16384-d128-f16", B=1, N=400_000_000, d=128, K=16384, dtype="f16",
+                 n_iter=3, seed=8, sigma=0.15, init="random", device_gen=True),
+        Workload("stream-n250m-k16384-d128-f16", B=1, N=250_000_000, d=128, K=16384, dtype="f16",
+                 n_iter=3, seed=8, sigma=0.15, init="random", host=True),
         # e-means against Lloyd: n_iter is the Lloyd comparison run
         Workload("emeans-n1m-k16384-d96-bf16", B=1, N=1 << 20, d=96, K=16384, dtype="bf16",
                  n_iter=25, seed=7, sigma=0.15, noise_frac=0.05, noise_range=3.0, init="random",
@@ -275,24 +285,42 @@ def dtype_name(x: torch.Tensor) -> str:
     return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype]
 
 
-def generate_host(wl: Workload, chunk: int = 1 << 22):
-    """Points of a host-memory workload, made on the GPU from a seeded generator
-    (numpy would take minutes at this size) and copied into pinned host memory:
-    a Gaussian mixture of wl.components means ~ N(0, 1) with per-coordinate
-    std wl.sigma, components drawn uniformly, stored in wl.dtype.  Returns
-    (x_host [N, d] pinned CPU tensor, init [K, d] float32 on the GPU: K
-    distinct random points)."""
-    assert wl.host and wl.B == 1 and wl.kind == "gmm"
+def _gmm_on_gpu(wl: Workload, x: torch.Tensor, chunk: int) -> torch.Tensor:
+    """Fill x [N, d] (host or device) with a Gaussian mixture made on the GPU
+    from a seeded generator (numpy would take minutes at these sizes):
+    wl.components means ~ N(0, 1), per-coordinate std wl.sigma, components
+    drawn uniformly, stored in wl.dtype.  Returns the indices of K distinct
+    random points (the initial centroids)."""
     g = torch.Generator(device="cuda").manual_seed(wl.seed)
     means = torch.randn((wl.components, wl.d), generator=g, device="cuda")
-    x = torch.empty((wl.N, wl.d), dtype=_TORCH_DTYPE[wl.dtype], pin_memory=True)
     for p0 in range(0, wl.N, chunk):
         n = min(chunk, wl.N - p0)
         comp = torch.randint(0, wl.components, (n,), generator=g, device="cuda")
         v = means[comp] + wl.sigma * torch.randn((n, wl.d), generator=g, device="cuda")
         x[p0:p0 + n].copy_(v.to(_TORCH_DTYPE[wl.dtype]))
-    idx = torch.randperm(wl.N, generator=g, device="cuda")[:wl.K].cpu()
+    return torch.randperm(wl.N, generator=g, device="cuda")[:wl.K]
+
+
+def generate_host(wl: Workload, chunk: int = 1 << 22):
+    """Points of a host-memory workload (_gmm_on_gpu, copied into pinned host
+    memory).  Returns (x_host [N, d] pinned CPU tensor, init [K, d] float32
+    on the GPU: K distinct random points)."""
+    assert wl.host and wl.B == 1 and wl.kind == "gmm"
+    x = torch.empty((wl.N, wl.d), dtype=_TORCH_DTYPE[wl.dtype], pin_memory=True)
+    idx = _gmm_on_gpu(wl, x, chunk).cpu()
     init = x[idx].float().cuda()
+    torch.cuda.synchronize()
+    return x, init
+
+
+def generate_device(wl: Workload, chunk: int = 1 << 22):
+    """Points of a workload made and kept on the GPU (_gmm_on_gpu).  Returns
+    (x [1, N, d] in device memory, init [1, K, d] float32: K distinct random
+    points)."""
+    assert wl.device_gen and wl.B == 1 and wl.kind == "gmm"
+    x = torch.empty((1, wl.N, wl.d), dtype=_TORCH_DTYPE[wl.dtype], device="cuda")
+    idx = _gmm_on_gpu(wl, x[0], chunk)
+    init = x[0, idx].float()[None].contiguous()
     torch.cuda.synchronize()
     return x, init
 
