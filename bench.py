@@ -181,6 +181,49 @@ def bench_update(km, wl, reps: int = 5) -> dict:
     return out
 
 
+def bench_graph_fit(km, x, init, w, steps: int, ws, reps: int = 20) -> dict:
+    """Launch overhead of a small fit: the same kmeans_fit of `steps`
+    iterations called eagerly and replayed from a HIP graph it was captured
+    into (the library enqueues kernels only, so the whole fit captures),
+    `reps` times each between synchronizations, wall clock."""
+    import torch
+
+    B, K, d = init.shape
+    N = x.shape[1]
+    cen = torch.empty_like(init)
+    lab = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    cnt = torch.empty((B, K), dtype=torch.int32, device=x.device)
+    obj = torch.empty((B, steps), dtype=torch.float64, device=x.device)
+
+    def fit():
+        km.kmeans_fit(x, init, steps, weights=w, centroids=cen, labels=lab, counts=cnt, objective=obj, ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fit()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fit()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fit()
+    torch.cuda.synchronize()
+    eager = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = time.perf_counter() - t0
+    return {"iterations_per_fit": steps, "fits": reps, "eager_ms_per_iter": eager / (reps * steps) * 1e3,
+            "graph_ms_per_iter": graph / (reps * steps) * 1e3, "graph_iter_per_s": reps * steps / graph,
+            "timing": "wall clock over `fits` back-to-back fits, eager calls vs replays of one captured fit"}
+
+
 def bench_fit_1d(args, km, wl, p, x, w, C):
     """Scalar rows: kmeans_fit runs every iteration of rows of up to 8192
     points with K <= 16 in one launch, so a step is one iteration inside
@@ -691,6 +734,8 @@ def main():
                              "argsort, segmented reduction, divide + next prep)"},
         "cpu_baseline": None,
     }
+    if B * N * K * d <= (1 << 30):  # launch-bound sizes: the same fit replayed from a HIP graph
+        out["graph"] = bench_graph_fit(km, x, C, w, K_steps, ws)
     del x, w, ws, labels, counts
     torch.cuda.empty_cache()
     if not args.no_zipf_update and wl.name == workloads.HEADLINE and not args.points:
