@@ -166,11 +166,12 @@ P* at(void* ws, size_t off) {
 // blob already holds C (written by the previous update's fused divide).
 // ev_begin / ev_end (may be NULL): recorded on s right before and right after
 // the assignment kernel launches (after the prep, before the objective
-// reduction).
+// reduction).  reduce_obj = false: leave the partials in W.obj_part for the
+// sort's column scan to sum (matrix-core path with N > 0 only).
 km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, const float* C, int64_t K,
                      const float* w, int32_t* labels, float* min_dist, double* obj_out, int64_t obj_stride,
                      const Workspace& W, void* ws, hipStream_t s, bool prep = true, hipEvent_t ev_begin = nullptr,
-                     hipEvent_t ev_end = nullptr, int32_t* hist = nullptr) {
+                     hipEvent_t ev_end = nullptr, int32_t* hist = nullptr, bool reduce_obj = true) {
     double* part = obj_out ? at<double>(ws, W.obj_part) : nullptr;
     if (use_assign_1d(d, K)) {
         if (ev_begin) KM_HIP(hipEventRecord(ev_begin, s), "event");
@@ -192,7 +193,7 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
                "assign_mfma");
     }
     if (ev_end) KM_HIP(hipEventRecord(ev_end, s), "event");
-    if (obj_out) {
+    if (obj_out && reduce_obj) {
         if (N == 0) {
             KM_HIP(launch_zero(part, (size_t)B * W.nblk_assign * sizeof(double), s), "zero");
         }
@@ -206,11 +207,19 @@ km_status run_assign(const void* x, DType xt, int64_t B, int64_t N, int64_t d, c
 // piece; short_flag (may be NULL): also flag the problems whose clusters are
 // all short enough for the one-segment-per-row-group reduction.  counted:
 // the assignment already built the histogram rows.
+// obj_out (may be NULL): the column scan also sums the assignment's objective
+// partials left in W.obj_part into obj_out[b * obj_stride].
 km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32_t* counts, int32_t* offsets,
                    int32_t* perm, int32_t* piece_seg, int32_t* short_flag, const Workspace& W, void* ws,
-                   hipStream_t s, bool counted = false) {
+                   hipStream_t s, bool counted = false, double* obj_out = nullptr, int64_t obj_stride = 0) {
     SortBufs o{counts, offsets, perm, at<int32_t>(ws, W.hist), at<int32_t>(ws, W.prefix), nullptr, piece_seg,
                short_flag};
+    if (obj_out) {
+        o.obj_part = at<double>(ws, W.obj_part);
+        o.obj_nblk = W.nblk_assign;
+        o.obj_out = obj_out;
+        o.obj_stride = obj_stride;
+    }
     KM_HIP(launch_sort(labels, B, N, K, o, segreduce_tw(B, N), segreduce_pieces(B, N), s,
                        counted ? SortMode::StableCounted : SortMode::Stable),
            "sort");
@@ -221,7 +230,8 @@ km_status run_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, int32
 // (the divide fused with the prep; matrix-core path only).
 km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t N, int64_t d,
                      const int32_t* labels, int64_t K, const float* c_old, float* c_new, int32_t* counts,
-                     const Workspace& W, void* ws, hipStream_t s, bool prep_next = false, bool counted = false) {
+                     const Workspace& W, void* ws, hipStream_t s, bool prep_next = false, bool counted = false,
+                     double* obj_out = nullptr, int64_t obj_stride = 0) {
     int32_t* cnt = counts ? counts : at<int32_t>(ws, W.counts);
     if (use_update_1d(xt, x, w, labels, d, N, K)) {
         KM_HIP(launch_update_1d_row(xt, x, w, B, N, labels, K, c_old, c_new, cnt, s), "update_1d_row");
@@ -235,7 +245,8 @@ km_status run_update(const void* x, DType xt, const float* w, int64_t B, int64_t
     int32_t* perm = at<int32_t>(ws, W.perm);
     int32_t* piece_seg = at<int32_t>(ws, W.piece_seg);
     int32_t* short_flag = at<int32_t>(ws, W.seg_short);
-    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, short_flag, W, ws, s, counted));
+    KM_TRY(run_sort(labels, B, N, K, cnt, offsets, perm, piece_seg, short_flag, W, ws, s, counted, obj_out,
+                    obj_stride));
     float* slot = at<float>(ws, W.slot);
     float* wslot = w ? at<float>(ws, W.wslot) : nullptr;
     float* gslot = at<float>(ws, W.gslot);
@@ -572,11 +583,12 @@ km_status run_fit(const void* x, int xt, const float* weights, int64_t B, int64_
         // from the second iteration on, the previous update's divide wrote the
         // centroid tiles, unless the update took the scalar-row path
         const bool fused = t > 0 && !use_update_1d((DType)enum_code(xt), x, weights, lab, d, N, K);
-        KM_TRY(run_assign(x, (DType)enum_code(xt), B, N, d, centroids, K, weights, lab, nullptr,
-                          objective ? objective + t : nullptr, n_iter, W, workspace, s, !fused, ev(2 * t),
-                          ev(2 * t + 1), hist));
+        // counted: the sort's column scan also sums the objective partials
+        double* obj_t = objective ? objective + t : nullptr;
+        KM_TRY(run_assign(x, (DType)enum_code(xt), B, N, d, centroids, K, weights, lab, nullptr, obj_t, n_iter, W,
+                          workspace, s, !fused, ev(2 * t), ev(2 * t + 1), hist, !counted));
         KM_TRY(run_update(x, (DType)enum_code(xt), weights, B, N, d, lab, K, centroids, centroids, counts, W, workspace, s,
-                          t + 1 < n_iter, counted));
+                          t + 1 < n_iter, counted, counted ? obj_t : nullptr, n_iter));
     }
     return KM_OK;
 }

@@ -166,6 +166,30 @@ hipError_t launch_assign_1d(DType xt, const void* x, int64_t B, int64_t N, const
 int64_t assign_1d_blocks(int64_t N);
 bool assign_1d_supports(int64_t K);
 
+// The sum of one problem's nblk objective partials by a block of 1024
+// threads: each sums a fixed strided subset with 8 independent accumulators
+// (loads stay in flight), then a fixed-order tree through red[1024] in LDS,
+// so the result does not depend on timing.  Every thread of the block calls
+// it; thread 0 stores the sum.
+__device__ inline void obj_sum_1024(const double* __restrict__ pb, int64_t nblk, double* out, double* red) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t i = threadIdx.x;
+    for (; i + 7 * 1024 < nblk; i += 8 * 1024) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += pb[i + u * 1024];
+    }
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+        if (i + u * 1024 < nblk) acc[u] += pb[i + u * 1024];
+    red[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    __syncthreads();
+    for (int o = 512; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = red[0];
+}
+
 hipError_t launch_obj_reduce(const double* part, int64_t B, int64_t nblk, double* out,
                              int64_t out_stride, hipStream_t s);
 
@@ -197,6 +221,12 @@ struct SortBufs {
     int32_t* cursor;      // [B][K] (direct modes)
     int32_t* piece_seg;   // [B][npieces] or NULL: first segment of every reduction piece
     int32_t* short_flag;  // [B] or NULL: 1 when no cluster has more than kShortSegMax points
+    // optional: the assignment's objective partials [B][obj_nblk], summed by
+    // the column scan into obj_out[b * obj_stride] (stable modes only)
+    const double* obj_part = nullptr;
+    int64_t obj_nblk = 0;
+    double* obj_out = nullptr;
+    int64_t obj_stride = 0;
 };
 int64_t sort_chunk(int64_t B, int64_t N, int64_t K);
 int64_t sort_chunks(int64_t B, int64_t N, int64_t K);

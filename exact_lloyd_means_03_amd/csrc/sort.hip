@@ -98,12 +98,21 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(const int32_t* __restrict
 // back to H (the assignment of the next iteration adds into it).
 constexpr int kColBins = 64, kColQ = 16, kColMaxPer = 16;
 
+// obj_out (may be NULL): the first block of each problem also sums the
+// assignment's objective partials of the problem (obj_sum_1024), which saves
+// the objective's own launch inside a fit.
+static_assert(kColBins * kColQ == 1024, "the objective sum takes a block of 1024 threads");
+
 __global__ __launch_bounds__(kColBins* kColQ) void k_colscan(int32_t* __restrict__ H, int64_t nch, int K,
                                                              int32_t* __restrict__ P, int32_t* __restrict__ counts,
-                                                             bool clear) {
+                                                             bool clear, const double* __restrict__ obj_part,
+                                                             int64_t obj_nblk, double* __restrict__ obj_out,
+                                                             int64_t obj_stride) {
     __shared__ int32_t s_tot[kColQ][kColBins];
+    __shared__ double s_red[1024];
     const int jl = threadIdx.x % kColBins, q = threadIdx.x / kColBins;
     const int64_t b = blockIdx.y;
+    if (obj_out && blockIdx.x == 0) obj_sum_1024(obj_part + b * obj_nblk, obj_nblk, obj_out + b * obj_stride, s_red);
     const int j = blockIdx.x * kColBins + jl;
     const int64_t per = (nch + kColQ - 1) / kColQ;  // <= kColMaxPer
     const int64_t c0 = q * per;
@@ -245,7 +254,12 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
 // consecutive parts of the chunk.  LDS: WB cursor tables of K bins.  Labels
 // are read kScatterR rounds of 64 at a time, the next batch's loads issued
 // before the current batch is ranked, so the ranking (a chain of LDS reads
-// and writes per round) runs under the loads.
+// and writes per round) runs under the loads.  The kernel is a chain of
+// device-memory round trips at one or two waves per SIMD, so it issues what
+// it can early: the first BU bins' bases (offsets + P) are loaded before the
+// wave counts its part, and a part of at most 2 kScatterR rounds keeps its
+// labels in registers from the count to the placement instead of reading
+// them twice.
 constexpr int kScatterR = 16;
 
 template <int WB, int NB>
@@ -255,6 +269,9 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
                                                      const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm) {
     constexpr int R = kScatterR;
+    // bins per thread in one pass of the base loop: all of them up to 32
+    constexpr int BINS = (1 << NB) / (64 * WB);
+    constexpr int BU = BINS < 1 ? 1 : (BINS > 32 ? 32 : BINS);
     extern __shared__ int32_t s_tab[];  // [WB][K]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t b = blockIdx.y, c = blockIdx.x;
@@ -272,28 +289,49 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
             v[u] = i < w1 ? L[i] : -1;
         }
     };
-    for (int j = lane; j < K; j += 64) tab[j] = 0;
-    __builtin_amdgcn_wave_barrier();
-    // this wave's histogram, R labels in flight per lane
-    for (int64_t r0 = w0; r0 < w1; r0 += 64 * R) {
-        int32_t v[R];
-        load_batch(r0, v);
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-            if ((uint32_t)v[u] < (uint32_t)K) atomicAdd(&tab[v[u]], 1);
-    }
-    __syncthreads();
     // cursor of bin j for wave w: where the chunk's points of bin j start,
-    // plus those of the earlier waves (bins loaded 8 at a time per thread)
+    // plus those of the earlier waves
     const int32_t* Pc = P + (b * nch + c) * (int64_t)K;
     const int32_t* ob = offsets + b * (K + 1);
-    constexpr int BU = 8;
-    for (int j0 = tid; j0 < K; j0 += 64 * WB * BU) {
-        int32_t base[BU];
+    auto load_bases = [&](int j0, int32_t (&base)[BU]) {
 #pragma unroll
         for (int e = 0; e < BU; ++e) {
             const int j = j0 + e * 64 * WB;
             base[e] = j < K ? ob[j] + Pc[j] : 0;
+        }
+    };
+    int32_t base0[BU];
+    load_bases(tid, base0);
+    const bool keep = part <= 2 * 64 * R;  // (a block-uniform choice)
+    int32_t kept[2][R];
+    for (int j = lane; j < K; j += 64) tab[j] = 0;
+    __builtin_amdgcn_wave_barrier();
+    // this wave's histogram, R labels in flight per lane
+    if (keep) {
+        load_batch(w0, kept[0]);
+        load_batch(w0 + 64 * R, kept[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+                if ((uint32_t)kept[h][u] < (uint32_t)K) atomicAdd(&tab[kept[h][u]], 1);
+    } else {
+        for (int64_t r0 = w0; r0 < w1; r0 += 64 * R) {
+            int32_t v[R];
+            load_batch(r0, v);
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+                if ((uint32_t)v[u] < (uint32_t)K) atomicAdd(&tab[v[u]], 1);
+        }
+    }
+    __syncthreads();
+    for (int j0 = tid; j0 < K; j0 += 64 * WB * BU) {
+        int32_t base[BU];
+        if (j0 == tid) {
+#pragma unroll
+            for (int e = 0; e < BU; ++e) base[e] = base0[e];
+        } else {
+            load_bases(j0, base);
         }
 #pragma unroll
         for (int e = 0; e < BU; ++e) {
@@ -310,14 +348,9 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     }
     __syncthreads();
     int32_t* Pb = perm + b * N;
-    int32_t nxt[R];
-    load_batch(w0, nxt);
-    for (int64_t r0 = w0; r0 < w1; r0 += 64 * R) {
-        int32_t cur[R];
-#pragma unroll
-        for (int u = 0; u < R; ++u) cur[u] = nxt[u];
-        load_batch(r0 + 64 * R, nxt);
-        // first every round's grouping (ballots only, no memory) ...
+    // one batch of R rounds from r0: every round's grouping first (ballots
+    // only, no memory), then the chain of cursor reads and advances
+    auto place = [&](int64_t r0, const int32_t (&cur)[R]) {
         int rank[R], cnt[R];
 #pragma unroll
         for (int u = 0; u < R; ++u) {
@@ -326,7 +359,6 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
             rank[u] = ok ? lanes_below(m) : -1;
             cnt[u] = (int)__popcll(m);
         }
-        // ... then the chain of cursor reads and advances, round by round
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int32_t l = rank[u] >= 0 ? cur[u] : 0;
@@ -334,6 +366,20 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
             if (rank[u] >= 0) Pb[base + rank[u]] = (int32_t)(r0 + u * 64 + lane);
             if (rank[u] == 0) tab[l] = base + cnt[u];
         }
+    };
+    if (keep) {
+        place(w0, kept[0]);
+        place(w0 + 64 * R, kept[1]);
+        return;
+    }
+    int32_t nxt[R];
+    load_batch(w0, nxt);
+    for (int64_t r0 = w0; r0 < w1; r0 += 64 * R) {
+        int32_t cur[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) cur[u] = nxt[u];
+        load_batch(r0 + 64 * R, nxt);
+        place(r0, cur);
     }
 }
 
@@ -408,7 +454,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
     if (N > 0) {
         hipLaunchKernelGGL(k_colscan, dim3((unsigned)((K + kColBins - 1) / kColBins), (unsigned)B),
                            dim3(kColBins * kColQ), 0, s, o.hist, nch, (int)K, o.prefix, o.counts,
-                           mode == SortMode::StableCounted);
+                           mode == SortMode::StableCounted, o.obj_part, o.obj_nblk, o.obj_out, o.obj_stride);
     } else {
         e = launch_zero(o.counts, (size_t)B * K * sizeof(int32_t), s);
     }
