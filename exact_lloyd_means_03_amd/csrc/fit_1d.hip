@@ -26,7 +26,9 @@
 //      rank of x is then the number of thresholds <= x.
 //   3. Each thread adds w*x and w of its points, in float64, into its own
 //      per-rank bins in LDS (adds that return nothing, on addresses no other
-//      lane touches), and w * (x - v)^2 into its objective partial.
+//      lane touches).  The block kernel also adds w * (x - v)^2 into an
+//      objective partial; the wave kernel takes the objective from the
+//      row's sum of w x^2 and the per-rank sums instead.
 //   4. The bins are reduced per rank in float64; the new centroid of the
 //      smallest index of each value is S / W (float64 divide, then float32),
 //      a value with no points keeps its centroid, and so does every centroid
