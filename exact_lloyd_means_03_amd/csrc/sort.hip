@@ -254,12 +254,13 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
 // consecutive parts of the chunk.  LDS: WB cursor tables of K bins.  Labels
 // are read kScatterR rounds of 64 at a time, the next batch's loads issued
 // before the current batch is ranked, so the ranking (a chain of LDS reads
-// and writes per round) runs under the loads.  The kernel is a chain of
-// device-memory round trips at one or two waves per SIMD, so it issues what
-// it can early: the first BU bins' bases (offsets + P) are loaded before the
-// wave counts its part, and a part of at most 2 kScatterR rounds keeps its
-// labels in registers from the count to the placement instead of reading
-// them twice.
+// and writes per round) runs under the loads.  At one or two waves per SIMD
+// the fixed work of a block (clearing WB·K table entries, reading K bases)
+// costs more than its labels, so it moves 16 bytes per lane per instruction
+// where the rows allow (K a multiple of 4, the offsets and prefix rows
+// 16-byte aligned), the first bases' loads are issued before the count, and a
+// part of at most 2 kScatterR rounds keeps its labels in registers from the
+// count to the placement instead of reading them twice.
 constexpr int kScatterR = 16;
 
 template <int WB, int NB>
@@ -269,10 +270,8 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
                                                      const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm) {
     constexpr int R = kScatterR;
-    // bins per thread in one pass of the base loop: all of them up to 32
-    constexpr int BINS = (1 << NB) / (64 * WB);
-    constexpr int BU = BINS < 1 ? 1 : (BINS > 32 ? 32 : BINS);
-    extern __shared__ int32_t s_tab[];  // [WB][K]
+    constexpr int BU = 8;  // bins (or groups of 4 bins) per thread and pass
+    extern __shared__ __attribute__((aligned(16))) int32_t s_tab[];  // [WB][K]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t b = blockIdx.y, c = blockIdx.x;
     const int64_t i0 = c * CH;
@@ -293,18 +292,26 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     // plus those of the earlier waves
     const int32_t* Pc = P + (b * nch + c) * (int64_t)K;
     const int32_t* ob = offsets + b * (K + 1);
-    auto load_bases = [&](int j0, int32_t (&base)[BU]) {
+    // 16-byte rows: thread tid takes the groups of 4 bins tid, tid + 64 WB, ...
+    const bool vec = (K & 3) == 0 && ((uintptr_t)ob & 15) == 0 && ((uintptr_t)Pc & 15) == 0;  // (block-uniform)
+    const int K4 = K >> 2;
+    auto load_bases4 = [&](int q0, i32x4 (&base)[BU]) {
 #pragma unroll
         for (int e = 0; e < BU; ++e) {
-            const int j = j0 + e * 64 * WB;
-            base[e] = j < K ? ob[j] + Pc[j] : 0;
+            const int q = q0 + e * 64 * WB;
+            base[e] = q < K4 ? ((const i32x4*)ob)[q] + ((const i32x4*)Pc)[q] : i32x4{0, 0, 0, 0};
         }
     };
-    int32_t base0[BU];
-    load_bases(tid, base0);
+    i32x4 base0[BU];
+    if (vec) load_bases4(tid, base0);
     const bool keep = part <= 2 * 64 * R;  // (a block-uniform choice)
     int32_t kept[2][R];
-    for (int j = lane; j < K; j += 64) tab[j] = 0;
+    if ((K & 3) == 0) {
+        i32x4* tab4 = (i32x4*)tab;
+        for (int q = lane; q < K4; q += 64) tab4[q] = i32x4{0, 0, 0, 0};
+    } else {
+        for (int j = lane; j < K; j += 64) tab[j] = 0;
+    }
     __builtin_amdgcn_wave_barrier();
     // this wave's histogram, R labels in flight per lane
     if (keep) {
@@ -325,23 +332,47 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
         }
     }
     __syncthreads();
-    for (int j0 = tid; j0 < K; j0 += 64 * WB * BU) {
-        int32_t base[BU];
-        if (j0 == tid) {
+    if (vec) {
+        for (int q0 = tid; q0 < K4; q0 += 64 * WB * BU) {
+            i32x4 base[BU];
+            if (q0 == tid) {
 #pragma unroll
-            for (int e = 0; e < BU; ++e) base[e] = base0[e];
-        } else {
-            load_bases(j0, base);
+                for (int e = 0; e < BU; ++e) base[e] = base0[e];
+            } else {
+                load_bases4(q0, base);
+            }
+#pragma unroll
+            for (int e = 0; e < BU; ++e) {
+                const int q = q0 + e * 64 * WB;
+                if (q < K4) {
+#pragma unroll
+                    for (int v = 0; v < WB; ++v) {
+                        i32x4* t4 = (i32x4*)(s_tab + v * K) + q;
+                        const i32x4 cnt = *t4;
+                        *t4 = base[e];
+                        base[e] += cnt;
+                    }
+                }
+            }
         }
+    } else {
+        for (int j0 = tid; j0 < K; j0 += 64 * WB * BU) {
+            int32_t base[BU];
 #pragma unroll
-        for (int e = 0; e < BU; ++e) {
-            const int j = j0 + e * 64 * WB;
-            if (j < K) {
+            for (int e = 0; e < BU; ++e) {
+                const int j = j0 + e * 64 * WB;
+                base[e] = j < K ? ob[j] + Pc[j] : 0;
+            }
 #pragma unroll
-                for (int v = 0; v < WB; ++v) {
-                    const int32_t t = s_tab[v * K + j];
-                    s_tab[v * K + j] = base[e];
-                    base[e] += t;
+            for (int e = 0; e < BU; ++e) {
+                const int j = j0 + e * 64 * WB;
+                if (j < K) {
+#pragma unroll
+                    for (int v = 0; v < WB; ++v) {
+                        const int32_t t = s_tab[v * K + j];
+                        s_tab[v * K + j] = base[e];
+                        base[e] += t;
+                    }
                 }
             }
         }
