@@ -88,9 +88,11 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                                                    float* __restrict__ wslot, bool accumulate,
                                                    const int32_t* __restrict__ skip) {
     constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 8;  // non-vector rows: 64 lanes x 8 = 512 elements
-    constexpr int U = 8;  // row steps in flight
+    constexpr int U = VEC ? 8 : 4;  // row steps per batch (two batches in flight)
     __shared__ int32_t s_idx[4][kSegChunk];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    // wv is uniform over the wave: saying so keeps the piece's bounds and
+    // every loop over them in scalar registers and scalar branches
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t piece = (int64_t)blockIdx.x * 4 + wv;
     const int64_t b = blockIdx.y;
     if (piece >= npieces) return;
@@ -109,26 +111,56 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
     const int32_t* pb = perm + b * N;
     int32_t* sidx = s_idx[wv];
 
+    // A chunk's point indices are staged in LDS: every load of the chunk is
+    // issued before the first store, so the staging costs one load latency.
+    constexpr int kIdxPerLane = kSegChunk / 64;
+    int32_t iv[kIdxPerLane];
+    auto load_idx = [&](int32_t c0, int32_t c1) {
+#pragma unroll
+        for (int i = 0; i < kIdxPerLane; ++i) {
+            // written on every path, so no value lives on to the next chunk
+            iv[i] = 0;
+            if (64 * i < c1 - c0) {
+                const int32_t r = c0 + lane + 64 * i;
+                iv[i] = pb[r < c1 ? r : c1 - 1];
+            }
+        }
+    };
+    auto store_idx = [&](int32_t c0, int32_t c1) {
+#pragma unroll
+        for (int i = 0; i < kIdxPerLane; ++i)
+            if (64 * i < c1 - c0) sidx[lane + 64 * i] = iv[i];
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+    const int32_t c1_first = (q0 + kSegChunk < q1) ? (int32_t)q0 + kSegChunk : q1;
+    load_idx((int32_t)q0, c1_first);
+
     // window of offsets: lane l holds offsets[wbase + l] (INT_MAX past K)
     int wbase = piece_seg[b * npieces + piece];
-    int32_t win = (wbase + lane <= K) ? offb[wbase + lane] : 0x7fffffff;
+    auto load_win = [&]() {
+        const int jw = wbase + lane;
+        const int32_t v = offb[jw <= K ? jw : K];
+        return jw <= K ? v : 0x7fffffff;
+    };
+    int32_t win = load_win();
     // segment containing q: the last j with offsets[j] <= q; returns its end
     int j = 0;
     auto locate = [&](int32_t q) -> int32_t {
         unsigned long long m = __ballot(win > q);
         while (m == 0ull) {
             wbase += 63;
-            win = (wbase + lane <= K) ? offb[wbase + lane] : 0x7fffffff;
+            win = load_win();
             m = __ballot(win > q);
         }
         const int l = __ffsll((long long)m) - 1;  // first lane with offsets > q (l >= 1)
         j = wbase + l - 1;
-        return __shfl(win, l, 64);
+        return __builtin_amdgcn_readfirstlane(__shfl(win, l, 64));
     };
     // whether the piece's first segment began in an earlier piece (then its
     // part here goes to the piece's slot); one that begins exactly at the
     // piece's first row is stored directly, like any later segment
-    const bool cont = offb[piece_seg[b * npieces + piece]] < (int32_t)q0;
+    const bool cont = offb[wbase] < (int32_t)q0;
 
     float acc[EPL];
 #pragma unroll
@@ -182,62 +214,87 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
         wacc = 0.f;
     };
 
-    int32_t send = locate((int32_t)q0);
+    // The piece is walked in batches of STEP = RPW*U sorted rows, each row
+    // group taking rows bs + u*RPW + gl.  The loads of the next batch are
+    // issued before the current one is added, so two batches are in flight
+    // whatever the segment lengths; a batch that crosses segment ends is
+    // added once per segment it holds, each row masked to its own segment.
+    // Every load is issued unconditionally (rows past the chunk read its last
+    // row, lanes past the row read its first 16 bytes, and the values are
+    // dropped), so the wait before a batch is added never has to cover the
+    // batch behind it.
+    const int STEP = RPW * U;
+    struct Batch {
+        u32x4 raw[U];
+        float vs[U][VEC ? 1 : EPL];
+        float wi[U];
+    };
+    // an empty asm statement that reads every register of a batch: the
+    // point where its loads are waited for.  Each use site passes its own
+    // text, so that the compiler cannot merge two of them into one placed
+    // after the paths join.
+#define KM_TOUCH(B, TAG)                                                                  \
+    do {                                                                                  \
+        _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_) {                                \
+            if constexpr (VEC) asm volatile("; " TAG ::"v"((B).raw[u_]));                \
+            else {                                                                        \
+                _Pragma("unroll") for (int t_ = 0; t_ < EPL; ++t_)                        \
+                    asm volatile("; " TAG ::"v"((B).vs[u_][t_]));                         \
+            }                                                                             \
+            if constexpr (WEIGHTED) asm volatile("; " TAG ::"v"((B).wi[u_]));             \
+        }                                                                                 \
+    } while (0)
+    auto load_batch = [&](Batch& B, int32_t bs, int32_t c0, int32_t c1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // row bs + u*RPW + gl, clamped to the chunk's last row; the
+            // wave-uniform part stays scalar
+            const int32_t sb = __builtin_amdgcn_readfirstlane(bs + u * RPW - c0);
+            const int32_t o = gl + sb, last = c1 - 1 - c0;
+            const int32_t ix = sidx[o < last ? o : last];
+            const T* row = Xb + (int64_t)ix * d;
+            if constexpr (VEC) {
+                B.raw[u] = __builtin_nontemporal_load((const u32x4*)(row + (active ? li * EPL : 0)));
+            } else {
+#pragma unroll
+                for (int t = 0; t < EPL; ++t) {
+                    const int k = li + LPR * t;
+                    B.vs[u][t] = ld_elem<T>(row + (k < d ? k : 0));
+                }
+            }
+            if constexpr (WEIGHTED) B.wi[u] = wb[ix];
+        }
+    };
+    int32_t send = 0;
     bool pending = false;  // rows accumulated since the last flush
-    for (int32_t c0 = (int32_t)q0; c0 < q1; c0 += kSegChunk) {
-        const int32_t c1 = (c0 + kSegChunk < q1) ? c0 + kSegChunk : q1;
-        // stage this chunk's point indices in LDS
-        for (int32_t r = c0 + lane; r < c1; r += 64) sidx[r - c0] = pb[r];
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        int32_t q = c0;
-        while (q < c1) {
-            const int32_t e = send < c1 ? send : c1;
-            for (int32_t r = q + gl; r < e; r += RPW * U) {
-                int32_t idx[U];
+    auto add_batch = [&](const Batch& B, int32_t bs, int32_t c1) {
+        // the batch's registers are read on every path, so no later
+        // instruction that reuses them waits on loads issued after them
+        KM_TOUCH(B, "batch");
+        const int32_t be = (bs + STEP < c1) ? bs + STEP : c1;
+        int32_t q = bs;
+        while (q < be) {
+            const int32_t e = send < be ? send : be;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int32_t rr = r + u * RPW;
-                    idx[u] = rr < e ? sidx[rr - c0] : -1;
+            for (int u = 0; u < U; ++u) {
+                // row bs + u*RPW + gl lies in [q, e): bounds on gl are scalar
+                const int32_t su = bs + u * RPW;
+                const bool in = gl >= q - su && gl < e - su;
+                float v[EPL];
+                if constexpr (VEC) {
+                    const u32x4 r = (in && active) ? B.raw[u] : u32x4{0u, 0u, 0u, 0u};
+                    unpack<T>(r, v);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < EPL; ++t) v[t] = (in && li + LPR * t < d) ? B.vs[u][t] : 0.f;
                 }
-                // raw 16-byte loads stay packed until they are accumulated,
-                // which keeps U row steps in flight at a low register cost;
-                // point rows are read once per update, so they bypass the caches
-                u32x4 raw[U];
-                float vs[U][VEC ? 1 : EPL];
-                float wi[U];
+                const float wu = in ? (WEIGHTED ? B.wi[u] : 1.f) : 0.f;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const bool ok = idx[u] >= 0;
-                    const T* row = Xb + (int64_t)(ok ? idx[u] : 0) * d;
-                    if constexpr (VEC) {
-                        raw[u] = (ok && active) ? __builtin_nontemporal_load((const u32x4*)(row + li * EPL))
-                                                : u32x4{0u, 0u, 0u, 0u};
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < EPL; ++t) {
-                            const int k = li + LPR * t;
-                            vs[u][t] = (ok && k < d) ? ld_elem<T>(row + k) : 0.f;
-                        }
-                    }
-                    if constexpr (WEIGHTED) wi[u] = ok ? wb[idx[u]] : 0.f;
-                    else wi[u] = ok ? 1.f : 0.f;
+                for (int t = 0; t < EPL; ++t) {
+                    if constexpr (WEIGHTED) acc[t] = fmaf(wu, v[t], acc[t]);
+                    else acc[t] += v[t];
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float v[EPL];
-                    if constexpr (VEC) unpack<T>(raw[u], v);
-                    else {
-#pragma unroll
-                        for (int t = 0; t < EPL; ++t) v[t] = vs[u][t];
-                    }
-#pragma unroll
-                    for (int t = 0; t < EPL; ++t) {
-                        if constexpr (WEIGHTED) acc[t] = fmaf(wi[u], v[t], acc[t]);
-                        else acc[t] += v[t];
-                    }
-                    wacc += wi[u];
-                }
+                wacc += wu;
             }
             pending = pending || (e > q);
             q = e;
@@ -247,9 +304,36 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
                 if (q < q1) send = locate(q);
             }
         }
+    };
+    Batch A, Bn;
+    // the first chunk's rows are requested before the segment lookup, whose
+    // loads then run under them
+    store_idx((int32_t)q0, c1_first);
+    load_batch(A, (int32_t)q0, (int32_t)q0, c1_first);
+    send = locate((int32_t)q0);
+    for (int32_t c0 = (int32_t)q0; c0 < q1; c0 += kSegChunk) {
+        const int32_t c1 = (c0 + kSegChunk < q1) ? c0 + kSegChunk : q1;
+        if (c0 != (int32_t)q0) {
+            load_idx(c0, c1);
+            store_idx(c0, c1);
+            load_batch(A, c0, c0, c1);
+        }
+        // one exit, at the top: both adds run in every round (an add of a
+        // batch that starts past the chunk only waits for its loads), so no
+        // path back into the loop leaves loads pending in either batch.  A
+        // batch loaded past the chunk's end repeats its last row, which has
+        // just arrived.
+        for (int32_t bs = c0; bs < c1; bs += 2 * STEP) {
+            load_batch(Bn, bs + STEP, c0, c1);
+            add_batch(A, bs, c1);
+            load_batch(A, bs + 2 * STEP, c0, c1);
+            add_batch(Bn, bs + STEP, c1);
+        }
+        KM_TOUCH(A, "past end");
         __builtin_amdgcn_wave_barrier();
     }
     if (pending) flush();
+#undef KM_TOUCH
 }
 
 // Second pass: fold the per-piece slots into the segment sums.  Pieces are in
