@@ -17,10 +17,9 @@
 //                    P[c][j] (the points of bin j in chunks before c), and
 //                    the column totals -> counts; H is cleared for the next
 //                    assignment that builds it.
-//   3. k_scan     -- exclusive prefix of counts -> offsets (and the first
-//                    segment of every reduction piece, and whether every
-//                    cluster is short enough for the one-segment-per-group
-//                    reduction).
+//   3. k_scan     -- exclusive prefix of counts -> offsets (and whether
+//                    every cluster is short enough for the one-segment-per-
+//                    group reduction).
 //   4. k_scatter  -- chunk c places its points of bin j from
 //                    offsets[j] + P[c][j] on, in index order: each wave of
 //                    the block takes a consecutive part of the chunk with its
@@ -29,7 +28,9 @@
 //                    labels at a time; lanes holding the same label find each
 //                    other with one ballot per label bit, the lower lanes
 //                    going first, and the lowest lane of each label advances
-//                    the cursor.
+//                    the cursor.  The lane that places a point at the first
+//                    sorted position of a reduction piece also stores the
+//                    point's label as the piece's first segment.
 // Every step is a deterministic function of the labels, so the whole sort
 // is: run twice on the same labels, it produces the same permutation.
 //
@@ -263,12 +264,16 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
 // count to the placement instead of reading them twice.
 constexpr int kScatterR = 16;
 
+// piece_seg (or NULL): [B][npieces], the first segment of every reduction
+// piece of 2^tw_shift sorted rows, that is the label of the point placed at
+// the piece's first position.
 template <int WB, int NB>
 __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__ labels, int64_t N, int K,
                                                      int64_t CH, int64_t nch,
                                                      const int32_t* __restrict__ P,
                                                      const int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm) {
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ piece_seg,
+                                                     int64_t npieces, int tw_shift) {
     constexpr int R = kScatterR;
     constexpr int BU = 8;  // bins (or groups of 4 bins) per thread and pass
     extern __shared__ __attribute__((aligned(16))) int32_t s_tab[];  // [WB][K]
@@ -379,6 +384,8 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     }
     __syncthreads();
     int32_t* Pb = perm + b * N;
+    int32_t* psb = piece_seg ? piece_seg + b * npieces : nullptr;
+    const int32_t tw_mask = (1 << tw_shift) - 1;
     // one batch of R rounds from r0: every round's grouping first (ballots
     // only, no memory), then the chain of cursor reads and advances
     auto place = [&](int64_t r0, const int32_t (&cur)[R]) {
@@ -394,7 +401,11 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
         for (int u = 0; u < R; ++u) {
             const int32_t l = rank[u] >= 0 ? cur[u] : 0;
             const int32_t base = tab[l];
-            if (rank[u] >= 0) Pb[base + rank[u]] = (int32_t)(r0 + u * 64 + lane);
+            if (rank[u] >= 0) {
+                const int32_t pos = base + rank[u];
+                Pb[pos] = (int32_t)(r0 + u * 64 + lane);
+                if (psb && (pos & tw_mask) == 0) psb[pos >> tw_shift] = cur[u];
+            }
             if (rank[u] == 0) tab[l] = base + cnt[u];
         }
     };
@@ -490,8 +501,14 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
         e = launch_zero(o.counts, (size_t)B * K * sizeof(int32_t), s);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan(o.counts, B, K, o.offsets, nullptr, TW, npieces, o.piece_seg, o.short_flag, s)) !=
-        hipSuccess)
+    // the pieces' first segments come from the scatter where the piece width
+    // is a power of two (always, for the widths the reduction picks), else
+    // from a search of the offsets in the scan
+    int tw_shift = 0;
+    while ((1 << tw_shift) < TW) ++tw_shift;
+    const bool seg_in_scatter = (1 << tw_shift) == TW;
+    if ((e = launch_scan(o.counts, B, K, o.offsets, nullptr, TW, npieces,
+                         seg_in_scatter || N == 0 ? nullptr : o.piece_seg, o.short_flag, s)) != hipSuccess)
         return e;
     if (N == 0) return hipSuccess;
     const int nbits = label_bits(K);
@@ -501,7 +518,8 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
         const size_t lds = (size_t)(WBV) * K * sizeof(int32_t);                                             \
         if ((e = set_lds((const void*)k_scatter<WBV, NBV>, lds)) != hipSuccess) return e;                  \
         hipLaunchKernelGGL((k_scatter<WBV, NBV>), grid, dim3(64 * WBV), lds, s, labels, N, (int)K, CH, nch, \
-                           o.prefix, o.offsets, o.perm);                                                    \
+                           o.prefix, o.offsets, o.perm, seg_in_scatter ? o.piece_seg : nullptr, npieces,    \
+                           tw_shift);                                                                       \
     } while (0)
     // waves per block: as many K-bin cursor tables as fit in 128 KB of LDS
     // (K <= 4096: 8, 8192: 4, 16384: 2, 32768: 1); labels of nbits bits
