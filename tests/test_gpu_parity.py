@@ -245,6 +245,41 @@ def test_update_short_segments(km, dtype, d, weighted, big):
     np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
 
 
+@pytest.mark.parametrize("dtype,d,weighted", [("f16", 64, False), ("bf16", 128, True), ("f32", 16, True)])
+def test_update_segments_aligned_to_pieces(km, dtype, d, weighted):
+    """Segment starts on the reduction pieces' first rows, with empty clusters
+    around them.  At N = 16384 the pieces hold 32 sorted rows; cluster sizes
+    of 32 and 64 put segment starts exactly on piece starts (the piece then
+    begins a segment and stores no continuation slot), empty clusters sit
+    between them (a piece's first segment is the non-empty one after them),
+    and sizes of 1, 31, 33 and a 1504-point cluster shift the alignment
+    between runs of aligned segments and make segments span many pieces."""
+    N, K = 16384, 700
+    pattern = [32, 0, 32, 0, 0, 64, 1, 31, 32, 33, 0, 31, 64, 0, 32, 1504, 32, 0, 1, 63]
+    sizes = []
+    while sum(sizes) < N and len(sizes) < K:
+        sizes.append(pattern[len(sizes) % len(pattern)])
+    sizes[-1] -= sum(sizes) - N if sum(sizes) > N else 0
+    if sum(sizes) < N:
+        sizes[0] += N - sum(sizes)
+    sizes += [0] * (K - len(sizes))
+    assert sum(sizes) == N and len(sizes) == K
+    rng = np.random.default_rng(d + 7)
+    lab = np.repeat(np.arange(K, dtype=np.int32), sizes)
+    lab = lab[rng.permutation(N)].reshape(1, N)
+    x, C = _rand_problem(1, N, d, K, dtype, seed=d + 11)
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, (1, N)).astype(np.float32)) if weighted else None
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(lab).cuda(), C.cuda(),
+                                     weights=None if w is None else w.cuda())
+    X = oracle.decode(workloads.raw_bits(x), dtype)
+    ref_c, ref_n, _, _ = oracle.update(X, None if w is None else w.numpy(), lab, C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    np.testing.assert_array_equal(ref_n[0], np.asarray(sizes))
+    parity.check_centroids(c_new.cpu().numpy(), ref_c, f"aligned segments {dtype} d{d} w{weighted}")
+    empty = ref_n == 0
+    np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
+
+
 @pytest.mark.parametrize("dtype,d,weighted", [("bf16", 128, False), ("f16", 64, True), ("f32", 1, True)])
 def test_update_parity_zipf_sizes(km, dtype, d, weighted):
     """Cluster sizes with a power-law tail: the largest segments span hundreds
