@@ -30,7 +30,9 @@ def main() -> int:
     run_env.update(
         KM_LIBRARY=os.path.join(ROOT, "exact_lloyd_means_03_amd", "_build_san", "libkmeans_mi355x.so"),
         KM_ORACLE_LIBRARY=os.path.join(ROOT, "oracle", "_build_san", "liblloyd_oracle.so"),
-        LD_PRELOAD=rt[-1],
+        # the sanitizer runtime goes first; whatever the environment already
+        # preloads stays loaded after it
+        LD_PRELOAD=":".join(x for x in (rt[-1], os.environ.get("LD_PRELOAD", "")) if x),
         # the interpreter and torch keep memory until exit: leaks are not checked
         ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=0",
         UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1",
