@@ -300,15 +300,19 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     // 16-byte rows: thread tid takes the groups of 4 bins tid, tid + 64 WB, ...
     const bool vec = (K & 3) == 0 && ((uintptr_t)ob & 15) == 0 && ((uintptr_t)Pc & 15) == 0;  // (block-uniform)
     const int K4 = K >> 2;
-    auto load_bases4 = [&](int q0, i32x4 (&base)[BU]) {
+    // the two rows are kept apart until the bases are formed, so that the
+    // first pass's loads are waited for together with the labels' (after the
+    // table clear), not before the clear
+    auto load_bases4 = [&](int q0, i32x4 (&ov)[BU], i32x4 (&pv)[BU]) {
 #pragma unroll
         for (int e = 0; e < BU; ++e) {
             const int q = q0 + e * 64 * WB;
-            base[e] = q < K4 ? ((const i32x4*)ob)[q] + ((const i32x4*)Pc)[q] : i32x4{0, 0, 0, 0};
+            ov[e] = q < K4 ? ((const i32x4*)ob)[q] : i32x4{0, 0, 0, 0};
+            pv[e] = q < K4 ? ((const i32x4*)Pc)[q] : i32x4{0, 0, 0, 0};
         }
     };
-    i32x4 base0[BU];
-    if (vec) load_bases4(tid, base0);
+    i32x4 ob0[BU], pc0[BU];
+    if (vec) load_bases4(tid, ob0, pc0);
     const bool keep = part <= 2 * 64 * R;  // (a block-uniform choice)
     int32_t kept[2][R];
     if ((K & 3) == 0) {
@@ -342,9 +346,12 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
             i32x4 base[BU];
             if (q0 == tid) {
 #pragma unroll
-                for (int e = 0; e < BU; ++e) base[e] = base0[e];
+                for (int e = 0; e < BU; ++e) base[e] = ob0[e] + pc0[e];
             } else {
-                load_bases4(q0, base);
+                i32x4 ov[BU], pv[BU];
+                load_bases4(q0, ov, pv);
+#pragma unroll
+                for (int e = 0; e < BU; ++e) base[e] = ov[e] + pv[e];
             }
 #pragma unroll
             for (int e = 0; e < BU; ++e) {
