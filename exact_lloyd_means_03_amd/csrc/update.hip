@@ -8,9 +8,11 @@
 // gfx950 layout (ours): the sorted positions are cut into pieces of TW rows,
 // one piece per 64-lane wave.  A point row is read with 16-byte loads by LPR
 // lanes (d=128 bf16: 16 lanes), so one wave gathers 64/LPR rows per step and
-// keeps U steps of loads in flight.  At a segment boundary the wave reduces
-// its row groups with cross-lane shuffles.  The first segment of every piece
-// is precomputed by the scan, and the following segment boundaries come from
+// keeps two batches of U steps of loads in flight.  At a segment boundary the
+// wave reduces its row groups with cross-lane shuffles.  The first segment of every piece
+// comes with the sort (the stable scatter stores the label of the point it
+// places at a piece's first position; the unordered variant's scan searches
+// the offsets for it), and the following segment boundaries come from
 // a 64-entry window of offsets held one per lane, so a wave never searches
 // device memory serially.
 //
@@ -589,7 +591,7 @@ int segreduce_tw(int64_t B, int64_t N) {
     return (int)tw;
 }
 
-// piece_seg: the first segment of every piece, written by the scan of the sort.
+// piece_seg: the first segment of every piece, written by the sort.
 hipError_t launch_segreduce(DType xt, const void* x, const float* w, int64_t B, int64_t N, int d,
                             const int32_t* perm, const int32_t* offsets, int64_t K, float* sums,
                             float* wsum, const int32_t* piece_seg, float* slot, float* wslot, float* gslot,
