@@ -9,12 +9,12 @@
 // one piece per 64-lane wave.  A point row is read with 16-byte loads by LPR
 // lanes (d=128 bf16: 16 lanes), so one wave gathers 64/LPR rows per step and
 // keeps two batches of U steps of loads in flight.  At a segment boundary the
-// wave reduces its row groups with cross-lane shuffles.  The first segment of every piece
-// comes with the sort (the stable scatter stores the label of the point it
-// places at a piece's first position; the unordered variant's scan searches
-// the offsets for it), and the following segment boundaries come from
-// a 64-entry window of offsets held one per lane, so a wave never searches
-// device memory serially.
+// wave reduces its row groups with cross-lane shuffles.  The first segment of
+// every piece comes with the sort (the stable scatter stores the label of the
+// point it places at a piece's first position; the unordered variant's scan
+// searches the offsets for it), and the following segment boundaries come
+// from a 64-entry window of offsets held one per lane, so a wave never
+// searches device memory serially.
 //
 // Where the partial sums go: a segment that starts inside a piece is stored
 // by that piece with plain stores, since no other piece writes it directly
