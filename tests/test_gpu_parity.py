@@ -245,6 +245,30 @@ def test_update_short_segments(km, dtype, d, weighted, big):
     np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
 
 
+@pytest.mark.parametrize("dtype,d,weighted", [("f16", 8, True), ("bf16", 6, False), ("f32", 12, True)])
+def test_update_long_pieces(km, dtype, d, weighted):
+    """Pieces longer than one staged chunk of 512 sorted rows: at 9M points the
+    reduction takes pieces of 1024 rows, so every piece stages its indices
+    twice and its batches run across the chunk boundary (16-byte rows at d = 8
+    fp16 and d = 12 fp32, element-wise rows at d = 6 bf16).  Cluster sizes
+    follow a power law, so segments range from empty to millions of rows."""
+    B, N, K = 1, 9_000_000, 3000
+    x, C = _rand_problem(B, N, d, K, dtype, seed=d + 21)
+    rng = np.random.default_rng(d + 22)
+    pk = np.arange(1, K + 1, dtype=np.float64) ** -1.1
+    pk /= pk.sum()
+    lab = rng.permutation(K)[rng.choice(K, size=(B, N), p=pk)].astype(np.int32)
+    w = torch.from_numpy(rng.uniform(0.1, 1.0, (B, N)).astype(np.float32)) if weighted else None
+    c_new, counts = km.kmeans_update(x.cuda(), torch.from_numpy(lab).cuda(), C.cuda(),
+                                     weights=None if w is None else w.cuda())
+    X = oracle.decode(workloads.raw_bits(x), dtype)
+    ref_c, ref_n, _, _ = oracle.update(X, None if w is None else w.numpy(), lab, C.numpy())
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_n)
+    parity.check_centroids(c_new.cpu().numpy(), ref_c, f"long pieces {dtype} d{d} w{weighted}")
+    empty = ref_n == 0
+    np.testing.assert_array_equal(c_new.cpu().numpy()[empty], C.numpy()[empty])
+
+
 @pytest.mark.parametrize("dtype,d,weighted", [("f16", 64, False), ("bf16", 128, True), ("f32", 16, True)])
 def test_update_segments_aligned_to_pieces(km, dtype, d, weighted):
     """Segment starts on the reduction pieces' first rows, with empty clusters
