@@ -99,9 +99,10 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(const int32_t* __restrict
 // back to H (the assignment of the next iteration adds into it).
 constexpr int kColBins = 64, kColQ = 16, kColMaxPer = 16;
 
-// obj_out (may be NULL): the first block of each problem also sums the
-// assignment's objective partials of the problem (obj_sum_1024), which saves
-// the objective's own launch inside a fit.
+// obj_out (may be NULL): one extra block per problem, after the bin blocks,
+// sums the assignment's objective partials of the problem (obj_sum_1024),
+// which saves the objective's own launch inside a fit; a block of its own
+// runs beside the bin blocks instead of lengthening one of them.
 static_assert(kColBins * kColQ == 1024, "the objective sum takes a block of 1024 threads");
 
 __global__ __launch_bounds__(kColBins* kColQ) void k_colscan(int32_t* __restrict__ H, int64_t nch, int K,
@@ -113,7 +114,10 @@ __global__ __launch_bounds__(kColBins* kColQ) void k_colscan(int32_t* __restrict
     __shared__ double s_red[1024];
     const int jl = threadIdx.x % kColBins, q = threadIdx.x / kColBins;
     const int64_t b = blockIdx.y;
-    if (obj_out && blockIdx.x == 0) obj_sum_1024(obj_part + b * obj_nblk, obj_nblk, obj_out + b * obj_stride, s_red);
+    if ((int)blockIdx.x == (K + kColBins - 1) / kColBins) {  // the objective's block
+        if (obj_out) obj_sum_1024(obj_part + b * obj_nblk, obj_nblk, obj_out + b * obj_stride, s_red);
+        return;
+    }
     const int j = blockIdx.x * kColBins + jl;
     const int64_t per = (nch + kColQ - 1) / kColQ;  // <= kColMaxPer
     const int64_t c0 = q * per;
@@ -501,7 +505,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
     }
     // StableCounted with N == 0: the rows are zero already
     if (N > 0) {
-        hipLaunchKernelGGL(k_colscan, dim3((unsigned)((K + kColBins - 1) / kColBins), (unsigned)B),
+        hipLaunchKernelGGL(k_colscan, dim3((unsigned)((K + kColBins - 1) / kColBins + (o.obj_out ? 1 : 0)), (unsigned)B),
                            dim3(kColBins * kColQ), 0, s, o.hist, nch, (int)K, o.prefix, o.counts,
                            mode == SortMode::StableCounted, o.obj_part, o.obj_nblk, o.obj_out, o.obj_stride);
     } else {
