@@ -79,23 +79,25 @@ __device__ __forceinline__ void unpack(const u32x4 u, float* out) {
 // are flushed whenever a segment ends and at the end of the piece.
 constexpr int kSegChunk = 512;
 
+// One piece per wave; a block holds the kFoldG pieces of one fold group.
 template <typename T, bool VEC, bool WEIGHTED>
-__global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, const float* __restrict__ w,
-                                                   int64_t N, int d, int lpr_shift,
-                                                   const int32_t* __restrict__ perm,
-                                                   const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ piece_seg, int64_t npieces,
-                                                   int K, int TW, float* __restrict__ sums,
-                                                   float* __restrict__ wsum, float* __restrict__ slot,
-                                                   float* __restrict__ wslot, bool accumulate,
-                                                   const int32_t* __restrict__ skip) {
+__device__ __forceinline__ void segreduce_piece(const T* __restrict__ X, const float* __restrict__ w, int64_t N,
+                                                int d, int lpr_shift, const int32_t* __restrict__ perm,
+                                                const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ piece_seg, int64_t npieces, int K,
+                                                int TW, float* __restrict__ sums, float* __restrict__ wsum,
+                                                float* __restrict__ slot, float* __restrict__ wslot,
+                                                bool accumulate, const int32_t* __restrict__ skip,
+                                                int32_t (*s_idx)[kSegChunk]) {
     constexpr int EPL = VEC ? 16 / (int)sizeof(T) : 8;  // non-vector rows: 64 lanes x 8 = 512 elements
-    constexpr int U = VEC ? 8 : 4;  // row steps per batch (two batches in flight)
-    __shared__ int32_t s_idx[4][kSegChunk];
+    // row steps per batch (two batches in flight); rows read one element per
+    // lane hold EPL values per step, and a block of kFoldG waves leaves 128
+    // VGPRs per lane
+    constexpr int U = VEC ? 8 : (WEIGHTED ? 1 : 2);
     // wv is uniform over the wave: saying so keeps the piece's bounds and
     // every loop over them in scalar registers and scalar branches
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t piece = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t piece = (int64_t)blockIdx.x * kFoldG + wv;
     const int64_t b = blockIdx.y;
     if (piece >= npieces) return;
     if (skip && skip[b]) return;  // reduced by k_segsum_short
@@ -338,6 +340,37 @@ __global__ __launch_bounds__(256) void k_segreduce(const T* __restrict__ X, cons
 #undef KM_TOUCH
 }
 
+template <bool WEIGHTED>
+__device__ __forceinline__ void fold_group(int64_t g, int64_t b, int lane, const float* __restrict__ slot,
+                                           const float* __restrict__ wslot, const int32_t* __restrict__ piece_seg,
+                                           const int32_t* __restrict__ offsets, int64_t npieces, int64_t ngroups,
+                                           int K, int TW, int d, float* __restrict__ gslot,
+                                           float* __restrict__ gwslot);
+
+// The segmented reduction of kFoldG pieces per block, then (gslot set: the
+// deterministic Lloyd fold) the fold of the block's own group: once every
+// piece of the block has stored its slot, wave 0 adds the slots of the
+// group's first run in piece order into the group slot (fold_group below).
+template <typename T, bool VEC, bool WEIGHTED>
+__global__ __launch_bounds__(64 * kFoldG) void k_segreduce(
+    const T* __restrict__ X, const float* __restrict__ w, int64_t N, int d, int lpr_shift,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets, const int32_t* __restrict__ piece_seg,
+    int64_t npieces, int K, int TW, float* __restrict__ sums, float* __restrict__ wsum, float* __restrict__ slot,
+    float* __restrict__ wslot, bool accumulate, const int32_t* __restrict__ skip, int64_t ngroups,
+    float* __restrict__ gslot, float* __restrict__ gwslot) {
+    __shared__ int32_t s_idx[kFoldG][kSegChunk];
+    segreduce_piece<T, VEC, WEIGHTED>(X, w, N, d, lpr_shift, perm, offsets, piece_seg, npieces, K, TW, sums, wsum,
+                                      slot, wslot, accumulate, skip, s_idx);
+    if (gslot) {
+        // the slots of every piece of the group are stored and visible to
+        // the block after the barrier
+        __syncthreads();
+        if (threadIdx.x < 64 && !(skip && skip[blockIdx.y]))  // (skip: reduced by k_segsum_short)
+            fold_group<WEIGHTED>(blockIdx.x, blockIdx.y, threadIdx.x, slot, wslot, piece_seg, offsets, npieces,
+                                 ngroups, K, TW, d, gslot, gwslot);
+    }
+}
+
 // Second pass: fold the per-piece slots into the segment sums.  Pieces are in
 // sorted order, so the pieces that share a first segment are consecutive;
 // each wave walks kFoldG of them and issues one atomic per coordinate per
@@ -428,18 +461,13 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
 // group.  A group whose first piece starts a segment holds no slot there and
 // stores nothing (no segment reads it).
 template <bool WEIGHTED>
-__global__ __launch_bounds__(256) void k_fold_groups(const float* __restrict__ slot, const float* __restrict__ wslot,
-                                                     const int32_t* __restrict__ piece_seg,
-                                                     const int32_t* __restrict__ offsets, int64_t npieces,
-                                                     int64_t ngroups, int K, int TW, int d,
-                                                     float* __restrict__ gslot, float* __restrict__ gwslot,
-                                                     const int32_t* __restrict__ skip) {
+__device__ __forceinline__ void fold_group(int64_t g, int64_t b, int lane, const float* __restrict__ slot,
+                                           const float* __restrict__ wslot, const int32_t* __restrict__ piece_seg,
+                                           const int32_t* __restrict__ offsets, int64_t npieces, int64_t ngroups,
+                                           int K, int TW, int d, float* __restrict__ gslot,
+                                           float* __restrict__ gwslot) {
     constexpr int U = 8;
-    const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t b = blockIdx.y;
     if (g >= ngroups) return;
-    if (skip && skip[b]) return;  // reduced by k_segsum_short
     const int32_t* offb = offsets + b * (K + 1);
     const int32_t total = offb[K];
     const int64_t np = ((int64_t)total + TW - 1) / TW;  // pieces that hold rows
@@ -639,10 +667,12 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 grid((unsigned)((npieces + 3) / 4), (unsigned)B);
-#define KM_SEG(T, V, W)                                                                                   \
-    hipLaunchKernelGGL((k_segreduce<T, V, W>), grid, dim3(256), 0, s, (const T*)x, w, N, d, shift, perm, \
-                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot, accumulate, skip)
+    const int64_t ng = fold_groups(npieces);
+    dim3 grid((unsigned)ng, (unsigned)B);
+#define KM_SEG(T, V, W)                                                                                        \
+    hipLaunchKernelGGL((k_segreduce<T, V, W>), grid, dim3(64 * kFoldG), 0, s, (const T*)x, w, N, d, shift, perm, \
+                       offsets, piece_seg, npieces, (int)K, TW, sums, wsum, slot, wslot, accumulate, skip, ng,    \
+                       gslot, gwslot)
 #define KM_SEG_T(T)                      \
     if (vec) {                           \
         if (w) KM_SEG(T, true, true);    \
@@ -658,17 +688,10 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
 #undef KM_SEG
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the deterministic fold's group slots came with the reduction; sums
+    // that accumulate over launches take the atomic fold
+    if (gslot) return hipSuccess;
     dim3 fgrid((unsigned)((npieces + 4 * kFoldG - 1) / (4 * kFoldG)), (unsigned)B);
-    if (gslot) {
-        const int64_t ng = fold_groups(npieces);
-        if (w)
-            hipLaunchKernelGGL(k_fold_groups<true>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
-                               ng, (int)K, TW, d, gslot, gwslot, skip);
-        else
-            hipLaunchKernelGGL(k_fold_groups<false>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets,
-                               npieces, ng, (int)K, TW, d, gslot, gwslot, skip);
-        return hipGetLastError();
-    }
     if (w)
         hipLaunchKernelGGL(k_fold_slots<true>, fgrid, dim3(256), 0, s, slot, wslot, piece_seg, offsets, npieces,
                            (int)K, TW, d, sums, wsum, skip);
