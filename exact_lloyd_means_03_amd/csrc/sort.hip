@@ -19,7 +19,11 @@
 //                    assignment that builds it.
 //   3. k_scan     -- exclusive prefix of counts -> offsets (and whether
 //                    every cluster is short enough for the one-segment-per-
-//                    group reduction).
+//                    group reduction).  With 16-byte count and prefix rows
+//                    the scatter forms the offsets itself instead (each
+//                    block scans the counts row it reads anyway; the block
+//                    of chunk 0 stores them and the flag), and this launch
+//                    is skipped.
 //   4. k_scatter  -- chunk c places its points of bin j from
 //                    offsets[j] + P[c][j] on, in index order: each wave of
 //                    the block takes a consecutive part of the chunk with its
@@ -271,16 +275,31 @@ constexpr int kScatterR = 16;
 // piece_seg (or NULL): [B][npieces], the first segment of every reduction
 // piece of 2^tw_shift sorted rows, that is the label of the point placed at
 // the piece's first position.
-template <int WB, int NB>
+//
+// SCAN (K a multiple of 4, 16-byte aligned count and prefix rows): the
+// offsets are not read but formed by every block from the counts row, the
+// exclusive prefix of the counts in bin order, which saves the scan's own
+// launch; the block of chunk 0 stores them (offsets[b][0..K]) and the
+// problem's short-segment flag.  A pass of the base loop covers 64 WB BU
+// groups of 4 bins: thread t holds groups t + 64 WB e, e < BU, so round e of
+// a pass is 256 WB consecutive bins, 4 per thread in thread order; one wave
+// scan per round (BU at once) and one barrier per pass give each bin its
+// prefix.
+template <int WB, int NB, bool SCAN>
 __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__ labels, int64_t N, int K,
                                                      int64_t CH, int64_t nch,
                                                      const int32_t* __restrict__ P,
-                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ offsets_in,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ piece_seg,
-                                                     int64_t npieces, int tw_shift) {
+                                                     int64_t npieces, int tw_shift,
+                                                     const int32_t* __restrict__ counts,
+                                                     int32_t* offsets_out,  // (the same buffer as offsets_in)
+                                                     int32_t* __restrict__ short_flag) {
     constexpr int R = kScatterR;
     constexpr int BU = 8;  // bins (or groups of 4 bins) per thread and pass
     extern __shared__ __attribute__((aligned(16))) int32_t s_tab[];  // [WB][K]
+    __shared__ int32_t s_ws[SCAN ? BU : 1][WB];  // SCAN: wave totals of each round of a pass
+    __shared__ int32_t s_max;                    // SCAN: the largest count
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t b = blockIdx.y, c = blockIdx.x;
     const int64_t i0 = c * CH;
@@ -300,9 +319,10 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     // cursor of bin j for wave w: where the chunk's points of bin j start,
     // plus those of the earlier waves
     const int32_t* Pc = P + (b * nch + c) * (int64_t)K;
-    const int32_t* ob = offsets + b * (K + 1);
+    // SCAN: the first row loaded with the prefix rows is the counts row
+    const int32_t* ob = SCAN ? counts + b * K : offsets_in + b * (K + 1);
     // 16-byte rows: thread tid takes the groups of 4 bins tid, tid + 64 WB, ...
-    const bool vec = (K & 3) == 0 && ((uintptr_t)ob & 15) == 0 && ((uintptr_t)Pc & 15) == 0;  // (block-uniform)
+    const bool vec = SCAN || ((K & 3) == 0 && ((uintptr_t)ob & 15) == 0 && ((uintptr_t)Pc & 15) == 0);  // (block-uniform)
     const int K4 = K >> 2;
     // the two rows are kept apart until the bases are formed, so that the
     // first pass's loads are waited for together with the labels' (after the
@@ -325,6 +345,7 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     } else {
         for (int j = lane; j < K; j += 64) tab[j] = 0;
     }
+    if (SCAN && tid == 0) s_max = 0;
     __builtin_amdgcn_wave_barrier();
     // this wave's histogram, R labels in flight per lane
     if (keep) {
@@ -345,7 +366,93 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
         }
     }
     __syncthreads();
-    if (vec) {
+    if constexpr (SCAN) {
+        // passes are block-uniform (every thread reaches every barrier)
+        constexpr int NT = 64 * WB;
+        int32_t* ob_out = offsets_out + b * (K + 1);
+        int32_t carry = 0, vmax = 0;  // bins of earlier passes; the largest count
+        for (int p0 = 0; p0 < K4; p0 += NT * BU) {
+            const int q0 = p0 + tid;
+            i32x4 cv[BU], pv[BU];
+            if (p0 == 0) {
+#pragma unroll
+                for (int e = 0; e < BU; ++e) {
+                    cv[e] = ob0[e];
+                    pv[e] = pc0[e];
+                }
+            } else {
+                load_bases4(q0, cv, pv);
+            }
+            int32_t sum[BU], incl[BU];
+#pragma unroll
+            for (int e = 0; e < BU; ++e) {
+                sum[e] = cv[e][0] + cv[e][1] + cv[e][2] + cv[e][3];
+                const int32_t m01 = cv[e][0] > cv[e][1] ? cv[e][0] : cv[e][1];
+                const int32_t m23 = cv[e][2] > cv[e][3] ? cv[e][2] : cv[e][3];
+                const int32_t m = m01 > m23 ? m01 : m23;
+                vmax = m > vmax ? m : vmax;
+                incl[e] = sum[e];
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+                for (int e = 0; e < BU; ++e) {
+                    const int32_t t = __shfl_up(incl[e], o, 64);
+                    if (lane >= o) incl[e] += t;
+                }
+            }
+            if (lane == 63) {
+#pragma unroll
+                for (int e = 0; e < BU; ++e) s_ws[e][w] = incl[e];
+            }
+            __syncthreads();
+            int32_t run = carry;
+#pragma unroll
+            for (int e = 0; e < BU; ++e) {
+                int32_t before = 0, tot = 0;
+#pragma unroll
+                for (int v = 0; v < WB; ++v) {
+                    const int32_t t = s_ws[e][v];
+                    before += v < w ? t : 0;
+                    tot += t;
+                }
+                const int q = q0 + e * NT;
+                i32x4 o;
+                o[0] = run + before + incl[e] - sum[e];
+                o[1] = o[0] + cv[e][0];
+                o[2] = o[1] + cv[e][1];
+                o[3] = o[2] + cv[e][2];
+                run += tot;
+                if (q < K4) {
+                    if (c == 0) {
+                        ob_out[4 * q + 0] = o[0];
+                        ob_out[4 * q + 1] = o[1];
+                        ob_out[4 * q + 2] = o[2];
+                        ob_out[4 * q + 3] = o[3];
+                    }
+                    i32x4 base = o + pv[e];
+#pragma unroll
+                    for (int v = 0; v < WB; ++v) {
+                        i32x4* t4 = (i32x4*)(s_tab + v * K) + q;
+                        const i32x4 cnt = *t4;
+                        *t4 = base;
+                        base += cnt;
+                    }
+                }
+            }
+            carry = run;
+            __syncthreads();  // s_ws is rewritten by the next pass
+        }
+        if (c == 0) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const int32_t t = __shfl_xor(vmax, o, 64);
+                vmax = t > vmax ? t : vmax;
+            }
+            if (lane == 0) atomicMax(&s_max, vmax);
+            if (tid == 0) ob_out[K] = carry;
+        }
+    } else if (vec) {
         for (int q0 = tid; q0 < K4; q0 += 64 * WB * BU) {
             i32x4 base[BU];
             if (q0 == tid) {
@@ -394,6 +501,7 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
         }
     }
     __syncthreads();
+    if (SCAN && c == 0 && tid == 0 && short_flag) short_flag[b] = s_max <= kShortSegMax ? 1 : 0;
     int32_t* Pb = perm + b * N;
     int32_t* psb = piece_seg ? piece_seg + b * npieces : nullptr;
     const int32_t tw_mask = (1 << tw_shift) - 1;
@@ -518,19 +626,29 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
     int tw_shift = 0;
     while ((1 << tw_shift) < TW) ++tw_shift;
     const bool seg_in_scatter = (1 << tw_shift) == TW;
-    if ((e = launch_scan(o.counts, B, K, o.offsets, nullptr, TW, npieces,
-                         seg_in_scatter || N == 0 ? nullptr : o.piece_seg, o.short_flag, s)) != hipSuccess)
-        return e;
+    // the scatter forms the offsets itself from 16-byte count and prefix rows
+    const bool scan_in_scatter = N > 0 && seg_in_scatter && (K & 3) == 0 && ((uintptr_t)o.counts & 15) == 0 &&
+                                 ((uintptr_t)o.prefix & 15) == 0;
+    if (!scan_in_scatter) {
+        if ((e = launch_scan(o.counts, B, K, o.offsets, nullptr, TW, npieces,
+                             seg_in_scatter || N == 0 ? nullptr : o.piece_seg, o.short_flag, s)) != hipSuccess)
+            return e;
+    }
     if (N == 0) return hipSuccess;
     const int nbits = label_bits(K);
     const dim3 grid((unsigned)nch, (unsigned)B);
-#define KM_SCATTER(WBV, NBV)                                                                                \
-    do {                                                                                                    \
-        const size_t lds = (size_t)(WBV) * K * sizeof(int32_t);                                             \
-        if ((e = set_lds((const void*)k_scatter<WBV, NBV>, lds)) != hipSuccess) return e;                  \
-        hipLaunchKernelGGL((k_scatter<WBV, NBV>), grid, dim3(64 * WBV), lds, s, labels, N, (int)K, CH, nch, \
-                           o.prefix, o.offsets, o.perm, seg_in_scatter ? o.piece_seg : nullptr, npieces,    \
-                           tw_shift);                                                                       \
+#define KM_SCATTER_S(WBV, NBV, SC)                                                                            \
+    do {                                                                                                      \
+        const size_t lds = (size_t)(WBV) * K * sizeof(int32_t);                                               \
+        if ((e = set_lds((const void*)k_scatter<WBV, NBV, SC>, lds)) != hipSuccess) return e;                \
+        hipLaunchKernelGGL((k_scatter<WBV, NBV, SC>), grid, dim3(64 * WBV), lds, s, labels, N, (int)K, CH, nch, \
+                           o.prefix, o.offsets, o.perm, seg_in_scatter ? o.piece_seg : nullptr, npieces,      \
+                           tw_shift, o.counts, o.offsets, o.short_flag);                                      \
+    } while (0)
+#define KM_SCATTER(WBV, NBV)                        \
+    do {                                            \
+        if (scan_in_scatter) KM_SCATTER_S(WBV, NBV, true); \
+        else KM_SCATTER_S(WBV, NBV, false);         \
     } while (0)
     // waves per block: as many K-bin cursor tables as fit in 128 KB of LDS
     // (K <= 4096: 8, 8192: 4, 16384: 2, 32768: 1); labels of nbits bits
@@ -540,6 +658,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
     else if (nbits <= 14) KM_SCATTER(2, 14);
     else KM_SCATTER(1, 15);
 #undef KM_SCATTER
+#undef KM_SCATTER_S
     return hipGetLastError();
 }
 
