@@ -301,7 +301,13 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     __shared__ int32_t s_ws[SCAN ? BU : 1][WB];  // SCAN: wave totals of each round of a pass
     __shared__ int32_t s_max;                    // SCAN: the largest count
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t b = blockIdx.y, c = blockIdx.x;
+    // Consecutive blocks go to the 8 XCDs in turn, each with its own L2; the
+    // points of one cluster sit in the permutation in chunk order, so with
+    // nch a multiple of 8 every XCD takes a contiguous range of chunks, and
+    // a 128-byte line of the permutation is written from two or three L2s
+    // instead of all eight.
+    const int64_t b = blockIdx.y;
+    const int64_t c = (nch & 7) == 0 ? (int64_t)(blockIdx.x & 7) * (nch >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int64_t i0 = c * CH;
     const int64_t i1 = (i0 + CH < N) ? i0 + CH : N;
     const int64_t part = ((i1 - i0 + WB - 1) / WB + 63) / 64 * 64;  // whole rounds per wave
