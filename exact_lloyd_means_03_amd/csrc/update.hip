@@ -378,7 +378,8 @@ __global__ __launch_bounds__(64 * kFoldG) void k_segreduce(
 // only (its pieces / kFoldG) atomic flushes.  The order of those atomics
 // varies from run to run; this fold serves the sums that accumulate over
 // several launches and the mini-batch steps, the Lloyd update folds
-// deterministically (k_fold_groups, then the divide).
+// deterministically (the group fold at the end of each k_segreduce block,
+// then the divide).
 int64_t fold_groups(int64_t npieces) { return (npieces + kFoldG - 1) / kFoldG; }
 
 template <bool WEIGHTED>
