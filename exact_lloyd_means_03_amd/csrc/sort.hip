@@ -49,12 +49,14 @@ namespace km {
 
 constexpr int kHistThreads = 512;
 
-// Labels per chunk: a power of two, at least 4096 and K, doubled until the
+// Labels per chunk: a power of two, at least 512 and K, doubled until the
 // whole job takes at most 256 chunks (or one chunk per problem).  A chunk is
 // a whole number of every assignment point group (those hold 128..512
 // points), so the assignment can add a group's labels to its chunk's row.
+// Small jobs thus spread their scatter over more blocks (8192 labels with K
+// = 256: 16 chunks of 512 instead of 2 of 4096).
 int64_t sort_chunk(int64_t B, int64_t N, int64_t K) {
-    int64_t ch = 4096;
+    int64_t ch = 512;
     while (ch < K) ch *= 2;
     while (ch < N && B * ((N + ch - 1) / ch) > 256) ch *= 2;
     return ch;
