@@ -21,8 +21,11 @@
 // (added with atomics instead when the sums accumulate over several
 // launches, as in the chunked streaming fit).
 // A piece's first segment (which may have begun in earlier pieces) is
-// written to the piece's own slot instead, and a second, small kernel adds
-// runs of slots into the sums with atomics after the first has finished.
+// written to the piece's own slot instead.  The Lloyd update adds the slots
+// in a fixed order (each block of kFoldG pieces sums its group's first run
+// at its end, and the divide adds the rest); sums that accumulate over
+// launches take a second, small kernel that adds runs of slots into the
+// sums with atomics after the first has finished.
 // Without that split, the pieces of a very large cluster (the head of a Zipf
 // size distribution spans thousands of pieces) would all finish together and
 // serialize on the same addresses; and device-wide float atomics are slow on
