@@ -291,11 +291,10 @@ template <int WB, int NB, bool SCAN>
 __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__ labels, int64_t N, int K,
                                                      int64_t CH, int64_t nch,
                                                      const int32_t* __restrict__ P,
-                                                     const int32_t* __restrict__ offsets_in,
+                                                     int32_t* offsets,  // read, or with SCAN written
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ piece_seg,
                                                      int64_t npieces, int tw_shift,
                                                      const int32_t* __restrict__ counts,
-                                                     int32_t* offsets_out,  // (the same buffer as offsets_in)
                                                      int32_t* __restrict__ short_flag) {
     constexpr int R = kScatterR;
     constexpr int BU = 8;  // bins (or groups of 4 bins) per thread and pass
@@ -328,7 +327,7 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     // plus those of the earlier waves
     const int32_t* Pc = P + (b * nch + c) * (int64_t)K;
     // SCAN: the first row loaded with the prefix rows is the counts row
-    const int32_t* ob = SCAN ? counts + b * K : offsets_in + b * (K + 1);
+    const int32_t* ob = SCAN ? counts + b * K : offsets + b * (K + 1);
     // 16-byte rows: thread tid takes the groups of 4 bins tid, tid + 64 WB, ...
     const bool vec = SCAN || ((K & 3) == 0 && ((uintptr_t)ob & 15) == 0 && ((uintptr_t)Pc & 15) == 0);  // (block-uniform)
     const int K4 = K >> 2;
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(64 * WB) void k_scatter(const int32_t* __restrict__
     if constexpr (SCAN) {
         // passes are block-uniform (every thread reaches every barrier)
         constexpr int NT = 64 * WB;
-        int32_t* ob_out = offsets_out + b * (K + 1);
+        int32_t* ob_out = offsets + b * (K + 1);
         int32_t carry = 0, vmax = 0;  // bins of earlier passes; the largest count
         for (int p0 = 0; p0 < K4; p0 += NT * BU) {
             const int q0 = p0 + tid;
@@ -651,7 +650,7 @@ hipError_t launch_sort(const int32_t* labels, int64_t B, int64_t N, int64_t K, c
         if ((e = set_lds((const void*)k_scatter<WBV, NBV, SC>, lds)) != hipSuccess) return e;                \
         hipLaunchKernelGGL((k_scatter<WBV, NBV, SC>), grid, dim3(64 * WBV), lds, s, labels, N, (int)K, CH, nch, \
                            o.prefix, o.offsets, o.perm, seg_in_scatter ? o.piece_seg : nullptr, npieces,      \
-                           tw_shift, o.counts, o.offsets, o.short_flag);                                      \
+                           tw_shift, o.counts, o.short_flag);                                                 \
     } while (0)
 #define KM_SCATTER(WBV, NBV)                        \
     do {                                            \
