@@ -457,13 +457,13 @@ __global__ __launch_bounds__(256) void k_fold_slots(const float* __restrict__ sl
 
 // Deterministic fold (sums that do not accumulate over launches): instead of
 // atomics, the slots of a segment are added in piece order by the divide.  A
-// segment spanning many pieces would make that a long serial walk, so this
-// pass first adds, for every group of kFoldG consecutive pieces, the slots of
-// the group's first run (its first piece and the following ones that share
-// that piece's segment), in piece order, into the group's own slot.  The
-// divide then adds at most kFoldG piece slots and one group slot per further
-// group.  A group whose first piece starts a segment holds no slot there and
-// stores nothing (no segment reads it).
+// segment spanning many pieces would make that a long serial walk, so the
+// reduction block of every group of kFoldG consecutive pieces first adds, at
+// its end, the slots of the group's first run (its first piece and the
+// following ones that share that piece's segment), in piece order, into the
+// group's own slot.  The divide then adds at most kFoldG piece slots and one
+// group slot per further group.  A group whose first piece starts a segment
+// holds no slot there and stores nothing (no segment reads it).
 template <bool WEIGHTED>
 __device__ __forceinline__ void fold_group(int64_t g, int64_t b, int lane, const float* __restrict__ slot,
                                            const float* __restrict__ wslot, const int32_t* __restrict__ piece_seg,
