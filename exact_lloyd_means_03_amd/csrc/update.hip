@@ -692,8 +692,12 @@ hipError_t launch_segreduce_tw(DType xt, const void* x, const float* w, int64_t 
 #undef KM_SEG
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the deterministic fold's group slots came with the reduction; sums
-    // that accumulate over launches take the atomic fold
+    // the deterministic fold's group slots came with the reduction.  The
+    // atomic fold stays a launch of its own: without `accumulate` the pieces
+    // store the sums of the segments they start with plain stores, and a
+    // slot's atomic add must not land before the plain store of its segment,
+    // which another block makes (folding each block's slots at its end gave
+    // wrong e-means sums in a test for exactly that reason)
     if (gslot) return hipSuccess;
     dim3 fgrid((unsigned)((npieces + 4 * kFoldG - 1) / (4 * kFoldG)), (unsigned)B);
     if (w)
